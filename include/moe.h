@@ -1,0 +1,157 @@
+/*
+ * moe.h -- C ABI of libmoe, the Mixtral sparse-MoE feed-forward layer on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (nnterp Mixtral encyclopedia page, "The API / support()" and
+ * "The Notes"; Transformers Mixtral page, "Architectural details" and
+ * MixtralConfig):
+ *   logits[t,e] = x[t,:] . router[e,:]               (+ optional bias[e])
+ *   p[t,:]      = softmax(logits[t,:])                in float32
+ *   idx[t,0..k) = the k largest, largest first; w = p[idx] / sum(p[idx])
+ *   out[t]      = sum_j w[t,j] * w2[e] (silu(w1[e] x[t]) * (w3[e] x[t])),  e = idx[t,j]
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: every tensor pointer is a DEVICE pointer (memory the caller got
+ *   from hipMalloc or a framework allocator on the current device). The
+ *   library never allocates, frees or synchronises; the caller owns every
+ *   buffer. Inputs are read-only. Outputs are fully overwritten (no
+ *   accumulation into them).
+ * Layout: dense, row-major, no padding:
+ *   x       [T, d]        dtype (MOE_F32 or MOE_BF16)
+ *   router  [E, d]        float32 for every dtype
+ *   w1, w3  [E, ffn, d]   gate and up projections (each expert's
+ *                         nn.Linear(d -> ffn).weight), same dtype as x
+ *   w2      [E, d, ffn]   down projection (nn.Linear(ffn -> d).weight)
+ *   topk_idx [T, k] int32, topk_w [T, k] float32: slot j of token t is
+ *   assignment a = t*k + j.
+ * Stream: `stream` is a hipStream_t (NULL = the null stream). All work is
+ *   enqueued on it in order and the call returns without waiting. Two calls
+ *   may run concurrently on different streams if they use distinct outputs
+ *   and workspaces.
+ * Sizes: 0 <= T, T*k < 2^31; 1 <= k <= E <= MOE_MAX_EXPERTS; d, ffn >= 1.
+ *   T == 0 is valid: nothing is computed, except that moe_permute (and
+ *   moe_forward's counts_out) still write zero counts and offsets.
+ *   MOE_BF16 additionally needs d % 64 == 0,
+ *   ffn % 64 == 0 and 16-byte aligned x/w1/w3/w2/workspace pointers, else
+ *   MOE_ENOTSUP.
+ * Errors: every function returns MOE_OK or an error code; arguments are
+ *   checked before anything is enqueued, so on MOE_EINVAL / MOE_ENOTSUP /
+ *   MOE_EWORKSPACE nothing ran. MOE_EHIP means the HIP runtime rejected a
+ *   launch (the stream state is then the runtime's). No C++ exception and no
+ *   abort crosses this boundary.
+ * Device-side preconditions (not checked): expert ids in [0, E) and distinct
+ *   within a token; offsets, sorted_asg and asg_pos exactly as moe_permute
+ *   produces them for the same T, k and E. moe_permute ignores expert ids
+ *   out of range; any other violation gives unspecified results and may
+ *   read or write out of bounds.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,     /* bad pointer, size, dtype or k/E */
+  MOE_ENOTSUP = 2,    /* valid but not supported (shape/alignment for bf16) */
+  MOE_EWORKSPACE = 3, /* workspace missing or smaller than moe_workspace_bytes */
+  MOE_EHIP = 4        /* the HIP runtime reported an error */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+#define MOE_MAX_EXPERTS 32
+
+/* Static description of a status code. Never NULL. */
+const char* moe_strerror(int status);
+
+/* Bytes of device workspace that moe_forward needs for these sizes; the same
+ * amount is always enough for moe_permute and moe_expert_ffn. Pure host
+ * function. Returns 0 for invalid arguments. */
+size_t moe_workspace_bytes(int64_t T, int d, int ffn, int E, int k, int dtype);
+
+/* Router + scoring (nnterp page, Notes: softmax over the experts in float32,
+ * keep the k largest, divide them by their sum; slot 0 is the larger).
+ *   x          [T, d] of x_dtype
+ *   router     [E, d] float32
+ *   logit_bias [E] float32 or NULL; added to the logits before the softmax
+ *   logits_out [T, E] float32 or NULL; receives the pre-softmax logits (+bias)
+ *   topk_idx   [T, k] int32 out; experts by decreasing logit, an exact tie
+ *              goes to the lower expert index
+ *   topk_w     [T, k] float32 out; renormalised weights, sum to 1 per token
+ * Logits accumulate in float32. */
+int moe_route(const void* x, int x_dtype, const float* router, const float* logit_bias,
+              int64_t T, int d, int E, int k, float* logits_out, int32_t* topk_idx,
+              float* topk_w, void* stream);
+
+/* Grouping of the T*k assignments by expert (each token is dispatched to its
+ * k experts: Transformers page, "Architectural details"). Integer only,
+ * deterministic. Outputs:
+ *   counts     [E]    assignments per expert
+ *   offsets    [E+1]  exclusive prefix sum of counts, offsets[E] = T*k
+ *   sorted_asg [T*k]  assignment ids a = t*k + j grouped by expert; within an
+ *                     expert in increasing a (a stable counting sort)
+ *   asg_pos    [T*k]  inverse: sorted_asg[asg_pos[a]] == a
+ * ws/ws_bytes: reserved scratch; the current kernel needs none, so NULL/0
+ * is accepted (any buffer passed is left untouched). */
+int moe_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_asg, int32_t* asg_pos, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* The experts on their grouped rows (nnterp page, support(): the down
+ * projection receives act(gate) * up, act = SiLU):
+ *   y[p] = w2[e] (silu(w1[e] x[r]) * (w3[e] x[r])),  r = sorted_asg[p] / k,
+ * for every p in [offsets[e], offsets[e+1]). y [T*k, d] float32, unweighted,
+ * in grouped order. offsets/sorted_asg are device arrays as produced by
+ * moe_permute. For MOE_BF16 the gate/up products accumulate in float32, the
+ * SwiGLU activation is rounded to bfloat16 (the down projection's MFMA input)
+ * and the down projection accumulates in float32. ws must hold
+ * moe_workspace_bytes(T, d, ffn, E, k, dtype) bytes. */
+int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
+                   const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d,
+                   int ffn, int E, int k, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Gate-weighted sum back in token order (nnterp page, Notes: each slot's
+ * weighted expert output, summed over the slots, is the layer output):
+ *   out[t] = sum_{j=0..k-1} topk_w[t*k+j] * y[asg_pos[t*k+j]]
+ * accumulated in float32 in slot order; out [T, d] float32 or bfloat16
+ * (round to nearest even). topk_w may be any caller array (e.g. with a slot
+ * zeroed to ablate an expert). */
+int moe_combine(const float* y, const int32_t* asg_pos, const float* topk_w, int64_t T, int d,
+                int k, void* out, int out_dtype, void* stream);
+
+/* The whole layer: moe_route, moe_permute, moe_expert_ffn and moe_combine
+ * in one call on one stream. topk_idx_out [T,k], topk_w_out [T,k] and
+ * counts_out [E] are optional (NULL) copies of the routing; logit_bias may be
+ * NULL. ws must hold moe_workspace_bytes(T, d, ffn, E, k, dtype) bytes. */
+int moe_forward(const void* x, int dtype, const float* router, const float* logit_bias,
+                const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
+                int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
+                float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* ---- tuning and profiling hooks (process-wide, not thread-safe) ---------- */
+
+/* Expert-FFN kernel family for MOE_BF16: 0 = choose by size (default),
+ * 1 = weight-streaming kernels (few rows per expert), 2 = LDS-tiled MFMA
+ * kernels (many rows per expert). Returns MOE_EINVAL for other values. */
+int moe_set_ffn_variant(int variant);
+
+/* Profiling: when n == 6, moe_forward records events[0] before the router,
+ * events[1] after it, then events[2..5] after the permutation, the gate/up
+ * kernel, the down kernel and the combine, on its stream. Each events[i] is
+ * a hipEvent_t the caller created. n == 0 (events may be NULL) turns it off.
+ * The array is copied. */
+int moe_set_stage_events(void* const* events, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,252 @@
+"""ctypes binding for libmoe.so (C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch supplies device memory (tensors) and the current HIP stream.
+The functions keep the C names; outputs that are not passed in are allocated
+with torch on the input's device. There is no fallback: if libmoe.so is
+missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
+
+MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
+MOE_F32, MOE_BF16 = 0, 1
+MOE_MAX_EXPERTS = 32
+
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+_c_sz = ctypes.c_size_t
+_vp = ctypes.c_void_p
+
+_SIGNATURES = {
+    "moe_strerror": (ctypes.c_char_p, [_c_int]),
+    "moe_workspace_bytes": (_c_sz, [_c_i64, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "moe_route": (_c_int, [_vp, _c_int, _vp, _vp, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                           _vp]),
+    "moe_permute": (_c_int, [_vp, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
+    "moe_expert_ffn": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _c_int,
+                                _c_int, _c_int, _vp, _vp, _c_sz, _vp]),
+    "moe_combine": (_c_int, [_vp, _vp, _vp, _c_i64, _c_int, _c_int, _vp, _c_int, _vp]),
+    "moe_forward": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _c_int,
+                             _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _c_sz, _vp]),
+    "moe_set_ffn_variant": (_c_int, [_c_int]),
+    "moe_set_stage_events": (_c_int, [_vp, _c_int]),
+}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({strerror(status)})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libmoe.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_mixture_experts_06_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/moe.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def strerror(status: int) -> str:
+    return load().moe_strerror(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return MOE_F32
+    if t == torch.bfloat16:
+        return MOE_BF16
+    raise ValueError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+# ---------------------------------------------------------------------------
+def moe_set_ffn_variant(variant: int) -> None:
+    _check("moe_set_ffn_variant", load().moe_set_ffn_variant(int(variant)))
+
+
+def moe_set_stage_events(events) -> None:
+    """events: a sequence of 6 hipEvent_t handles (ints), or None to turn off."""
+    lib = load()
+    if not events:
+        _check("moe_set_stage_events", lib.moe_set_stage_events(None, 0))
+        return
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(int(e)) for e in events])
+    _check("moe_set_stage_events", lib.moe_set_stage_events(arr, len(events)))
+
+
+def moe_workspace_bytes(T: int, d: int, ffn: int, E: int, k: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(load().moe_workspace_bytes(int(T), int(d), int(ffn), int(E), int(k), code))
+
+
+def workspace(T: int, d: int, ffn: int, E: int, k: int, dtype, device) -> torch.Tensor:
+    n = moe_workspace_bytes(T, d, ffn, E, k, dtype)
+    if n == 0:
+        raise ValueError("invalid sizes for moe_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_route(x, router, k: int, logit_bias=None, logits_out=None, topk_idx=None, topk_w=None):
+    """Returns (topk_idx [T,k] int32, topk_w [T,k] float32); logits_out, if
+    given ([T,E] float32), receives the pre-softmax logits."""
+    T, d = x.shape
+    E = router.shape[0]
+    dev = x.device
+    _need(router, "router", torch.float32, (E, d), dev)
+    if logit_bias is not None:
+        _need(logit_bias, "logit_bias", torch.float32, (E,), dev)
+    if logits_out is not None:
+        _need(logits_out, "logits_out", torch.float32, (T, E), dev)
+    if topk_idx is None:
+        topk_idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    st = load().moe_route(_ptr(x), _dtype_code(x.dtype), _ptr(router), _ptr(logit_bias), T, d, E,
+                          k, _ptr(logits_out), _ptr(topk_idx), _ptr(topk_w), _stream(dev))
+    _check("moe_route", st)
+    return topk_idx, topk_w
+
+
+def moe_permute(topk_idx, E: int, counts=None, offsets=None, sorted_asg=None, asg_pos=None):
+    """Returns (counts [E], offsets [E+1], sorted_asg [T*k], asg_pos [T*k]), int32."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    A = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    sorted_asg = torch.empty(A, dtype=torch.int32, device=dev) if sorted_asg is None else sorted_asg
+    asg_pos = torch.empty(A, dtype=torch.int32, device=dev) if asg_pos is None else asg_pos
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(counts, "counts", torch.int32, (E,), dev)
+    _need(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _need(sorted_asg, "sorted_asg", torch.int32, (A,), dev)
+    _need(asg_pos, "asg_pos", torch.int32, (A,), dev)
+    st = load().moe_permute(_ptr(topk_idx), T, E, k, _ptr(counts), _ptr(offsets),
+                            _ptr(sorted_asg), _ptr(asg_pos), None, 0, _stream(dev))
+    _check("moe_permute", st)
+    return counts, offsets, sorted_asg, asg_pos
+
+
+def moe_expert_ffn(x, w1, w3, w2, offsets, sorted_asg, k: int, y=None, ws=None):
+    """Returns y [T*k, d] float32 (unweighted expert outputs, grouped order)."""
+    T, d = x.shape
+    E, ffn, _ = w1.shape
+    dev = x.device
+    for name, t, shp in (("w1", w1, (E, ffn, d)), ("w3", w3, (E, ffn, d)), ("w2", w2, (E, d, ffn))):
+        _need(t, name, x.dtype, shp, dev)
+    _need(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _need(sorted_asg, "sorted_asg", torch.int32, (T * k,), dev)
+    if y is None:
+        y = torch.empty(T * k, d, dtype=torch.float32, device=dev)
+    _need(y, "y", torch.float32, (T * k, d), dev)
+    if ws is None:
+        ws = workspace(T, d, ffn, E, k, x.dtype, dev)
+    st = load().moe_expert_ffn(_ptr(x), _dtype_code(x.dtype), _ptr(w1), _ptr(w3), _ptr(w2),
+                               _ptr(offsets), _ptr(sorted_asg), T, d, ffn, E, k, _ptr(y),
+                               _ptr(ws), ws.numel(), _stream(dev))
+    _check("moe_expert_ffn", st)
+    return y
+
+
+def moe_combine(y, asg_pos, topk_w, out=None, out_dtype=torch.float32):
+    """Returns out [T, d] = sum_j topk_w[t, j] * y[asg_pos[t*k + j]]."""
+    T, k = topk_w.shape
+    d = y.shape[1]
+    dev = y.device
+    _need(y, "y", torch.float32, (T * k, d), dev)
+    _need(asg_pos, "asg_pos", torch.int32, (T * k,), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    if out is None:
+        out = torch.empty(T, d, dtype=out_dtype, device=dev)
+    _need(out, "out", out.dtype, (T, d), dev)
+    st = load().moe_combine(_ptr(y), _ptr(asg_pos), _ptr(topk_w), T, d, k, _ptr(out),
+                            _dtype_code(out.dtype), _stream(dev))
+    _check("moe_combine", st)
+    return out
+
+
+def moe_forward(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dtype=None,
+                ws=None, topk_idx_out=None, topk_w_out=None, counts_out=None):
+    """The whole layer; returns out [T, d] (dtype out_dtype, default x.dtype)."""
+    T, d = x.shape
+    E, ffn, _ = w1.shape
+    dev = x.device
+    _need(router, "router", torch.float32, (E, d), dev)
+    for name, t, shp in (("w1", w1, (E, ffn, d)), ("w3", w3, (E, ffn, d)), ("w2", w2, (E, d, ffn))):
+        _need(t, name, x.dtype, shp, dev)
+    if logit_bias is not None:
+        _need(logit_bias, "logit_bias", torch.float32, (E,), dev)
+    if out is None:
+        out = torch.empty(T, d, dtype=out_dtype or x.dtype, device=dev)
+    _need(out, "out", out.dtype, (T, d), dev)
+    if topk_idx_out is not None:
+        _need(topk_idx_out, "topk_idx_out", torch.int32, (T, k), dev)
+    if topk_w_out is not None:
+        _need(topk_w_out, "topk_w_out", torch.float32, (T, k), dev)
+    if counts_out is not None:
+        _need(counts_out, "counts_out", torch.int32, (E,), dev)
+    if ws is None:
+        ws = workspace(T, d, ffn, E, k, x.dtype, dev)
+    st = load().moe_forward(_ptr(x), _dtype_code(x.dtype), _ptr(router), _ptr(logit_bias),
+                            _ptr(w1), _ptr(w3), _ptr(w2), T, d, ffn, E, k, _ptr(out),
+                            _dtype_code(out.dtype), _ptr(topk_idx_out), _ptr(topk_w_out),
+                            _ptr(counts_out), _ptr(ws), ws.numel(), _stream(dev))
+    _check("moe_forward", st)
+    return out

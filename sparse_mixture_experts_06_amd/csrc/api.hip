@@ -1,0 +1,243 @@
+// libmoe C ABI: argument checks, workspace carving and stream-ordered
+// launches. Nothing here allocates, frees or synchronises.
+#include "moe.h"
+
+#include <string.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr int64_t kMaxAssignments = (int64_t(1) << 31) - 1;
+
+int g_ffn_variant = 0;
+void* g_events[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+int g_nevents = 0;
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t idx, w, counts, offsets, sorted, pos, h, y, total;
+};
+
+Layout layout(int64_t T, int d, int ffn, int E, int k, int dtype) {
+  const size_t A = static_cast<size_t>(T) * static_cast<size_t>(k);
+  const size_t hb = (dtype == MOE_BF16) ? 2 : 4;
+  Layout L;
+  size_t o = 0;
+  L.idx = o;     o = align256(o + A * 4);
+  L.w = o;       o = align256(o + A * 4);
+  L.counts = o;  o = align256(o + static_cast<size_t>(E) * 4);
+  L.offsets = o; o = align256(o + static_cast<size_t>(E + 1) * 4);
+  L.sorted = o;  o = align256(o + A * 4);
+  L.pos = o;     o = align256(o + A * 4);
+  L.h = o;       o = align256(o + A * static_cast<size_t>(ffn) * hb);
+  L.y = o;       o = align256(o + A * static_cast<size_t>(d) * 4);
+  L.total = o;
+  return L;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline bool valid_dtype(int t) { return t == MOE_F32 || t == MOE_BF16; }
+
+int check_sizes(int64_t T, int E, int k) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E) return MOE_EINVAL;
+  if (T > kMaxAssignments / k) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int check_ffn_shape(int64_t T, int d, int ffn, int E, int k, int dtype) {
+  if (d < 1 || ffn < 1) return MOE_EINVAL;
+  if (!valid_dtype(dtype)) return MOE_EINVAL;
+  const int64_t A = T * k;
+  if (dtype == MOE_BF16) {
+    if (d % 64 != 0 || ffn % 64 != 0) return MOE_ENOTSUP;
+    // worst-case tile grid of the tiled kernels must fit a 1-D launch
+    const int64_t mt = (A + 127) / 128 + E;
+    const int64_t n = (ffn / 64 > (d + 127) / 128) ? ffn / 64 : (d + 127) / 128;
+    if (mt * n >= (int64_t(1) << 31)) return MOE_ENOTSUP;
+  } else {
+    const int64_t mt = (A + 15) / 16 + E;
+    const int64_t n = ((ffn > d ? ffn : d) + 15) / 16;
+    if (mt * n >= (int64_t(1) << 31)) return MOE_ENOTSUP;
+  }
+  return MOE_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+inline void stage(int i, hipStream_t s) {
+  if (g_nevents == 6 && g_events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(g_events[i]), s);
+}
+
+int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
+            const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d, int ffn, int E,
+            int k, float* y, void* h, hipStream_t s, bool with_events) {
+  const int64_t A = T * k;
+  hipError_t err;
+  if (dtype == MOE_BF16) {
+    err = moe::launch_gate_up_bf16(g_ffn_variant, static_cast<const uint16_t*>(x),
+                                   static_cast<const uint16_t*>(w1),
+                                   static_cast<const uint16_t*>(w3), offsets, sorted_asg, A, d,
+                                   ffn, E, k, static_cast<uint16_t*>(h), s);
+    if (err != hipSuccess) return MOE_EHIP;
+    if (with_events) stage(3, s);
+    err = moe::launch_down_bf16(g_ffn_variant, static_cast<const uint16_t*>(h),
+                                static_cast<const uint16_t*>(w2), offsets, A, d, ffn, E, y, s);
+  } else {
+    err = moe::launch_gate_up_f32(static_cast<const float*>(x), static_cast<const float*>(w1),
+                                  static_cast<const float*>(w3), offsets, sorted_asg, A, d, ffn,
+                                  E, k, static_cast<float*>(h), s);
+    if (err != hipSuccess) return MOE_EHIP;
+    if (with_events) stage(3, s);
+    err = moe::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w2),
+                               offsets, A, d, ffn, E, y, s);
+  }
+  return hip_status(err);
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "success";
+    case MOE_EINVAL: return "invalid argument (pointer, size, dtype, k or E)";
+    case MOE_ENOTSUP: return "unsupported shape or alignment (bf16 needs d, ffn % 64 == 0 and 16-byte aligned buffers)";
+    case MOE_EWORKSPACE: return "workspace missing or smaller than moe_workspace_bytes()";
+    case MOE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(int64_t T, int d, int ffn, int E, int k, int dtype) {
+  if (check_sizes(T, E, k) != MOE_OK || d < 1 || ffn < 1 || !valid_dtype(dtype)) return 0;
+  return layout(T, d, ffn, E, k, dtype).total;
+}
+
+int moe_route(const void* x, int x_dtype, const float* router, const float* logit_bias,
+              int64_t T, int d, int E, int k, float* logits_out, int32_t* topk_idx,
+              float* topk_w, void* stream) {
+  int st = check_sizes(T, E, k);
+  if (st != MOE_OK) return st;
+  if (d < 1 || !valid_dtype(x_dtype)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !router || !topk_idx || !topk_w) return MOE_EINVAL;
+  return hip_status(moe::launch_route(x, x_dtype == MOE_BF16, router, logit_bias, T, d, E, k,
+                                      logits_out, topk_idx, topk_w,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int moe_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_asg, int32_t* asg_pos, void* ws,
+                size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_sizes(T, E, k);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets) return MOE_EINVAL;
+  if (T > 0 && (!topk_idx || !sorted_asg || !asg_pos)) return MOE_EINVAL;
+  return hip_status(moe::launch_permute(topk_idx, T * k, E, counts, offsets, sorted_asg,
+                                        asg_pos, static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
+                   const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d,
+                   int ffn, int E, int k, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_sizes(T, E, k);
+  if (st != MOE_OK) return st;
+  st = check_ffn_shape(T, d, ffn, E, k, dtype);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w1 || !w3 || !w2 || !offsets || !sorted_asg || !y) return MOE_EINVAL;
+  if (!ws || ws_bytes < layout(T, d, ffn, E, k, dtype).total) return MOE_EWORKSPACE;
+  if (dtype == MOE_BF16 &&
+      !(aligned16(x) && aligned16(w1) && aligned16(w3) && aligned16(w2) && aligned16(ws) &&
+        aligned16(y)))
+    return MOE_ENOTSUP;
+  return run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, ws,
+                 static_cast<hipStream_t>(stream), false);
+}
+
+int moe_combine(const float* y, const int32_t* asg_pos, const float* topk_w, int64_t T, int d,
+                int k, void* out, int out_dtype, void* stream) {
+  if (T < 0 || d < 1 || k < 1 || !valid_dtype(out_dtype)) return MOE_EINVAL;
+  if (T > kMaxAssignments / k) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!y || !asg_pos || !topk_w || !out) return MOE_EINVAL;
+  return hip_status(moe::launch_combine(y, asg_pos, topk_w, T, d, k, out, out_dtype == MOE_BF16,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward(const void* x, int dtype, const float* router, const float* logit_bias,
+                const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
+                int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
+                float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                void* stream) {
+  int st = check_sizes(T, E, k);
+  if (st != MOE_OK) return st;
+  st = check_ffn_shape(T, d, ffn, E, k, dtype);
+  if (st != MOE_OK) return st;
+  if (!valid_dtype(out_dtype)) return MOE_EINVAL;
+  if (T > 0 && (!x || !router || !w1 || !w3 || !w2 || !out)) return MOE_EINVAL;
+  const Layout L = layout(T, d, ffn, E, k, dtype);
+  if (!ws || ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (dtype == MOE_BF16 && T > 0 &&
+      !(aligned16(x) && aligned16(w1) && aligned16(w3) && aligned16(w2) && aligned16(ws)))
+    return MOE_ENOTSUP;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(base + L.idx);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(base + L.w);
+  int32_t* counts = counts_out ? counts_out : reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* sorted_asg = reinterpret_cast<int32_t*>(base + L.sorted);
+  int32_t* asg_pos = reinterpret_cast<int32_t*>(base + L.pos);
+  void* h = base + L.h;
+  float* y = reinterpret_cast<float*>(base + L.y);
+
+  stage(0, s);
+  if (T > 0 && moe::launch_route(x, dtype == MOE_BF16, router, logit_bias, T, d, E, k, nullptr,
+                                 idx, w, s) != hipSuccess)
+    return MOE_EHIP;
+  stage(1, s);
+  if (moe::launch_permute(idx, T * k, E, counts, offsets, sorted_asg, asg_pos, s) != hipSuccess)
+    return MOE_EHIP;
+  stage(2, s);
+  if (T == 0) {
+    for (int i = 3; i < 6; ++i) stage(i, s);
+    return MOE_OK;
+  }
+  st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, h, s, true);
+  if (st != MOE_OK) return st;
+  stage(4, s);
+  if (moe::launch_combine(y, asg_pos, w, T, d, k, out, out_dtype == MOE_BF16, s) != hipSuccess)
+    return MOE_EHIP;
+  stage(5, s);
+  return MOE_OK;
+}
+
+int moe_set_ffn_variant(int variant) {
+  if (variant < 0 || variant > 2) return MOE_EINVAL;
+  g_ffn_variant = variant;
+  return MOE_OK;
+}
+
+int moe_set_stage_events(void* const* events, int n) {
+  if (n == 0) {
+    g_nevents = 0;
+    return MOE_OK;
+  }
+  if (n != 6 || !events) return MOE_EINVAL;
+  for (int i = 0; i < 6; ++i)
+    if (!events[i]) return MOE_EINVAL;
+  memcpy(g_events, events, sizeof(g_events));
+  g_nevents = 6;
+  return MOE_OK;
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,81 @@
+// Device helpers and internal launcher declarations shared by the libmoe
+// translation units. gfx950 (CDNA4) only: wave64, bf16 MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 32;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// SiLU(z) = z / (1 + exp(-z)) in float32.
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// 16 bytes (8 bf16) as an MFMA operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D += A(16x32) * B(32x16); lane l holds A row (l%16), k-group (l/16) and the
+// matching B column/k-group; D lane l holds column (l%16), rows 4*(l/16)+i.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// internal launchers (host side); each returns hipSuccess or the launch error
+// ---------------------------------------------------------------------------
+hipError_t launch_route(const void* x, int x_bf16, const float* router, const float* bias,
+                        int64_t T, int d, int E, int k, float* logits_out, int32_t* idx,
+                        float* w, hipStream_t s);
+
+hipError_t launch_permute(const int32_t* idx, int64_t A, int E, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_asg, int32_t* asg_pos,
+                          hipStream_t s);
+
+// bf16 experts: gate/up (+SiLU*mul) -> h [A, ffn] bf16, down -> y [A, d] f32
+hipError_t launch_gate_up_bf16(int variant, const uint16_t* x, const uint16_t* w1,
+                               const uint16_t* w3, const int32_t* offsets,
+                               const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
+                               int k, uint16_t* h, hipStream_t s);
+hipError_t launch_down_bf16(int variant, const uint16_t* h, const uint16_t* w2,
+                            const int32_t* offsets, int64_t A, int d, int ffn, int E, float* y,
+                            hipStream_t s);
+
+// f32 experts: same steps in float32 (h stays float32)
+hipError_t launch_gate_up_f32(const float* x, const float* w1, const float* w3,
+                              const int32_t* offsets, const int32_t* sorted_asg, int64_t A,
+                              int d, int ffn, int E, int k, float* h, hipStream_t s);
+hipError_t launch_down_f32(const float* h, const float* w2, const int32_t* offsets, int64_t A,
+                           int d, int ffn, int E, float* y, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const int32_t* asg_pos, const float* w, int64_t T,
+                          int d, int k, void* out, int out_bf16, hipStream_t s);
+
+// Resolved expert-FFN kernel family for these sizes (1 streaming, 2 tiled).
+int choose_ffn_variant(int requested, int64_t A, int E);
+
+}  // namespace moe

@@ -1,0 +1,99 @@
+// Expert SwiGLU in float32 (the all-fp32 workloads): the same two grouped
+// steps as the bf16 path, one thread per output element, float32 FMA
+// accumulation, h kept in float32. Any d and ffn.
+//   gate/up: h[p, n] = silu(x[r] . w1[e, n]) * (x[r] . w3[e, n]),  r = sorted_asg[p] / k
+//   down:    y[p, n] = h[p] . w2[e, n]
+// (nnterp Mixtral page, support(): act(gate) * up feeds the down projection.)
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int TM = 16;  // rows per tile
+constexpr int TN = 16;  // columns per tile
+
+// tile b of a 1-D grid -> (expert, first row, first column); tiles are
+// (expert, m-tile) major, n-tile minor, counted from the device offsets
+__device__ __forceinline__ bool decode(const int32_t* __restrict__ offsets, int E, int ntn,
+                                       int& e, int& beg, int& M, int& m0, int& n0) {
+  int L = blockIdx.x / ntn;
+  n0 = (blockIdx.x % ntn) * TN;
+  for (int i = 0; i < E; ++i) {
+    const int Mi = offsets[i + 1] - offsets[i];
+    const int mt = (Mi + TM - 1) / TM;
+    if (L < mt) {
+      e = i;
+      beg = offsets[i];
+      M = Mi;
+      m0 = L * TM;
+      return true;
+    }
+    L -= mt;
+  }
+  return false;
+}
+
+__global__ __launch_bounds__(TM* TN) void gate_up_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ w1, const float* __restrict__ w3,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_asg, int d, int ffn,
+    int E, int k, float* __restrict__ h, int ntn) {
+  int e, beg, M, m0, n0;
+  if (!decode(offsets, E, ntn, e, beg, M, m0, n0)) return;
+  const int m = m0 + static_cast<int>(threadIdx.x) / TN;
+  const int n = n0 + static_cast<int>(threadIdx.x) % TN;
+  if (m >= M || n >= ffn) return;
+  const int64_t row = sorted_asg[beg + m] / k;
+  const float* xr = x + row * d;
+  const float* g1 = w1 + (static_cast<int64_t>(e) * ffn + n) * d;
+  const float* g3 = w3 + (static_cast<int64_t>(e) * ffn + n) * d;
+  float g = 0.0f, u = 0.0f;
+  for (int i = 0; i < d; ++i) {
+    g = fmaf(xr[i], g1[i], g);
+    u = fmaf(xr[i], g3[i], u);
+  }
+  h[static_cast<int64_t>(beg + m) * ffn + n] = g / (1.0f + expf(-g)) * u;
+}
+
+__global__ __launch_bounds__(TM* TN) void down_f32_kernel(const float* __restrict__ h,
+                                                         const float* __restrict__ w2,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int d, int ffn, int E,
+                                                         float* __restrict__ y, int ntn) {
+  int e, beg, M, m0, n0;
+  if (!decode(offsets, E, ntn, e, beg, M, m0, n0)) return;
+  const int m = m0 + static_cast<int>(threadIdx.x) / TN;
+  const int n = n0 + static_cast<int>(threadIdx.x) % TN;
+  if (m >= M || n >= d) return;
+  const float* hr = h + static_cast<int64_t>(beg + m) * ffn;
+  const float* wr = w2 + (static_cast<int64_t>(e) * d + n) * ffn;
+  float acc = 0.0f;
+  for (int f = 0; f < ffn; ++f) acc = fmaf(hr[f], wr[f], acc);
+  y[static_cast<int64_t>(beg + m) * d + n] = acc;
+}
+
+inline unsigned grid_for(int64_t A, int E, int ntn) {
+  return static_cast<unsigned>(((A + TM - 1) / TM + E) * ntn);
+}
+
+}  // namespace
+
+hipError_t launch_gate_up_f32(const float* x, const float* w1, const float* w3,
+                              const int32_t* offsets, const int32_t* sorted_asg, int64_t A,
+                              int d, int ffn, int E, int k, float* h, hipStream_t s) {
+  if (A == 0) return hipSuccess;
+  const int ntn = (ffn + TN - 1) / TN;
+  hipLaunchKernelGGL(gate_up_f32_kernel, dim3(grid_for(A, E, ntn)), dim3(TM * TN), 0, s, x, w1,
+                     w3, offsets, sorted_asg, d, ffn, E, k, h, ntn);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_f32(const float* h, const float* w2, const int32_t* offsets, int64_t A,
+                           int d, int ffn, int E, float* y, hipStream_t s) {
+  if (A == 0) return hipSuccess;
+  const int ntn = (d + TN - 1) / TN;
+  hipLaunchKernelGGL(down_f32_kernel, dim3(grid_for(A, E, ntn)), dim3(TM * TN), 0, s, h, w2,
+                     offsets, d, ffn, E, y, ntn);
+  return hipGetLastError();
+}
+
+}  // namespace moe
