@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Throughput of the Mixtral sparse-MoE layer (libmoe) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one moe_forward call (router, permutation, gate/up, down, combine)
+over one batch of synthetic, seeded inputs already resident in HBM. W
+untimed steps run first, then exactly K steps are timed between two device
+synchronisations. Consecutive steps alternate between two copies of the
+expert weights, so no step can find the previous step's weights in the
+256 MB Infinity Cache. Per-kernel times come from HIP events the library
+records on its stream between the stages.
+
+Prints one JSON line: tokens/s for the whole job, the dominant kernel's
+roofline position and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE-layer tokens/sec at 1 GPU; % of HBM BW peak (decode) / bf16 MFMA peak "
+          "(prefill)")
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+STAGES = ("route", "permute", "gate_up", "down", "combine")
+FFN_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_06_amd", "csrc", "ffn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode_8x7b",
+                   help="decode_8x7b (default), prefill_8x7b, skew_8x7b, prefill_8x22b, tiny")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip timing the CPU oracle (e.g. under a profiler)")
+    p.add_argument("--variant", type=int, default=0, help="expert-FFN kernel family (0 = auto)")
+    return p.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls needed for events on the library's stream."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        ev = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev: int):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def upload(inp, torch):
+    import numpy as np
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+    return {k: up(inp[k]) for k in ("x", "router", "w1", "w3", "w2", "bias")}
+
+
+def algorithmic_work(cfg, counts):
+    """Bytes and flops the layer must move/do (intermediates h and y excluded)."""
+    T, d, F, E, k = cfg["T"], cfg["d"], cfg["ffn"], cfg["E"], cfg["k"]
+    wb = 2 if cfg["dtype"] == "bf16" else 4
+    A = T * k
+    active = sum(1 for c in counts if c > 0)
+    layer_bytes = active * 3 * d * F * wb + T * d * wb + T * d * wb + E * d * 4
+    layer_flops = 2 * A * 3 * d * F + 2 * T * E * d
+    gate_up_bytes = active * 2 * d * F * wb + T * d * wb + A * F * wb
+    gate_up_flops = 2 * A * 2 * d * F
+    return layer_bytes, layer_flops, gate_up_bytes, gate_up_flops
+
+
+def traffic_entry(workload):
+    """rocprofv3 FETCH/WRITE bytes of the gate/up kernel, if they were taken
+    on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(FFN_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("workloads", {}).get(workload)
+    if not ent or rec.get("ffn_bf16_sha256") != sha:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp):
+    """The float64 oracle on a bounded sample of the same workload."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    n = min(cfg["T"], 32 if cfg["d"] <= 4096 else 16)
+    sub = dict(inp)
+    sub["x"] = inp["x"][:n]
+    t0 = time.perf_counter()
+    oracle.forward(sub["x"], sub["router"], sub["w1"], sub["w3"], sub["w2"], cfg["k"], sub["bias"])
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} tokens of the {cfg['T']}-token batch, full routing and all "
+                      f"their experts, float64 NumPy ({dt:.1f} s)",
+            "seconds": round(dt, 3), "blas_threads": int(threads),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the layer's multi-GPU path is not built in this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import sparse_mixture_experts_06_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = dict(gen.CONFIGS[args.workload])
+    T, d, F, E, k = cfg["T"], cfg["d"], cfg["ffn"], cfg["E"], cfg["k"]
+    print(f"[bench] workload {args.workload}: T={T} d={d} ffn={F} E={E} k={k} {cfg['dtype']}",
+          file=sys.stderr, flush=True)
+    inp = gen.make_inputs(**cfg)
+    dev = upload(inp, torch)
+    sets = [dev, dict(dev, w1=dev["w1"].clone(), w3=dev["w3"].clone(), w2=dev["w2"].clone())]
+    moe.moe_set_ffn_variant(args.variant)
+    wdt = dev["x"].dtype
+    ws = moe.workspace(T, d, F, E, k, wdt, "cuda")
+    out = torch.empty(T, d, dtype=wdt, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    hip = Hip()
+
+    def step(i, events=None):
+        s = sets[i % 2]
+        if events is not None:
+            moe.moe_set_stage_events(events)
+        moe.moe_forward(s["x"], s["router"], s["w1"], s["w3"], s["w2"], k,
+                        logit_bias=s["bias"], out=out, ws=ws, counts_out=counts)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[hip.event() for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    moe.moe_set_stage_events(None)
+    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs]))
+                for j, name in enumerate(STAGES)}
+    for e in evs:
+        for ev in e:
+            hip.destroy(ev)
+
+    cnt = counts.cpu().tolist()
+    layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt)
+    ms_step = wall * 1e3 / args.steps
+    tok_s = T / (ms_step / 1e3)
+    decode_like = (T * k) <= 32 * E  # the streaming kernels' regime: weight-bandwidth bound
+    gu_s = stage_ms["gate_up"] / 1e3
+    if decode_like:
+        ach = gu_bytes / gu_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = gu_flops / gu_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    roof.update({"kernel": "gate_up (w1/w3 grouped GEMM + SiLU*mul)",
+                 "avg_us": round(stage_ms["gate_up"] * 1e3, 2),
+                 "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops,
+                 "traffic": traffic_entry(args.workload)})
+    layer_tflops = layer_flops / (ms_step / 1e3) / 1e12
+    layer_gbs = layer_bytes / (ms_step / 1e3) / 1e9
+    rec = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg["dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "d": d, "ffn": F, "E": E, "k": k,
+                   "seed": cfg["seed"], "logit_bias": cfg["bias"]},
+        "roofline": roof,
+        "layer": {"tflops": round(layer_tflops, 2),
+                  "tflops_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
+                  "gbs": round(layer_gbs, 1), "gbs_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                  "algorithmic_bytes": layer_bytes, "algorithmic_flops": layer_flops,
+                  "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
+                  "expert_counts": cnt},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
