@@ -11,6 +11,10 @@ expert weights, so no step can find the previous step's weights in the
 256 MB Infinity Cache. Per-kernel times come from HIP events the library
 records on its stream between the stages.
 
+By default the expert weights are held in fragment order (moe_pack_weight,
+run once when the weights are loaded, outside the timed region); the rate
+with the standard [E, ffn, d] layout is measured too and reported beside it.
+
 Prints one JSON line: tokens/s for the whole job, the dominant kernel's
 roofline position and the CPU oracle's throughput on a bounded sample.
 """
@@ -46,6 +50,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle (e.g. under a profiler)")
     p.add_argument("--variant", type=int, default=0, help="expert-FFN kernel family (0 = auto)")
+    p.add_argument("--layout", choices=("packed", "standard"), default="packed",
+                   help="expert weight layout of the timed steps")
+    p.add_argument("--no-compare", action="store_true",
+                   help="do not also time the other weight layout")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="first copy a buffer of this many MiB once (a known-size kernel that "
+                        "calibrates hardware byte counters under a profiler)")
     return p.parse_args()
 
 
@@ -160,7 +171,19 @@ def main():
           file=sys.stderr, flush=True)
     inp = gen.make_inputs(**cfg)
     dev = upload(inp, torch)
-    sets = [dev, dict(dev, w1=dev["w1"].clone(), w3=dev["w3"].clone(), w2=dev["w2"].clone())]
+    std_sets = [dev, dict(dev, w1=dev["w1"].clone(), w3=dev["w3"].clone(), w2=dev["w2"].clone())]
+    packed = args.layout == "packed" and cfg["dtype"] == "bf16"
+    if packed:
+        pk_sets = []
+        for st in std_sets:
+            pw = moe.PackedWeights(st["w1"], st["w3"], st["w2"])
+            pk_sets.append(dict(st, w1=pw.w1, w3=pw.w3, w2=pw.w2))
+        if args.no_compare:
+            std_sets = None
+        sets = pk_sets
+    else:
+        sets = std_sets
+    torch.cuda.synchronize()
     moe.moe_set_ffn_variant(args.variant)
     wdt = dev["x"].dtype
     ws = moe.workspace(T, d, F, E, k, wdt, "cuda")
@@ -168,21 +191,29 @@ def main():
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     hip = Hip()
 
-    def step(i, events=None):
-        s = sets[i % 2]
+    def step(i, use_sets, is_packed, events=None):
+        s = use_sets[i % 2]
         if events is not None:
             moe.moe_set_stage_events(events)
         moe.moe_forward(s["x"], s["router"], s["w1"], s["w3"], s["w2"], k,
-                        logit_bias=s["bias"], out=out, ws=ws, counts_out=counts)
+                        logit_bias=s["bias"], out=out, ws=ws, counts_out=counts,
+                        packed=is_packed)
 
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
-        step(i)
+        step(i, sets, packed)
     torch.cuda.synchronize()
     evs = [[hip.event() for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, sets, packed, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     moe.moe_set_stage_events(None)
@@ -191,6 +222,19 @@ def main():
     for e in evs:
         for ev in e:
             hip.destroy(ev)
+
+    other = None
+    if packed and std_sets is not None:
+        for i in range(args.warmup):
+            step(i, std_sets, False)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, std_sets, False)
+        torch.cuda.synchronize()
+        ms_std = (time.perf_counter() - t1) * 1e3 / args.steps
+        other = {"layout": "standard [E, ffn, d]", "value": round(T / (ms_std / 1e3), 1),
+                 "ms_per_step": round(ms_std, 4)}
 
     cnt = counts.cpu().tolist()
     layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt)
@@ -227,6 +271,10 @@ def main():
                   "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
                   "expert_counts": cnt},
     }
+    rec["weights_layout"] = ("fragment order (moe_pack_weight once at load time)" if packed
+                             else "standard [E, ffn, d]")
+    if other is not None:
+        rec["other_layout"] = other
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, inp)

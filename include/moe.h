@@ -64,7 +64,11 @@ enum moe_status {
   MOE_EHIP = 4        /* the HIP runtime reported an error */
 };
 
-enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+/* Element types. MOE_BF16_PACKED is accepted only as the `dtype` of
+ * moe_expert_ffn and moe_forward: x is bfloat16 as for MOE_BF16, and w1, w3
+ * and w2 are the bfloat16 weights rearranged by moe_pack_weight (same
+ * values, fragment order); everything else is unchanged. */
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_BF16_PACKED = 2 };
 
 #define MOE_MAX_EXPERTS 32
 
@@ -109,9 +113,11 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* count
  *   y[p] = w2[e] (silu(w1[e] x[r]) * (w3[e] x[r])),  r = sorted_asg[p] / k,
  * for every p in [offsets[e], offsets[e+1]). y [T*k, d] float32, unweighted,
  * in grouped order. offsets/sorted_asg are device arrays as produced by
- * moe_permute. For MOE_BF16 the gate/up products accumulate in float32, the
- * SwiGLU activation is rounded to bfloat16 (the down projection's MFMA input)
- * and the down projection accumulates in float32. ws must hold
+ * moe_permute. For MOE_BF16 / MOE_BF16_PACKED the gate/up products
+ * accumulate in float32, the SwiGLU activation is rounded to bfloat16 (the
+ * down projection's MFMA input) and the down projection accumulates in
+ * float32 (on few rows per expert it splits K two ways and adds the two
+ * float32 partial sums in a fixed order). ws must hold
  * moe_workspace_bytes(T, d, ffn, E, k, dtype) bytes. */
 int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
                    const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d,
@@ -135,6 +141,19 @@ int moe_forward(const void* x, int dtype, const float* router, const float* logi
                 int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
                 float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                 void* stream);
+
+/* One-time weight preparation for the MOE_BF16_PACKED path: copies the
+ * bfloat16 matrices w [E, rows, cols] (standard layout, cols contiguous) into
+ * `out` (same size, E*rows*cols*2 bytes, must not overlap w) in fragment
+ * order: 16-row x 32-column fragments, each 1 KiB in the lane order of a
+ * 16x16x32 bf16 MFMA operand (value w[e][16*rt + r][32*s + 8*g + i] at
+ * element ((e*rows/16 + rt)*cols/32 + s)*512 + (16*g + r)*8 + i). Pack w1 and
+ * w3 with rows = ffn, cols = d, and w2 with rows = d, cols = ffn. Expert
+ * weights do not change between calls, so this runs once when they are
+ * loaded. dtype must be MOE_BF16; rows % 16 == 0 and cols % 32 == 0, and
+ * both pointers 16-byte aligned, else MOE_ENOTSUP. */
+int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* out,
+                    void* stream);
 
 /* ---- tuning and profiling hooks (process-wide, not thread-safe) ---------- */
 

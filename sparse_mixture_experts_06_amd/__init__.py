@@ -1,17 +1,18 @@
 """Mixtral sparse-MoE feed-forward layer for AMD Instinct MI355X (gfx950).
 
 The layer runs in libmoe.so (hand-written HIP kernels behind the C ABI in
-include/moe.h); this package is its Python binding. Importing it loads the
-library and fails if it has not been built.
+include/moe.h); this package is its Python binding. The library is loaded on
+first use (or by load()), and every call raises if it has not been built;
+there is no fallback.
 """
-from ._lib import (MOE_BF16, MOE_EHIP, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_F32,
-                   MOE_MAX_EXPERTS, MOE_OK, MoeError, header_functions, load, moe_combine,
-                   moe_expert_ffn, moe_forward, moe_permute, moe_route, moe_set_ffn_variant,
-                   moe_set_stage_events, moe_workspace_bytes, strerror, workspace)
+from ._lib import (MOE_BF16, MOE_BF16_PACKED, MOE_EHIP, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE,
+                   MOE_F32, MOE_MAX_EXPERTS, MOE_OK, MoeError, PackedWeights, header_functions,
+                   load, moe_combine, moe_expert_ffn, moe_forward, moe_pack_weight, moe_permute,
+                   moe_route, moe_set_ffn_variant, moe_set_stage_events, moe_workspace_bytes,
+                   strerror, workspace)
 
-load()
-
-__all__ = ["MOE_BF16", "MOE_EHIP", "MOE_EINVAL", "MOE_ENOTSUP", "MOE_EWORKSPACE", "MOE_F32",
-           "MOE_MAX_EXPERTS", "MOE_OK", "MoeError", "header_functions", "load", "moe_combine",
-           "moe_expert_ffn", "moe_forward", "moe_permute", "moe_route", "moe_set_ffn_variant",
+__all__ = ["MOE_BF16", "MOE_BF16_PACKED", "MOE_EHIP", "MOE_EINVAL", "MOE_ENOTSUP",
+           "MOE_EWORKSPACE", "MOE_F32", "MOE_MAX_EXPERTS", "MOE_OK", "MoeError", "PackedWeights",
+           "header_functions", "load", "moe_combine", "moe_expert_ffn", "moe_forward",
+           "moe_pack_weight", "moe_permute", "moe_route", "moe_set_ffn_variant",
            "moe_set_stage_events", "moe_workspace_bytes", "strerror", "workspace"]

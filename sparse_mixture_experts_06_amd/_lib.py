@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_BF16_PACKED = 0, 1, 2
 MOE_MAX_EXPERTS = 32
 
 _c_i64 = ctypes.c_int64
@@ -38,6 +38,7 @@ _SIGNATURES = {
     "moe_combine": (_c_int, [_vp, _vp, _vp, _c_i64, _c_int, _c_int, _vp, _c_int, _vp]),
     "moe_forward": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _c_int,
                              _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _c_sz, _vp]),
+    "moe_pack_weight": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_set_ffn_variant": (_c_int, [_c_int]),
     "moe_set_stage_events": (_c_int, [_vp, _c_int]),
 }
@@ -93,6 +94,15 @@ def _dtype_code(t: torch.dtype) -> int:
     raise ValueError(f"unsupported dtype {t} (float32 or bfloat16)")
 
 
+def _weight_code(t: torch.dtype, packed: bool) -> int:
+    code = _dtype_code(t)
+    if packed:
+        if code != MOE_BF16:
+            raise ValueError("packed weights are bfloat16 only")
+        return MOE_BF16_PACKED
+    return code
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -127,6 +137,29 @@ def moe_set_stage_events(events) -> None:
         return
     arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(int(e)) for e in events])
     _check("moe_set_stage_events", lib.moe_set_stage_events(arr, len(events)))
+
+
+def moe_pack_weight(w, out=None):
+    """Fragment-order copy of bf16 weights w [E, rows, cols] (see moe.h)."""
+    if w.dtype != torch.bfloat16 or w.dim() != 3:
+        raise ValueError("moe_pack_weight takes a bfloat16 tensor [E, rows, cols]")
+    E, rows, cols = w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    _need(out, "out", torch.bfloat16, (E, rows, cols), w.device)
+    st = load().moe_pack_weight(_ptr(w), MOE_BF16, E, rows, cols, _ptr(out), _stream(w.device))
+    _check("moe_pack_weight", st)
+    return out
+
+
+class PackedWeights:
+    """w1, w3, w2 in fragment order (moe_pack_weight), for moe_forward /
+    moe_expert_ffn with packed=True. Shapes are those of the originals."""
+
+    def __init__(self, w1, w3, w2):
+        self.w1 = moe_pack_weight(w1)
+        self.w3 = moe_pack_weight(w3)
+        self.w2 = moe_pack_weight(w2)
 
 
 def moe_workspace_bytes(T: int, d: int, ffn: int, E: int, k: int, dtype) -> int:
@@ -184,8 +217,9 @@ def moe_permute(topk_idx, E: int, counts=None, offsets=None, sorted_asg=None, as
     return counts, offsets, sorted_asg, asg_pos
 
 
-def moe_expert_ffn(x, w1, w3, w2, offsets, sorted_asg, k: int, y=None, ws=None):
-    """Returns y [T*k, d] float32 (unweighted expert outputs, grouped order)."""
+def moe_expert_ffn(x, w1, w3, w2, offsets, sorted_asg, k: int, y=None, ws=None, packed=False):
+    """Returns y [T*k, d] float32 (unweighted expert outputs, grouped order).
+    packed=True: w1/w3/w2 come from moe_pack_weight."""
     T, d = x.shape
     E, ffn, _ = w1.shape
     dev = x.device
@@ -196,9 +230,10 @@ def moe_expert_ffn(x, w1, w3, w2, offsets, sorted_asg, k: int, y=None, ws=None):
     if y is None:
         y = torch.empty(T * k, d, dtype=torch.float32, device=dev)
     _need(y, "y", torch.float32, (T * k, d), dev)
+    code = _weight_code(x.dtype, packed)
     if ws is None:
-        ws = workspace(T, d, ffn, E, k, x.dtype, dev)
-    st = load().moe_expert_ffn(_ptr(x), _dtype_code(x.dtype), _ptr(w1), _ptr(w3), _ptr(w2),
+        ws = workspace(T, d, ffn, E, k, code, dev)
+    st = load().moe_expert_ffn(_ptr(x), code, _ptr(w1), _ptr(w3), _ptr(w2),
                                _ptr(offsets), _ptr(sorted_asg), T, d, ffn, E, k, _ptr(y),
                                _ptr(ws), ws.numel(), _stream(dev))
     _check("moe_expert_ffn", st)
@@ -223,8 +258,9 @@ def moe_combine(y, asg_pos, topk_w, out=None, out_dtype=torch.float32):
 
 
 def moe_forward(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dtype=None,
-                ws=None, topk_idx_out=None, topk_w_out=None, counts_out=None):
-    """The whole layer; returns out [T, d] (dtype out_dtype, default x.dtype)."""
+                ws=None, topk_idx_out=None, topk_w_out=None, counts_out=None, packed=False):
+    """The whole layer; returns out [T, d] (dtype out_dtype, default x.dtype).
+    packed=True: w1/w3/w2 come from moe_pack_weight."""
     T, d = x.shape
     E, ffn, _ = w1.shape
     dev = x.device
@@ -242,9 +278,10 @@ def moe_forward(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dt
         _need(topk_w_out, "topk_w_out", torch.float32, (T, k), dev)
     if counts_out is not None:
         _need(counts_out, "counts_out", torch.int32, (E,), dev)
+    code = _weight_code(x.dtype, packed)
     if ws is None:
-        ws = workspace(T, d, ffn, E, k, x.dtype, dev)
-    st = load().moe_forward(_ptr(x), _dtype_code(x.dtype), _ptr(router), _ptr(logit_bias),
+        ws = workspace(T, d, ffn, E, k, code, dev)
+    st = load().moe_forward(_ptr(x), code, _ptr(router), _ptr(logit_bias),
                             _ptr(w1), _ptr(w3), _ptr(w2), T, d, ffn, E, k, _ptr(out),
                             _dtype_code(out.dtype), _ptr(topk_idx_out), _ptr(topk_w_out),
                             _ptr(counts_out), _ptr(ws), ws.numel(), _stream(dev))

@@ -20,9 +20,16 @@ struct Layout {
   size_t idx, w, counts, offsets, sorted, pos, h, y, total;
 };
 
+inline bool is_bf16(int dtype) { return dtype == MOE_BF16 || dtype == MOE_BF16_PACKED; }
+
+// float32 partial results the down projection may leave (split K); sized for
+// the streaming kernels so that the workspace does not depend on the variant
+int ws_splits(int64_t A, int dtype) { return is_bf16(dtype) ? moe::down_splits(1, A) : 1; }
+
 Layout layout(int64_t T, int d, int ffn, int E, int k, int dtype) {
   const size_t A = static_cast<size_t>(T) * static_cast<size_t>(k);
-  const size_t hb = (dtype == MOE_BF16) ? 2 : 4;
+  const size_t hb = is_bf16(dtype) ? 2 : 4;
+  const size_t ns = static_cast<size_t>(ws_splits(static_cast<int64_t>(A), dtype));
   Layout L;
   size_t o = 0;
   L.idx = o;     o = align256(o + A * 4);
@@ -32,13 +39,14 @@ Layout layout(int64_t T, int d, int ffn, int E, int k, int dtype) {
   L.sorted = o;  o = align256(o + A * 4);
   L.pos = o;     o = align256(o + A * 4);
   L.h = o;       o = align256(o + A * static_cast<size_t>(ffn) * hb);
-  L.y = o;       o = align256(o + A * static_cast<size_t>(d) * 4);
+  L.y = o;       o = align256(o + ns * A * static_cast<size_t>(d) * 4);
   L.total = o;
   return L;
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 inline bool valid_dtype(int t) { return t == MOE_F32 || t == MOE_BF16; }
+inline bool valid_weight_dtype(int t) { return valid_dtype(t) || t == MOE_BF16_PACKED; }
 
 int check_sizes(int64_t T, int E, int k) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E) return MOE_EINVAL;
@@ -48,9 +56,9 @@ int check_sizes(int64_t T, int E, int k) {
 
 int check_ffn_shape(int64_t T, int d, int ffn, int E, int k, int dtype) {
   if (d < 1 || ffn < 1) return MOE_EINVAL;
-  if (!valid_dtype(dtype)) return MOE_EINVAL;
+  if (!valid_weight_dtype(dtype)) return MOE_EINVAL;
   const int64_t A = T * k;
-  if (dtype == MOE_BF16) {
+  if (is_bf16(dtype)) {
     if (d % 64 != 0 || ffn % 64 != 0) return MOE_ENOTSUP;
     // worst-case tile grid of the tiled kernels must fit a 1-D launch
     const int64_t mt = (A + 127) / 128 + E;
@@ -70,28 +78,34 @@ inline void stage(int i, hipStream_t s) {
   if (g_nevents == 6 && g_events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(g_events[i]), s);
 }
 
+// gate/up then down; the down result is left as `nsplit_out` partial arrays
+// at `part` (the caller sums them: the combine, or moe_expert_ffn)
 int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
             const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d, int ffn, int E,
-            int k, float* y, void* h, hipStream_t s, bool with_events) {
+            int k, float* part, void* h, hipStream_t s, bool with_events, int* nsplit_out) {
   const int64_t A = T * k;
   hipError_t err;
-  if (dtype == MOE_BF16) {
-    err = moe::launch_gate_up_bf16(g_ffn_variant, static_cast<const uint16_t*>(x),
+  if (is_bf16(dtype)) {
+    const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
+    const bool packed = dtype == MOE_BF16_PACKED;
+    *nsplit_out = moe::down_splits(variant, A);
+    err = moe::launch_gate_up_bf16(variant, packed, static_cast<const uint16_t*>(x),
                                    static_cast<const uint16_t*>(w1),
                                    static_cast<const uint16_t*>(w3), offsets, sorted_asg, A, d,
                                    ffn, E, k, static_cast<uint16_t*>(h), s);
     if (err != hipSuccess) return MOE_EHIP;
     if (with_events) stage(3, s);
-    err = moe::launch_down_bf16(g_ffn_variant, static_cast<const uint16_t*>(h),
-                                static_cast<const uint16_t*>(w2), offsets, A, d, ffn, E, y, s);
+    err = moe::launch_down_bf16(variant, packed, static_cast<const uint16_t*>(h),
+                                static_cast<const uint16_t*>(w2), offsets, A, d, ffn, E, part, s);
   } else {
+    *nsplit_out = 1;
     err = moe::launch_gate_up_f32(static_cast<const float*>(x), static_cast<const float*>(w1),
                                   static_cast<const float*>(w3), offsets, sorted_asg, A, d, ffn,
                                   E, k, static_cast<float*>(h), s);
     if (err != hipSuccess) return MOE_EHIP;
     if (with_events) stage(3, s);
     err = moe::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w2),
-                               offsets, A, d, ffn, E, y, s);
+                               offsets, A, d, ffn, E, part, s);
   }
   return hip_status(err);
 }
@@ -113,7 +127,7 @@ const char* moe_strerror(int status) {
 }
 
 size_t moe_workspace_bytes(int64_t T, int d, int ffn, int E, int k, int dtype) {
-  if (check_sizes(T, E, k) != MOE_OK || d < 1 || ffn < 1 || !valid_dtype(dtype)) return 0;
+  if (check_sizes(T, E, k) != MOE_OK || d < 1 || ffn < 1 || !valid_weight_dtype(dtype)) return 0;
   return layout(T, d, ffn, E, k, dtype).total;
 }
 
@@ -152,13 +166,25 @@ int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, con
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!x || !w1 || !w3 || !w2 || !offsets || !sorted_asg || !y) return MOE_EINVAL;
-  if (!ws || ws_bytes < layout(T, d, ffn, E, k, dtype).total) return MOE_EWORKSPACE;
-  if (dtype == MOE_BF16 &&
+  const Layout L = layout(T, d, ffn, E, k, dtype);
+  if (!ws || ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (is_bf16(dtype) &&
       !(aligned16(x) && aligned16(w1) && aligned16(w3) && aligned16(w2) && aligned16(ws) &&
         aligned16(y)))
     return MOE_ENOTSUP;
-  return run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, ws,
-                 static_cast<hipStream_t>(stream), false);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const int64_t A = T * k;
+  const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
+  const int nsplit = is_bf16(dtype) ? moe::down_splits(variant, A) : 1;
+  float* part = nsplit > 1 ? reinterpret_cast<float*>(base + L.y) : y;
+  int used = 1;
+  st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, part, base + L.h, s,
+               false, &used);
+  if (st != MOE_OK) return st;
+  if (used > 1)
+    return hip_status(moe::launch_sum_partials(part, used, A * static_cast<int64_t>(d), y, s));
+  return MOE_OK;
 }
 
 int moe_combine(const float* y, const int32_t* asg_pos, const float* topk_w, int64_t T, int d,
@@ -167,8 +193,8 @@ int moe_combine(const float* y, const int32_t* asg_pos, const float* topk_w, int
   if (T > kMaxAssignments / k) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   if (!y || !asg_pos || !topk_w || !out) return MOE_EINVAL;
-  return hip_status(moe::launch_combine(y, asg_pos, topk_w, T, d, k, out, out_dtype == MOE_BF16,
-                                        static_cast<hipStream_t>(stream)));
+  return hip_status(moe::launch_combine(y, 1, asg_pos, topk_w, T, d, k, out,
+                                        out_dtype == MOE_BF16, static_cast<hipStream_t>(stream)));
 }
 
 int moe_forward(const void* x, int dtype, const float* router, const float* logit_bias,
@@ -184,7 +210,7 @@ int moe_forward(const void* x, int dtype, const float* router, const float* logi
   if (T > 0 && (!x || !router || !w1 || !w3 || !w2 || !out)) return MOE_EINVAL;
   const Layout L = layout(T, d, ffn, E, k, dtype);
   if (!ws || ws_bytes < L.total) return MOE_EWORKSPACE;
-  if (dtype == MOE_BF16 && T > 0 &&
+  if (is_bf16(dtype) && T > 0 &&
       !(aligned16(x) && aligned16(w1) && aligned16(w3) && aligned16(w2) && aligned16(ws)))
     return MOE_ENOTSUP;
 
@@ -200,7 +226,7 @@ int moe_forward(const void* x, int dtype, const float* router, const float* logi
   float* y = reinterpret_cast<float*>(base + L.y);
 
   stage(0, s);
-  if (T > 0 && moe::launch_route(x, dtype == MOE_BF16, router, logit_bias, T, d, E, k, nullptr,
+  if (T > 0 && moe::launch_route(x, is_bf16(dtype), router, logit_bias, T, d, E, k, nullptr,
                                  idx, w, s) != hipSuccess)
     return MOE_EHIP;
   stage(1, s);
@@ -211,13 +237,31 @@ int moe_forward(const void* x, int dtype, const float* router, const float* logi
     for (int i = 3; i < 6; ++i) stage(i, s);
     return MOE_OK;
   }
-  st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, h, s, true);
+  int nsplit = 1;
+  st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, h, s, true, &nsplit);
   if (st != MOE_OK) return st;
   stage(4, s);
-  if (moe::launch_combine(y, asg_pos, w, T, d, k, out, out_dtype == MOE_BF16, s) != hipSuccess)
+  if (moe::launch_combine(y, nsplit, asg_pos, w, T, d, k, out, out_dtype == MOE_BF16, s) !=
+      hipSuccess)
     return MOE_EHIP;
   stage(5, s);
   return MOE_OK;
+}
+
+int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* out,
+                    void* stream) {
+  if (dtype != MOE_BF16) return MOE_EINVAL;
+  if (E < 1 || E > MOE_MAX_EXPERTS || rows < 1 || cols < 1) return MOE_EINVAL;
+  if (rows % 16 != 0 || cols % 32 != 0) return MOE_ENOTSUP;
+  if (!w || !out) return MOE_EINVAL;
+  if (!aligned16(w) || !aligned16(out)) return MOE_ENOTSUP;
+  const size_t bytes = static_cast<size_t>(E) * rows * cols * 2;
+  const char* a = static_cast<const char*>(w);
+  const char* b = static_cast<const char*>(out);
+  if (a < b + bytes && b < a + bytes) return MOE_EINVAL;  // must not overlap
+  return hip_status(moe::launch_pack_bf16(static_cast<const uint16_t*>(w), E, rows, cols,
+                                          static_cast<uint16_t*>(out),
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int moe_set_ffn_variant(int variant) {

@@ -4,8 +4,11 @@
 //   out[t] = sum_{j<k} w[t*k+j] * y[asg_pos[t*k+j]]
 // A gather, not a scatter: no atomics, float32 accumulation in slot order,
 // so the result is deterministic and a token whose weights are unchanged
-// gives bit-identical output. One workgroup per token row; 16-byte accesses
-// when d % 4 == 0.
+// gives bit-identical output. Workgroup (t, c) handles columns
+// [c*1024, (c+1)*1024) of token t, 4 per thread with 16-byte accesses when
+// d % 4 == 0, so all of a thread's k*nsplit loads are in flight together. When the down projection left its result as nsplit
+// partial sums (split K), each y row is first summed over the splits in
+// split order.
 #include "common.h"
 
 namespace moe {
@@ -15,17 +18,22 @@ constexpr int kThreads = 256;
 
 template <bool OUT_BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y,
+                                                          int nsplit, int64_t pstride,
                                                           const int32_t* __restrict__ asg_pos,
                                                           const float* __restrict__ w, int d,
                                                           int k, void* __restrict__ out) {
   const int64_t t = blockIdx.x;
+  const int col0 = blockIdx.y * kThreads * 4;
+  const int col1 = min(d, col0 + kThreads * 4);
   if constexpr (VEC) {
-    for (int i = threadIdx.x * 4; i < d; i += kThreads * 4) {
+    for (int i = col0 + threadIdx.x * 4; i < col1; i += kThreads * 4) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int j = 0; j < k; ++j) {
         const int64_t p = asg_pos[t * k + j];
         const float wt = w[t * k + j];
-        const f32x4 v = *reinterpret_cast<const f32x4*>(y + p * d + i);
+        f32x4 v = *reinterpret_cast<const f32x4*>(y + p * d + i);
+        for (int sp = 1; sp < nsplit; ++sp)
+          v += *reinterpret_cast<const f32x4*>(y + sp * pstride + p * d + i);
         acc[0] = fmaf(wt, v[0], acc[0]);
         acc[1] = fmaf(wt, v[1], acc[1]);
         acc[2] = fmaf(wt, v[2], acc[2]);
@@ -41,11 +49,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
       }
     }
   } else {
-    for (int i = threadIdx.x; i < d; i += kThreads) {
+    for (int i = col0 + threadIdx.x; i < col1; i += kThreads) {
       float acc = 0.0f;
       for (int j = 0; j < k; ++j) {
         const int64_t p = asg_pos[t * k + j];
-        acc = fmaf(w[t * k + j], y[p * d + i], acc);
+        float v = y[p * d + i];
+        for (int sp = 1; sp < nsplit; ++sp) v += y[sp * pstride + p * d + i];
+        acc = fmaf(w[t * k + j], v, acc);
       }
       if constexpr (OUT_BF16) {
         static_cast<uint16_t*>(out)[t * d + i] = f32_to_bf16(acc);
@@ -56,29 +66,49 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
   }
 }
 
+__global__ __launch_bounds__(kThreads) void sum_partials_kernel(const float* __restrict__ part,
+                                                               int nsplit, int64_t n,
+                                                               float* __restrict__ y) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads) {
+    float v = part[i];
+    for (int sp = 1; sp < nsplit; ++sp) v += part[sp * n + i];
+    y[i] = v;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_combine(const float* y, const int32_t* asg_pos, const float* w, int64_t T,
-                          int d, int k, void* out, int out_bf16, hipStream_t s) {
+hipError_t launch_combine(const float* y, int nsplit, const int32_t* asg_pos, const float* w,
+                          int64_t T, int d, int k, void* out, int out_bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  const int64_t pstride = T * k * static_cast<int64_t>(d);
   const bool vec = (d % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(out) & (out_bf16 ? 7 : 15)) == 0);
-  const dim3 grid(static_cast<unsigned>(T));
+  const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>((d + kThreads * 4 - 1) / (kThreads * 4)));
   if (out_bf16) {
     if (vec)
-      hipLaunchKernelGGL((combine_kernel<true, true>), grid, dim3(kThreads), 0, s, y, asg_pos, w,
-                         d, k, out);
+      hipLaunchKernelGGL((combine_kernel<true, true>), grid, dim3(kThreads), 0, s, y, nsplit,
+                         pstride, asg_pos, w, d, k, out);
     else
-      hipLaunchKernelGGL((combine_kernel<true, false>), grid, dim3(kThreads), 0, s, y, asg_pos,
-                         w, d, k, out);
+      hipLaunchKernelGGL((combine_kernel<true, false>), grid, dim3(kThreads), 0, s, y, nsplit,
+                         pstride, asg_pos, w, d, k, out);
   } else {
     if (vec)
-      hipLaunchKernelGGL((combine_kernel<false, true>), grid, dim3(kThreads), 0, s, y, asg_pos,
-                         w, d, k, out);
+      hipLaunchKernelGGL((combine_kernel<false, true>), grid, dim3(kThreads), 0, s, y, nsplit,
+                         pstride, asg_pos, w, d, k, out);
     else
-      hipLaunchKernelGGL((combine_kernel<false, false>), grid, dim3(kThreads), 0, s, y, asg_pos,
-                         w, d, k, out);
+      hipLaunchKernelGGL((combine_kernel<false, false>), grid, dim3(kThreads), 0, s, y, nsplit,
+                         pstride, asg_pos, w, d, k, out);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_partials(const float* part, int nsplit, int64_t n, float* y, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t want = (n + kThreads - 1) / kThreads;
+  const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(sum_partials_kernel, dim3(blocks), dim3(kThreads), 0, s, part, nsplit, n, y);
   return hipGetLastError();
 }
 

@@ -56,14 +56,20 @@ hipError_t launch_permute(const int32_t* idx, int64_t A, int E, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_asg, int32_t* asg_pos,
                           hipStream_t s);
 
-// bf16 experts: gate/up (+SiLU*mul) -> h [A, ffn] bf16, down -> y [A, d] f32
-hipError_t launch_gate_up_bf16(int variant, const uint16_t* x, const uint16_t* w1,
+// bf16 experts: gate/up (+SiLU*mul) -> h [A, ffn] bf16, down -> y [A, d] f32.
+// `variant` is resolved (1 streaming, 2 tiled); `packed` selects the
+// fragment-order weight layout. The down kernel writes down_splits(variant, A)
+// float32 partial results [nsplit, A, d] whose sum (in split order) is y.
+hipError_t launch_gate_up_bf16(int variant, bool packed, const uint16_t* x, const uint16_t* w1,
                                const uint16_t* w3, const int32_t* offsets,
                                const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
                                int k, uint16_t* h, hipStream_t s);
-hipError_t launch_down_bf16(int variant, const uint16_t* h, const uint16_t* w2,
-                            const int32_t* offsets, int64_t A, int d, int ffn, int E, float* y,
+hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const uint16_t* w2,
+                            const int32_t* offsets, int64_t A, int d, int ffn, int E, float* part,
                             hipStream_t s);
+int down_splits(int variant, int64_t A);
+// standard [E, R, C] bf16 -> fragment order (16-row x 32-column fragments)
+hipError_t launch_pack_bf16(const uint16_t* w, int E, int R, int C, uint16_t* out, hipStream_t s);
 
 // f32 experts: same steps in float32 (h stays float32)
 hipError_t launch_gate_up_f32(const float* x, const float* w1, const float* w3,
@@ -72,8 +78,12 @@ hipError_t launch_gate_up_f32(const float* x, const float* w1, const float* w3,
 hipError_t launch_down_f32(const float* h, const float* w2, const int32_t* offsets, int64_t A,
                            int d, int ffn, int E, float* y, hipStream_t s);
 
-hipError_t launch_combine(const float* y, const int32_t* asg_pos, const float* w, int64_t T,
-                          int d, int k, void* out, int out_bf16, hipStream_t s);
+// out[t] = sum_j w[t*k+j] * y[asg_pos[t*k+j]], with y the split-order sum of
+// nsplit partial arrays of A x d floats (A = T*k) starting at `part`
+hipError_t launch_combine(const float* part, int nsplit, const int32_t* asg_pos, const float* w,
+                          int64_t T, int d, int k, void* out, int out_bf16, hipStream_t s);
+// y[i] = sum_s part[s*n + i] in split order
+hipError_t launch_sum_partials(const float* part, int nsplit, int64_t n, float* y, hipStream_t s);
 
 // Resolved expert-FFN kernel family for these sizes (1 streaming, 2 tiled).
 int choose_ffn_variant(int requested, int64_t A, int E);

@@ -1,6 +1,7 @@
 // Expert SwiGLU on bf16 MFMA (nnterp Mixtral page, support(): the down
-// projection receives act(gate) * up with act = SiLU; "expert_outputs needs
-// the default experts implementation": the 8 experts are one stacked module).
+// projection receives act(gate) * up with act = SiLU; section "expert_outputs
+// needs the default experts implementation": the 8 experts are one stacked
+// module).
 //
 //   gate/up:  h[p, n] = silu(sum_i x[r,i] w1[e,n,i]) * (sum_i x[r,i] w3[e,n,i])
 //             r = sorted_asg[p] / k,  p in expert e's grouped range; h is bf16
@@ -9,15 +10,27 @@
 // Both are grouped GEMMs whose two operands are "row x K" with K contiguous
 // (weight rows n, token rows m), so the weights are the MFMA A operand and the
 // tokens the B operand: D[n][m] = W[n,:] . X[m,:]. With
-// v_mfma_f32_16x16x32_bf16 a lane holds 8 consecutive K values of one row for
-// either operand, and four consecutive n of one token in the result, which
-// gives 8-byte (h) and 16-byte (y) row stores.
+// v_mfma_f32_16x16x32_bf16 a lane (r = lane % 16, g = lane / 16) holds the 8
+// values k = 8g .. 8g+7 of row r of either operand, and the result rows
+// 4g .. 4g+3 of token column r, which gives 8-byte (h) and 16-byte (y) stores.
 //
-// Two families:
-//  * streaming (few rows per expert, decode): no LDS staging. A workgroup owns
-//    16 weight rows (of w1 and w3 together for gate/up); its 4 waves split K
-//    and stream those rows once from HBM with 16-byte loads, reusing each load
-//    for up to 32 token rows; partial sums meet in LDS.
+// Weight layouts (template parameter PACKED):
+//  * standard: w[e][n][k], k contiguous.
+//  * fragment order (moe_pack_weight): the matrix is cut into 16-row x 32-k
+//    fragments, each stored as 1 KiB in MFMA lane order (lane l's 8 values at
+//    byte 16*l), fragments ordered (expert, row tile, k step). A wave's load
+//    of one A fragment is then one contiguous KiB, the friendliest access for
+//    HBM3E; the values are the same, only their order differs.
+//
+// Two kernel families:
+//  * streaming (few rows per expert, decode): no LDS staging of weights.
+//    gate/up: a workgroup owns RT 16-row tiles of w1 and w3; its 4 waves split
+//    K and stream those rows once with 16-byte loads, each token fragment
+//    serving 2*RT weight fragments; the partial sums meet in LDS.
+//    down: every wave is independent: RT 16-row tiles of w2 over 1/nsplit of
+//    K, written as a float32 partial; the partials are summed later in a
+//    fixed order (by the combine, or by moe_expert_ffn before it returns).
+//    With fragment-order weights the weight loads are non-temporal.
 //  * tiled (many rows per expert, prefill): 128 weight rows x 128 token rows
 //    x 64 K per step, double-buffered in LDS with an XOR swizzle of the
 //    16-byte chunks (conflict-free ds_read_b128 for the MFMA fragments); 4
@@ -30,24 +43,66 @@
 namespace moe {
 namespace {
 
+// element offset of w[e][n][k] (k a multiple of 8) in either layout
+template <bool PACKED>
+__device__ __forceinline__ size_t wofs(int e, int n, int k, int N, int K) {
+  if constexpr (PACKED) {
+    return ((static_cast<size_t>(e) * (N >> 4) + (n >> 4)) * static_cast<size_t>(K >> 5) +
+            (k >> 5)) * 512 + ((((k & 31) >> 3) << 4) + (n & 15)) * 8;
+  } else {
+    return (static_cast<size_t>(e) * N + n) * K + k;
+  }
+}
+
+// elements between one lane's values of consecutive 32-wide k steps
+template <bool PACKED>
+constexpr int kStep32() { return PACKED ? 512 : 32; }
+
+// 16-byte weight load; NT marks it non-temporal (streamed once, not kept)
+template <bool NT>
+__device__ __forceinline__ u32x4 ldw(const uint16_t* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  } else {
+    return ldg16(p);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// weight packing
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ w, int64_t chunks,
+                                                   int R, int C, uint16_t* __restrict__ out) {
+  const int nrt = R >> 4;
+  const int S = C >> 5;
+  for (int64_t o = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; o < chunks;
+       o += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t f = o >> 6;
+    const int lane = static_cast<int>(o & 63);
+    const int s = static_cast<int>(f % S);
+    const int64_t t = f / S;
+    const int rt = static_cast<int>(t % nrt);
+    const int64_t e = t / nrt;
+    const uint16_t* src = w + (e * R + rt * 16 + (lane & 15)) * C + s * 32 + (lane >> 4) * 8;
+    *reinterpret_cast<u32x4*>(out + o * 8) = ldg16(src);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // streaming kernels
 // ----------------------------------------------------------------------------
 constexpr int kStreamWaves = 4;
-constexpr int kStreamUnroll = 4;
 
-// GATE_UP: act = x [T, K=d] with rows gathered through sorted_asg / ktop,
-//          wa = w1, wb = w3 (each [E, N=ffn, K]), out = h bf16 [A, N].
-// !GATE_UP: act = h [A, K=ffn] in grouped order, wa = w2 [E, N=d, K],
-//          out = y f32 [A, N].
-template <bool GATE_UP>
-__global__ __launch_bounds__(kWave* kStreamWaves) void stream_kernel(
-    const uint16_t* __restrict__ act, const uint16_t* __restrict__ wa,
-    const uint16_t* __restrict__ wb, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_asg, int K, int N, int ktop, void* __restrict__ out) {
-  constexpr int NM = GATE_UP ? 2 : 1;
+// x [T, K=d] rows gathered through sorted_asg / ktop; w1, w3 [E, N=ffn, K];
+// h bf16 [A, N]. Token rows go 32 at a time (two 16-row MFMA column tiles;
+// the second is skipped when the rows run out).
+template <int RT, int U, bool PACKED, bool NT>
+__global__ __launch_bounds__(kWave* kStreamWaves) void gate_up_stream_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
+    const uint16_t* __restrict__ w3, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_asg, int K, int N, int ktop, uint16_t* __restrict__ h) {
   const int e = blockIdx.y;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * (16 * RT);
   const int beg = offsets[e];
   const int M = offsets[e + 1] - beg;
   if (M <= 0) return;
@@ -59,98 +114,110 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void stream_kernel(
   const int S = K / 32;
   const int s_lo = (wave * S) / kStreamWaves;
   const int s_hi = ((wave + 1) * S) / kStreamWaves;
-  const size_t wrow = (static_cast<size_t>(e) * N + n0 + r) * K + g * 8;
-  const uint16_t* pa = wa + wrow;
-  const uint16_t* pb = GATE_UP ? wb + wrow : wa + wrow;
+  constexpr int ST = kStep32<PACKED>();
+  const uint16_t* pg[RT];
+  const uint16_t* pu[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const size_t o = wofs<PACKED>(e, n0 + t * 16 + r, g * 8, N, K);
+    pg[t] = w1 + o;
+    pu[t] = w3 + o;
+  }
 
-  __shared__ f32x4 red[kStreamWaves - 1][NM][2][kWave];
+  __shared__ f32x4 red[kStreamWaves - 1][2][RT][2][kWave];
 
   for (int mb = 0; mb < M; mb += 32) {
     const bool two = (M - mb) > 16;  // wave-uniform
     const int m0 = min(mb + r, M - 1);
     const int m1 = min(mb + 16 + r, M - 1);
-    int64_t row0, row1;
-    if constexpr (GATE_UP) {
-      row0 = sorted_asg[beg + m0] / ktop;
-      row1 = sorted_asg[beg + m1] / ktop;
-    } else {
-      row0 = beg + m0;
-      row1 = beg + m1;
-    }
-    const uint16_t* px0 = act + row0 * K + g * 8;
-    const uint16_t* px1 = act + row1 * K + g * 8;
+    const uint16_t* px0 = x + static_cast<int64_t>(sorted_asg[beg + m0] / ktop) * K + g * 8;
+    const uint16_t* px1 = x + static_cast<int64_t>(sorted_asg[beg + m1] / ktop) * K + g * 8;
 
-    f32x4 acc[NM][2];
+    f32x4 ag[RT][2], au[RT][2];
 #pragma unroll
-    for (int a = 0; a < NM; ++a) acc[a][0] = acc[a][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < RT; ++t)
+      ag[t][0] = ag[t][1] = au[t][0] = au[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int s = s_lo;
-    for (; s + kStreamUnroll <= s_hi; s += kStreamUnroll) {
-      u32x4 A0[kStreamUnroll], A1[kStreamUnroll], B0[kStreamUnroll], B1[kStreamUnroll];
+    for (; s + U <= s_hi; s += U) {
+      u32x4 G[U][RT], V[U][RT], B0[U], B1[U];
 #pragma unroll
-      for (int u = 0; u < kStreamUnroll; ++u) {
-        const int off = (s + u) * 32;
-        A0[u] = ldg16(pa + off);
-        if constexpr (GATE_UP) A1[u] = ldg16(pb + off);
-        B0[u] = ldg16(px0 + off);
-        B1[u] = two ? ldg16(px1 + off) : u32x4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          G[u][t] = ldw<NT>(pg[t] + (s + u) * ST);
+          V[u][t] = ldw<NT>(pu[t] + (s + u) * ST);
+        }
+        B0[u] = ldg16(px0 + (s + u) * 32);
+        B1[u] = two ? ldg16(px1 + (s + u) * 32) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < kStreamUnroll; ++u) {
-        acc[0][0] = mfma16x16x32(A0[u], B0[u], acc[0][0]);
-        if constexpr (GATE_UP) acc[1][0] = mfma16x16x32(A1[u], B0[u], acc[1][0]);
-        if (two) {
-          acc[0][1] = mfma16x16x32(A0[u], B1[u], acc[0][1]);
-          if constexpr (GATE_UP) acc[1][1] = mfma16x16x32(A1[u], B1[u], acc[1][1]);
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          ag[t][0] = mfma16x16x32(G[u][t], B0[u], ag[t][0]);
+          au[t][0] = mfma16x16x32(V[u][t], B0[u], au[t][0]);
+          if (two) {
+            ag[t][1] = mfma16x16x32(G[u][t], B1[u], ag[t][1]);
+            au[t][1] = mfma16x16x32(V[u][t], B1[u], au[t][1]);
+          }
         }
       }
     }
     for (; s < s_hi; ++s) {
-      const int off = s * 32;
-      const u32x4 a0 = ldg16(pa + off);
-      const u32x4 b0 = ldg16(px0 + off);
-      acc[0][0] = mfma16x16x32(a0, b0, acc[0][0]);
-      u32x4 a1 = a0;
-      if constexpr (GATE_UP) {
-        a1 = ldg16(pb + off);
-        acc[1][0] = mfma16x16x32(a1, b0, acc[1][0]);
-      }
-      if (two) {
-        const u32x4 b1 = ldg16(px1 + off);
-        acc[0][1] = mfma16x16x32(a0, b1, acc[0][1]);
-        if constexpr (GATE_UP) acc[1][1] = mfma16x16x32(a1, b1, acc[1][1]);
+      const u32x4 b0 = ldg16(px0 + s * 32);
+      const u32x4 b1 = two ? ldg16(px1 + s * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const u32x4 gw = ldw<NT>(pg[t] + s * ST);
+        const u32x4 uw = ldw<NT>(pu[t] + s * ST);
+        ag[t][0] = mfma16x16x32(gw, b0, ag[t][0]);
+        au[t][0] = mfma16x16x32(uw, b0, au[t][0]);
+        if (two) {
+          ag[t][1] = mfma16x16x32(gw, b1, ag[t][1]);
+          au[t][1] = mfma16x16x32(uw, b1, au[t][1]);
+        }
       }
     }
 
     if (wave > 0) {
 #pragma unroll
-      for (int a = 0; a < NM; ++a)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) red[wave - 1][a][t][lane] = acc[a][t];
+      for (int t = 0; t < RT; ++t) {
+        red[wave - 1][0][t][0][lane] = ag[t][0];
+        red[wave - 1][1][t][0][lane] = au[t][0];
+        if (two) {
+          red[wave - 1][0][t][1][lane] = ag[t][1];
+          red[wave - 1][1][t][1][lane] = au[t][1];
+        }
+      }
     }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
       for (int w = 0; w < kStreamWaves - 1; ++w)
 #pragma unroll
-        for (int a = 0; a < NM; ++a)
+        for (int t = 0; t < RT; ++t) {
+          ag[t][0] += red[w][0][t][0][lane];
+          au[t][0] += red[w][1][t][0][lane];
+          if (two) {
+            ag[t][1] += red[w][0][t][1][lane];
+            au[t][1] += red[w][1][t][1][lane];
+          }
+        }
+      // lane holds token column r and weight rows 4g .. 4g+3 of each tile
 #pragma unroll
-          for (int t = 0; t < 2; ++t) acc[a][t] += red[w][a][t][lane];
-      // lane holds token column r and weight rows n0 + 4g .. n0 + 4g + 3
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int m = mb + t * 16 + r;
+      for (int c = 0; c < 2; ++c) {
+        const int m = mb + c * 16 + r;
         if (m < M) {
-          const size_t o = static_cast<size_t>(beg + m) * N + n0 + 4 * g;
-          if constexpr (GATE_UP) {
-            const f32x4 gt = acc[0][t];
-            const f32x4 up = acc[1][t];
+#pragma unroll
+          for (int t = 0; t < RT; ++t) {
+            const f32x4 gt = ag[t][c];
+            const f32x4 up = au[t][c];
             uint2 v;
             v.x = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
             v.y = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = v;
-          } else {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = acc[0][t];
+            *reinterpret_cast<uint2*>(h + static_cast<size_t>(beg + m) * N + n0 + t * 16 + 4 * g) =
+                v;
           }
         }
       }
@@ -158,6 +225,92 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void stream_kernel(
     __syncthreads();
   }
 }
+
+// h [A, K=ffn] in grouped order; w2 [E, N=d, K]; part [nsplit, A, N] f32.
+// Wave task = (row group of RT 16-row tiles, split sp); no barriers, so a
+// wave with no task simply returns.
+template <int RT, int U, bool PACKED, bool NT>
+__global__ __launch_bounds__(kWave* kStreamWaves) void down_stream_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w2,
+    const int32_t* __restrict__ offsets, int K, int N, int A, int nsplit,
+    float* __restrict__ part) {
+  const int e = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int task = blockIdx.x * kStreamWaves + static_cast<int>(threadIdx.x) / kWave;
+  const int ngroups = N / (16 * RT);
+  if (task >= ngroups * nsplit) return;
+  const int sp = task % nsplit;
+  const int n0 = (task / nsplit) * (16 * RT);
+  const int beg = offsets[e];
+  const int M = offsets[e + 1] - beg;
+  if (M <= 0) return;
+
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int S = K / 32;
+  const int s_lo = (sp * S) / nsplit;
+  const int s_hi = ((sp + 1) * S) / nsplit;
+  constexpr int ST = kStep32<PACKED>();
+  const uint16_t* pw[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) pw[t] = w2 + wofs<PACKED>(e, n0 + t * 16 + r, g * 8, N, K);
+  float* dst = part + static_cast<size_t>(sp) * A * N;
+
+  for (int mb = 0; mb < M; mb += 32) {
+    const bool two = (M - mb) > 16;
+    const uint16_t* px0 = h + static_cast<int64_t>(beg + min(mb + r, M - 1)) * K + g * 8;
+    const uint16_t* px1 = h + static_cast<int64_t>(beg + min(mb + 16 + r, M - 1)) * K + g * 8;
+    f32x4 acc[RT][2];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int s = s_lo;
+    for (; s + U <= s_hi; s += U) {
+      u32x4 W[U][RT], B0[U], B1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) W[u][t] = ldw<NT>(pw[t] + (s + u) * ST);
+        B0[u] = ldg16(px0 + (s + u) * 32);
+        B1[u] = two ? ldg16(px1 + (s + u) * 32) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          acc[t][0] = mfma16x16x32(W[u][t], B0[u], acc[t][0]);
+          if (two) acc[t][1] = mfma16x16x32(W[u][t], B1[u], acc[t][1]);
+        }
+    }
+    for (; s < s_hi; ++s) {
+      const u32x4 b0 = ldg16(px0 + s * 32);
+      const u32x4 b1 = two ? ldg16(px1 + s * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const u32x4 w = ldw<NT>(pw[t] + s * ST);
+        acc[t][0] = mfma16x16x32(w, b0, acc[t][0]);
+        if (two) acc[t][1] = mfma16x16x32(w, b1, acc[t][1]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int m = mb + c * 16 + r;
+      if (m < M) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          *reinterpret_cast<f32x4*>(dst + static_cast<size_t>(beg + m) * N + n0 + t * 16 + 4 * g) =
+              acc[t][c];
+      }
+    }
+  }
+}
+
+// tuned on the Mixtral-8x7B decode shapes (weights streamed once per call)
+constexpr int kGateUpRT = 1, kGateUpU = 8;
+constexpr int kDownRT = 2, kDownU = 8;
+// non-temporal weight loads pay off when each wave load is one contiguous KiB
+// (fragment order); on the standard layout's 16 rows x 64 B pattern they cost
+template <bool PACKED>
+constexpr bool kStreamNT = PACKED;
 
 // ----------------------------------------------------------------------------
 // tiled kernels
@@ -203,10 +356,12 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
-// GATE_UP: the 128 weight rows of a tile are w1 rows [n, n+32), w3 rows
-// [n, n+32), w1 rows [n+32, n+64), w3 rows [n+32, n+64) with n = nt*64, so
-// wave column wn holds gate and up for the same 32 h-columns.
-template <bool GATE_UP>
+// GATE_UP: act = x (rows gathered), wa = w1, wb = w3, out = h bf16 [A, N=ffn];
+// the 128 weight rows of a tile are w1 rows [n, n+32), w3 rows [n, n+32),
+// w1 rows [n+32, n+64), w3 rows [n+32, n+64) with n = nt*64, so wave column
+// wn holds gate and up for the same 32 h-columns.
+// !GATE_UP: act = h (grouped rows), wa = w2, out = y f32 [A, N=d].
+template <bool GATE_UP, bool PACKED>
 __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ wa,
     const uint16_t* __restrict__ wb, const int32_t* __restrict__ offsets,
@@ -227,6 +382,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
   // this thread moves 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 j, j < 4
   const int lrow = tid >> 3;
   const int lch = tid & 7;
+  constexpr int WSTEP = PACKED ? 1024 : BK;  // weight elements per BK advance
   const uint16_t* gw[4];
   const uint16_t* gx[4];
   int so[4];
@@ -242,7 +398,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
       base = wa;
       n = min(nt * BN + R, N - 1);
     }
-    gw[j] = base + (static_cast<size_t>(e) * N + n) * K + lch * 8;
+    gw[j] = base + wofs<PACKED>(e, n, lch * 8, N, K);
     const int mm = min(m0 + R, M - 1);
     int64_t row;
     if constexpr (GATE_UP) {
@@ -280,11 +436,10 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
     const int cur = kb & 1;
     const bool more = (kb + 1) < nk;
     if (more) {
-      const int off = (kb + 1) * BK;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        rw[j] = ldg16(gw[j] + off);
-        rx[j] = ldg16(gx[j] + off);
+        rw[j] = ldg16(gw[j] + static_cast<size_t>(kb + 1) * WSTEP);
+        rx[j] = ldg16(gx[j] + (kb + 1) * BK);
       }
     }
 #pragma unroll
@@ -352,6 +507,58 @@ inline unsigned tiled_grid(int64_t A, int E, int ntn) {
   return static_cast<unsigned>((tiles + 7) / 8 * 8);
 }
 
+template <bool PACKED>
+hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
+                        const int32_t* offsets, const int32_t* sorted_asg, int64_t A, int d,
+                        int ffn, int E, int k, uint16_t* h, hipStream_t s) {
+  if (variant == 1) {
+    constexpr int rows = 16 * kGateUpRT;
+    if (ffn % rows != 0)
+      hipLaunchKernelGGL((gate_up_stream_kernel<1, kGateUpU, PACKED, kStreamNT<PACKED>>), dim3(ffn / 16, E),
+                         dim3(kWave * kStreamWaves), 0, s, x, w1, w3, offsets, sorted_asg, d, ffn,
+                         k, h);
+    else
+      hipLaunchKernelGGL((gate_up_stream_kernel<kGateUpRT, kGateUpU, PACKED, kStreamNT<PACKED>>),
+                         dim3(ffn / rows, E), dim3(kWave * kStreamWaves), 0, s, x, w1, w3,
+                         offsets, sorted_asg, d, ffn, k, h);
+  } else {
+    const int ntn = ffn / 64;
+    hipLaunchKernelGGL((tiled_kernel<true, PACKED>), dim3(tiled_grid(A, E, ntn)),
+                       dim3(kTiledThreads), 0, s, x, w1, w3, offsets, sorted_asg, d, ffn, E, k,
+                       static_cast<void*>(h), ntn);
+  }
+  return hipGetLastError();
+}
+
+template <bool PACKED>
+hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
+                     int64_t A, int d, int ffn, int E, float* part, hipStream_t s) {
+  if (variant == 1) {
+    const int nsplit = down_splits(1, A);
+    constexpr int rows = 16 * kDownRT;
+    if (d % rows != 0) {
+      const unsigned blocks =
+          static_cast<unsigned>((d / 16 * nsplit + kStreamWaves - 1) / kStreamWaves);
+      hipLaunchKernelGGL((down_stream_kernel<1, kDownU, PACKED, kStreamNT<PACKED>>), dim3(blocks, E),
+                         dim3(kWave * kStreamWaves), 0, s, h, w2, offsets, ffn, d,
+                         static_cast<int>(A), nsplit, part);
+    } else {
+      const unsigned blocks =
+          static_cast<unsigned>((d / rows * nsplit + kStreamWaves - 1) / kStreamWaves);
+      hipLaunchKernelGGL((down_stream_kernel<kDownRT, kDownU, PACKED, kStreamNT<PACKED>>), dim3(blocks, E),
+                         dim3(kWave * kStreamWaves), 0, s, h, w2, offsets, ffn, d,
+                         static_cast<int>(A), nsplit, part);
+    }
+  } else {
+    const int ntn = (d + BN - 1) / BN;
+    hipLaunchKernelGGL((tiled_kernel<false, PACKED>), dim3(tiled_grid(A, E, ntn)),
+                       dim3(kTiledThreads), 0, s, h, w2, w2, offsets,
+                       static_cast<const int32_t*>(nullptr), ffn, d, E, 1,
+                       static_cast<void*>(part), ntn);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int choose_ffn_variant(int requested, int64_t A, int E) {
@@ -360,38 +567,36 @@ int choose_ffn_variant(int requested, int64_t A, int E) {
   return (A <= static_cast<int64_t>(32) * E) ? 1 : 2;
 }
 
-hipError_t launch_gate_up_bf16(int variant, const uint16_t* x, const uint16_t* w1,
+int down_splits(int variant, int64_t A) {
+  // the streaming down kernel splits K two ways while its float32 partials
+  // stay small; the tiled kernel writes the final sums directly
+  return (variant == 1 && A <= 4096) ? 2 : 1;
+}
+
+hipError_t launch_pack_bf16(const uint16_t* w, int E, int R, int C, uint16_t* out, hipStream_t s) {
+  const int64_t chunks = static_cast<int64_t>(E) * R * C / 8;
+  if (chunks == 0) return hipSuccess;
+  const int64_t want = (chunks + 255) / 256;
+  const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(pack_kernel, dim3(blocks), dim3(256), 0, s, w, chunks, R, C, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_bf16(int variant, bool packed, const uint16_t* x, const uint16_t* w1,
                                const uint16_t* w3, const int32_t* offsets,
                                const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
                                int k, uint16_t* h, hipStream_t s) {
   if (A == 0) return hipSuccess;
-  if (choose_ffn_variant(variant, A, E) == 1) {
-    hipLaunchKernelGGL(stream_kernel<true>, dim3(ffn / 16, E), dim3(kWave * kStreamWaves), 0, s,
-                       x, w1, w3, offsets, sorted_asg, d, ffn, k, static_cast<void*>(h));
-  } else {
-    const int ntn = ffn / 64;
-    hipLaunchKernelGGL(tiled_kernel<true>, dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0,
-                       s, x, w1, w3, offsets, sorted_asg, d, ffn, E, k, static_cast<void*>(h),
-                       ntn);
-  }
-  return hipGetLastError();
+  return packed ? gate_up_impl<true>(variant, x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s)
+                : gate_up_impl<false>(variant, x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s);
 }
 
-hipError_t launch_down_bf16(int variant, const uint16_t* h, const uint16_t* w2,
-                            const int32_t* offsets, int64_t A, int d, int ffn, int E, float* y,
+hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const uint16_t* w2,
+                            const int32_t* offsets, int64_t A, int d, int ffn, int E, float* part,
                             hipStream_t s) {
   if (A == 0) return hipSuccess;
-  if (choose_ffn_variant(variant, A, E) == 1) {
-    hipLaunchKernelGGL(stream_kernel<false>, dim3(d / 16, E), dim3(kWave * kStreamWaves), 0, s,
-                       h, w2, w2, offsets, static_cast<const int32_t*>(nullptr), ffn, d, 1,
-                       static_cast<void*>(y));
-  } else {
-    const int ntn = (d + BN - 1) / BN;
-    hipLaunchKernelGGL(tiled_kernel<false>, dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0,
-                       s, h, w2, w2, offsets, static_cast<const int32_t*>(nullptr), ffn, d, E, 1,
-                       static_cast<void*>(y), ntn);
-  }
-  return hipGetLastError();
+  return packed ? down_impl<true>(variant, h, w2, offsets, A, d, ffn, E, part, s)
+                : down_impl<false>(variant, h, w2, offsets, A, d, ffn, E, part, s);
 }
 
 }  // namespace moe

@@ -4,18 +4,22 @@
 // the router renormalizes its top 2 in float32; support(): router_logits is
 // the router's linear output, before the scoring).
 //
-// Work split: one wave handles kTokensPerWave tokens at once, so each router
-// element fetched from L2 is used for several tokens. Lanes stride over the
-// hidden dimension in 8-element chunks (16-byte loads for bf16), accumulate
-// kTokensPerWave x E float32 partial dot products, and a butterfly reduction
-// leaves every logit in every lane. Lane j then finishes token j.
+// Work split (latency first: a decode batch has only a few dozen tokens): a
+// workgroup of 256 threads takes kVals / EM tokens and splits the hidden
+// dimension across all its threads in 8-element chunks (16-byte loads), so
+// every load of a token row and of the router is in flight at once. Each
+// thread then holds kVals = 64 float32 partial sums (token x expert); a
+// reduce-scatter across the wave (63 shuffles) leaves lane l with the wave's
+// sum for value l, the four waves meet in LDS in a fixed order, and one
+// thread per token finishes the scoring.
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTokensPerWave = 4;
-constexpr int kWavesPerBlock = 4;
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kVals = 64;  // partial sums per thread: tokens per block x EM
 
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* x, int64_t row, int d, int i, float* v) {
@@ -45,100 +49,122 @@ __device__ __forceinline__ float load1(const void* x, int64_t row, int d, int i)
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// One halving step of the reduce-scatter: lanes with bit O set keep the
+// upper half of the O*2 live values, the others the lower half, and each adds
+// the half its partner (lane ^ O) gives away.
+template <int O>
+__device__ __forceinline__ void reduce_scatter_step(float (&v)[kVals], bool upper) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  for (int i = 0; i < O; ++i) {
+    const float keep = upper ? v[i + O] : v[i];
+    const float give = upper ? v[i] : v[i + O];
+    v[i] = keep + __shfl_xor(give, O, kWave);
+  }
 }
 
-// EM: compile-time upper bound on E (8 or 32). VEC: rows are 16-byte aligned
-// and d % 8 == 0, so the 8-wide loads are legal.
+// v[0..63] in every lane -> lane l returns the sum over the wave of v[l].
+__device__ __forceinline__ float wave_reduce_scatter64(float (&v)[kVals], int lane) {
+  reduce_scatter_step<32>(v, (lane & 32) != 0);
+  reduce_scatter_step<16>(v, (lane & 16) != 0);
+  reduce_scatter_step<8>(v, (lane & 8) != 0);
+  reduce_scatter_step<4>(v, (lane & 4) != 0);
+  reduce_scatter_step<2>(v, (lane & 2) != 0);
+  reduce_scatter_step<1>(v, (lane & 1) != 0);
+  return v[0];
+}
+
+// EM: compile-time bound on E (8 or 32); TB = kVals / EM tokens per block.
+// VEC: x and router rows are 16-byte aligned and d % 8 == 0.
 template <bool BF16, int EM, bool VEC>
-__global__ __launch_bounds__(kWave* kWavesPerBlock) void route_kernel(
+__global__ __launch_bounds__(kThreads, 1) void route_kernel(
     const void* __restrict__ x, const float* __restrict__ router, const float* __restrict__ bias,
     int64_t T, int d, int E, int k, float* __restrict__ logits_out, int32_t* __restrict__ idx,
     float* __restrict__ wout) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int64_t t0 = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave) * kTokensPerWave;
+  constexpr int TB = kVals / EM;
+  __shared__ float s_part[kWavesPerBlock][kVals];
+  __shared__ float s_logit[kVals];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
 
-  float acc[kTokensPerWave][EM];
+  float acc[kVals];
 #pragma unroll
-  for (int tt = 0; tt < kTokensPerWave; ++tt)
-#pragma unroll
-    for (int e = 0; e < EM; ++e) acc[tt][e] = 0.0f;
+  for (int i = 0; i < kVals; ++i) acc[i] = 0.0f;
 
-  int64_t rows[kTokensPerWave];
-  bool live[kTokensPerWave];
+  int64_t rows[TB];
+  bool live[TB];
 #pragma unroll
-  for (int tt = 0; tt < kTokensPerWave; ++tt) {
+  for (int tt = 0; tt < TB; ++tt) {
     live[tt] = (t0 + tt) < T;
     rows[tt] = live[tt] ? t0 + tt : 0;
   }
 
+  // router rows e >= E (when E < EM) read row E-1: every load and FMA is
+  // unconditional, so all loads of a chunk are in flight together; those
+  // sums are never used
+  const float* rrow[EM];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) rrow[e] = router + static_cast<int64_t>(e < E ? e : E - 1) * d;
+
   int tail_start = 0;
   if constexpr (VEC) {
     const int nvec = d / 8;
-    for (int c = lane; c < nvec; c += kWave) {
+    for (int c = tid; c < nvec; c += kThreads) {
       const int i = c * 8;
-      float xv[kTokensPerWave][8];
+      float xv[TB][8];
 #pragma unroll
-      for (int tt = 0; tt < kTokensPerWave; ++tt) {
-        if (live[tt]) {
-          load8<BF16>(x, rows[tt], d, i, xv[tt]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < 8; ++v) xv[tt][v] = 0.0f;
-        }
-      }
+      for (int tt = 0; tt < TB; ++tt) load8<BF16>(x, rows[tt], d, i, xv[tt]);
+      float4 ra[EM], rb[EM];
 #pragma unroll
       for (int e = 0; e < EM; ++e) {
-        if (e < E) {
-          const float* rp = router + static_cast<int64_t>(e) * d + i;
-          float4 ra = *reinterpret_cast<const float4*>(rp);
-          float4 rb = *reinterpret_cast<const float4*>(rp + 4);
-          const float r8[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+        ra[e] = *reinterpret_cast<const float4*>(rrow[e] + i);
+        rb[e] = *reinterpret_cast<const float4*>(rrow[e] + i + 4);
+      }
+      // keep every load of the chunk ahead of the arithmetic (one round trip)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int tt = 0; tt < kTokensPerWave; ++tt)
+      for (int e = 0; e < EM; ++e) {
+        const float r8[8] = {ra[e].x, ra[e].y, ra[e].z, ra[e].w, rb[e].x, rb[e].y, rb[e].z, rb[e].w};
 #pragma unroll
-            for (int v = 0; v < 8; ++v) acc[tt][e] = fmaf(xv[tt][v], r8[v], acc[tt][e]);
+        for (int tt = 0; tt < TB; ++tt) {
+          float a = acc[tt * EM + e];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) a = fmaf(live[tt] ? xv[tt][v] : 0.0f, r8[v], a);
+          acc[tt * EM + e] = a;
         }
       }
     }
     tail_start = nvec * 8;
   }
-  for (int i = tail_start + lane; i < d; i += kWave) {
-    float xs[kTokensPerWave];
+  for (int i = tail_start + tid; i < d; i += kThreads) {
+    float xs[TB];
 #pragma unroll
-    for (int tt = 0; tt < kTokensPerWave; ++tt) xs[tt] = live[tt] ? load1<BF16>(x, rows[tt], d, i) : 0.0f;
+    for (int tt = 0; tt < TB; ++tt) xs[tt] = live[tt] ? load1<BF16>(x, rows[tt], d, i) : 0.0f;
 #pragma unroll
     for (int e = 0; e < EM; ++e) {
-      if (e < E) {
-        const float r = router[static_cast<int64_t>(e) * d + i];
+      const float r = rrow[e][i];
 #pragma unroll
-        for (int tt = 0; tt < kTokensPerWave; ++tt) acc[tt][e] = fmaf(xs[tt], r, acc[tt][e]);
-      }
+      for (int tt = 0; tt < TB; ++tt) acc[tt * EM + e] = fmaf(xs[tt], r, acc[tt * EM + e]);
     }
   }
 
+  s_part[wave][lane] = wave_reduce_scatter64(acc, lane);
+  __syncthreads();
+  if (tid < kVals) {
+    float sum = s_part[0][tid];
 #pragma unroll
-  for (int tt = 0; tt < kTokensPerWave; ++tt)
-#pragma unroll
-    for (int e = 0; e < EM; ++e)
-      if (e < E) acc[tt][e] = wave_sum(acc[tt][e]);
+    for (int w = 1; w < kWavesPerBlock; ++w) sum += s_part[w][tid];
+    s_logit[tid] = sum;
+  }
+  __syncthreads();
+  if (tid >= TB) return;
+  const int64_t t = t0 + tid;
+  if (t >= T) return;
 
-  // lane tt finishes token t0 + tt
-  if (lane >= kTokensPerWave) return;
   float l[EM];
 #pragma unroll
-  for (int e = 0; e < EM; ++e) l[e] = 0.0f;
-#pragma unroll
-  for (int tt = 0; tt < kTokensPerWave; ++tt)
-    if (lane == tt)
-#pragma unroll
-      for (int e = 0; e < EM; ++e) l[e] = acc[tt][e];
-  const int64_t t = t0 + lane;
-  if (t >= T) return;
+  for (int e = 0; e < EM; ++e) l[e] = s_logit[tid * EM + e];
 
   float m = -INFINITY;
 #pragma unroll
@@ -195,9 +221,9 @@ __global__ __launch_bounds__(kWave* kWavesPerBlock) void route_kernel(
 template <bool BF16, int EM>
 hipError_t launch_em(const void* x, const float* router, const float* bias, int64_t T, int d,
                      int E, int k, float* logits_out, int32_t* idx, float* w, hipStream_t s) {
-  const int64_t per_block = static_cast<int64_t>(kTokensPerWave) * kWavesPerBlock;
+  constexpr int64_t per_block = kVals / EM;
   const dim3 grid(static_cast<unsigned>((T + per_block - 1) / per_block));
-  const dim3 block(kWave * kWavesPerBlock);
+  const dim3 block(kThreads);
   const bool vec = (d % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(router) & 15) == 0);
   if (vec)

@@ -35,11 +35,16 @@ def test_workspace_bytes():
     f = moe.moe_workspace_bytes
     A = 32 * 2
     n = f(32, 4096, 14336, 8, 2, moe.MOE_BF16)
-    # at least h (bf16) and y (f32) plus four int/float arrays of A entries
-    assert n >= A * 14336 * 2 + A * 4096 * 4 + 4 * A * 4
+    # h (bf16), two float32 split-K partials of y, four int/float arrays of A entries
+    assert n >= A * 14336 * 2 + 2 * A * 4096 * 4 + 4 * A * 4
     assert n % 256 == 0
-    assert f(32, 4096, 14336, 8, 2, moe.MOE_F32) > n            # h is f32 there
+    assert f(32, 4096, 14336, 8, 2, moe.MOE_BF16_PACKED) == n   # same buffers
+    n32 = f(32, 4096, 14336, 8, 2, moe.MOE_F32)                 # h f32, one y
+    assert n32 >= A * 14336 * 4 + A * 4096 * 4
     assert f(64, 4096, 14336, 8, 2, moe.MOE_BF16) > n
+    # large batches use the tiled kernels, which leave y as one array
+    big = 4096 * 2
+    assert f(4096, 4096, 14336, 8, 2, moe.MOE_BF16) < big * 14336 * 2 + 2 * big * 4096 * 4 + 2 ** 20
     assert f(0, 128, 256, 8, 2, moe.MOE_F32) > 0                # counts/offsets still live
     for bad in [(-1, 128, 256, 8, 2, 0), (4, 128, 256, 8, 9, 0), (4, 128, 256, 33, 2, 0),
                 (4, 0, 256, 8, 2, 0), (4, 128, 256, 8, 0, 0), (4, 128, 256, 8, 2, 7),
@@ -104,6 +109,17 @@ def test_combine_and_forward_reject_bad_arguments():
     assert call(x=None) == moe.MOE_EINVAL
     assert call(wsb=0) == moe.MOE_EWORKSPACE
     assert call(x=MISALIGNED) == moe.MOE_ENOTSUP
+
+
+def test_pack_weight_rejects_bad_arguments():
+    pk = lib.moe_pack_weight
+    assert pk(BAD, moe.MOE_F32, 8, 64, 64, BAD, None) == moe.MOE_EINVAL      # bf16 only
+    assert pk(BAD, moe.MOE_BF16, 8, 40, 64, BAD, None) == moe.MOE_ENOTSUP    # rows % 16
+    assert pk(BAD, moe.MOE_BF16, 8, 64, 48, BAD, None) == moe.MOE_ENOTSUP    # cols % 32
+    assert pk(None, moe.MOE_BF16, 8, 64, 64, BAD, None) == moe.MOE_EINVAL
+    assert pk(MISALIGNED, moe.MOE_BF16, 8, 64, 64, ctypes.c_void_p(1 << 40), None) == moe.MOE_ENOTSUP
+    assert pk(ctypes.c_void_p(1 << 40), moe.MOE_BF16, 1, 64, 64,
+              ctypes.c_void_p((1 << 40) + 4096), None) == moe.MOE_EINVAL   # overlapping buffers
 
 
 def test_tuning_hooks_validate():

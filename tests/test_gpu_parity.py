@@ -95,6 +95,41 @@ def test_steps_and_forward_match_oracle(m, name, cfg, variant):
     assert torch.equal(counts_f, g["counts"])
     assert torch.equal(out_f, g["out"])
 
+    if inp["dtype"] == gen.BF16:
+        # fragment-order weights: same values in the same MFMA lanes -> same bits
+        pw = m.PackedWeights(dev["w1"], dev["w3"], dev["w2"])
+        y_p = m.moe_expert_ffn(dev["x"], pw.w1, pw.w3, pw.w2, g["offsets"], g["sasg"], k,
+                               packed=True)
+        out_p = m.moe_forward(dev["x"], dev["router"], pw.w1, pw.w3, pw.w2, k,
+                              logit_bias=dev["bias"], out_dtype=torch.float32, packed=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y_p, g["y"])
+        assert torch.equal(out_p, g["out"])
+
+
+def _pack_reference(w):
+    """Fragment order as include/moe.h defines it, by plain index arithmetic."""
+    E, R, C = w.shape
+    out = np.empty(E * R * C, w.dtype)
+    for e in range(E):
+        for rt in range(R // 16):
+            for s in range(C // 32):
+                base = ((e * (R // 16) + rt) * (C // 32) + s) * 512
+                for g in range(4):
+                    for r in range(16):
+                        o = base + (16 * g + r) * 8
+                        out[o:o + 8] = w[e, 16 * rt + r, 32 * s + 8 * g:32 * s + 8 * g + 8]
+    return out.reshape(E, R, C)
+
+
+def test_pack_weight_fragment_order(m):
+    rng = np.random.default_rng(50)
+    w = rng.integers(0, 2 ** 16, size=(3, 48, 96), dtype=np.uint16)
+    dev = torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16)
+    got = m.moe_pack_weight(dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), _pack_reference(w))
+
 
 @pytest.mark.parametrize("dtype", [gen.F32, gen.BF16])
 def test_ablation_changes_exactly_tokens_that_chose_e(m, dtype):
@@ -201,3 +236,13 @@ def test_full_size_workload(m, name):
     print(f"[parity] {name}: counts={host(counts).tolist()} near_ties={int(near.sum())} "
           f"set_compared={nsets} sampled={tokens.size} max|err|/rms={err:.3e}", flush=True)
     assert err <= OUT_TOL[gen.BF16]
+    # the benchmarked configuration: weights in fragment order, bf16 output
+    pw = m.PackedWeights(dev["w1"], dev["w3"], dev["w2"])
+    out_p = m.moe_forward(dev["x"], dev["router"], pw.w1, pw.w3, pw.w2, k,
+                          logit_bias=dev["bias"], out_dtype=torch.float32, packed=True)
+    out_b = m.moe_forward(dev["x"], dev["router"], pw.w1, pw.w3, pw.w2, k,
+                          logit_bias=dev["bias"], packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out)
+    assert np.array_equal(out_b.view(torch.int16).cpu().numpy().view(np.uint16),
+                          gen.f32_to_bf16_bits(out.cpu().numpy()))
