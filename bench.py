@@ -42,6 +42,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU run: turn the counter_collection.csv files of a rocprofv3 "
+                        "--pmc FETCH_SIZE run and a --pmc WRITE_SIZE run of this script "
+                        "(with --calib-copy-mib) into profiles/traffic.json for --workload")
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
@@ -127,6 +131,53 @@ def traffic_entry(workload):
     return ent.get("hbm_bytes_per_launch")
 
 
+GATE_UP_KERNELS = ("gate_up_stream_kernel", "tiled_kernel<true")
+
+
+def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
+    """HBM bytes per gate/up launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the counter reads for the plain
+    calibration copy of calib_mib MiB (read calib, write calib)."""
+    import csv
+    calib = calib_mib * 1024.0  # KiB
+
+    def load(path):
+        rows = list(csv.DictReader(open(path)))
+        cal = [float(r["Counter_Value"]) for r in rows
+               if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) > 1
+               and abs(float(r["Counter_Value"]) - calib) < 0.6 * calib]
+        gu = [float(r["Counter_Value"]) for r in rows
+              if any(k in r["Kernel_Name"] for k in GATE_UP_KERNELS)]
+        return cal, gu, rows
+
+    f_cal, f_gu, _ = load(fetch_csv)
+    w_cal, w_gu, _ = load(write_csv)
+    if not (f_cal and w_cal and f_gu and w_gu):
+        raise SystemExit("calibration copy or gate/up kernel not found in the counter files")
+    f_factor = f_cal[-1] / calib
+    w_factor = w_cal[-1] / calib
+    fetch = sum(f_gu) / len(f_gu) / f_factor * 1024
+    write = sum(w_gu) / len(w_gu) / w_factor * 1024
+    with open(FFN_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        if rec.get("ffn_bf16_sha256") != sha:
+            rec = {}
+    except (OSError, ValueError):
+        rec = {}
+    rec["ffn_bf16_sha256"] = sha
+    rec.setdefault("workloads", {})[workload] = {
+        "hbm_bytes_per_launch": int(fetch + write), "fetch_bytes": int(fetch),
+        "write_bytes": int(write), "fetch_counter_per_byte": round(f_factor, 5),
+        "write_counter_per_byte": round(w_factor, 5), "dispatches": len(f_gu),
+        "calibration": f"one {calib_mib} MiB device-to-device copy"}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec["workloads"][workload]))
+
+
 def cpu_baseline(cfg, inp):
     """The float64 oracle on a bounded sample of the same workload."""
     import numpy as np
@@ -149,6 +200,10 @@ def cpu_baseline(cfg, inp):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.workload, args.pmc_summary[0], args.pmc_summary[1],
+                    args.calib_copy_mib or 1024)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}); "
