@@ -45,6 +45,20 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Workgroup barrier for handing LDS data between waves. __syncthreads() also
+// orders global memory, which here means waiting for every global load still
+// in flight; a software pipeline that keeps loads in flight across the
+// barrier only needs this wave's LDS operations finished (lgkmcnt = 0; vmcnt
+// and expcnt left at their maxima, 63 and 7, in the gfx9 s_waitcnt encoding)
+// and the hardware barrier. The signal fences stop the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------------------
 // internal launchers (host side); each returns hipSuccess or the launch error
 // ---------------------------------------------------------------------------

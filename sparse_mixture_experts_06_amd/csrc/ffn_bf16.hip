@@ -38,6 +38,9 @@
 //    by expert, n-tile by n-tile, m-tile by m-tile, and consecutive tiles go
 //    to the same XCD so the m-tiles sharing a weight tile meet in that XCD's
 //    L2.
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 
 namespace moe {
@@ -361,6 +364,16 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chu
 // w1 rows [n+32, n+64), w3 rows [n+32, n+64) with n = nt*64, so wave column
 // wn holds gate and up for the same 32 h-columns.
 // !GATE_UP: act = h (grouped rows), wa = w2, out = y f32 [A, N=d].
+//
+// Pipeline: the global loads of K stage s are issued two iterations before
+// stage s is written to LDS (two register sets alternate), so each load has
+// two stages of MFMA work to arrive; LDS is double-buffered and one barrier
+// per stage separates the writes of stage s+1 from the reads of stage s. The
+// barrier waits for LDS operations only (lds_barrier), never for the global
+// loads in flight.
+// Weight tile loading: standard layout, thread t moves 16-byte chunk t % 8 of
+// rows t / 8 + 32 j; fragment order, wave w moves whole fragments w + 4 j
+// (one contiguous KiB per load instruction).
 template <bool GATE_UP, bool PACKED>
 __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ wa,
@@ -379,35 +392,52 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
   const int wn = wave & 1;
   const int wm = wave >> 1;
 
-  // this thread moves 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 j, j < 4
-  const int lrow = tid >> 3;
-  const int lch = tid & 7;
+  // weight row of LDS row R
+  auto wrow = [&](int R) -> int {
+    if constexpr (GATE_UP) {
+      return nt * 64 + ((R >> 5) >> 1) * 32 + (R & 31);
+    } else {
+      return min(nt * BN + R, N - 1);
+    }
+  };
+  auto wmat = [&](int R) -> const uint16_t* {
+    if constexpr (GATE_UP) {
+      return ((R >> 5) & 1) ? wb : wa;
+    } else {
+      return wa;
+    }
+  };
+
   constexpr int WSTEP = PACKED ? 1024 : BK;  // weight elements per BK advance
   const uint16_t* gw[4];
   const uint16_t* gx[4];
-  int so[4];
+  int sow[4], sox[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int R = lrow + 32 * j;
-    int n;
-    const uint16_t* base;
-    if constexpr (GATE_UP) {
-      base = (j & 1) ? wb : wa;
-      n = nt * 64 + (j >> 1) * 32 + lrow;
+    // weight chunk j of this thread: LDS row Rw, 16-byte chunk cw (of 8 per row)
+    int Rw, cw;
+    if constexpr (PACKED) {
+      const int F = wave + 4 * j;  // fragment: row tile F >> 1, k step F & 1
+      Rw = (F >> 1) * 16 + (lane & 15);
+      cw = (F & 1) * 4 + (lane >> 4);
     } else {
-      base = wa;
-      n = min(nt * BN + R, N - 1);
+      Rw = (tid >> 3) + 32 * j;
+      cw = tid & 7;
     }
-    gw[j] = base + wofs<PACKED>(e, n, lch * 8, N, K);
-    const int mm = min(m0 + R, M - 1);
+    gw[j] = wmat(Rw) + wofs<PACKED>(e, wrow(Rw), cw * 8, N, K);
+    sow[j] = swz(Rw, cw);
+    // token chunk j: LDS row Rx, chunk cx
+    const int Rx = (tid >> 3) + 32 * j;
+    const int cx = tid & 7;
+    const int mm = min(m0 + Rx, M - 1);
     int64_t row;
     if constexpr (GATE_UP) {
       row = sorted_asg[beg + mm] / ktop;
     } else {
       row = beg + mm;
     }
-    gx[j] = act + row * K + lch * 8;
-    so[j] = swz(R, lch);
+    gx[j] = act + row * K + cx * 8;
+    sox[j] = swz(Rx, cx);
   }
 
   f32x4 acc[4][4];
@@ -416,32 +446,44 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 rw[4], rx[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    rw[j] = ldg16(gw[j]);
-    rx[j] = ldg16(gx[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    *reinterpret_cast<u32x4*>(&sW[0][so[j]]) = rw[j];
-    *reinterpret_cast<u32x4*>(&sX[0][so[j]]) = rx[j];
-  }
-  __syncthreads();
-
   const int nk = K / BK;
+  u32x4 rw[2][4], rx[2][4];
+  auto issue = [&](int set, int kb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      rw[set][j] = ldg16(gw[j] + static_cast<size_t>(kb) * WSTEP);
+      rx[set][j] = ldg16(gx[j] + kb * BK);
+    }
+  };
+  auto stash = [&](int set, int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4*>(&sW[buf][sow[j]]) = rw[set][j];
+      *reinterpret_cast<u32x4*>(&sX[buf][sox[j]]) = rx[set][j];
+    }
+  };
+
+  // prologue: stage 0 -> LDS, stages 1 and 2 in flight. Stage indices past
+  // the end are clamped to the last stage: the loop body has no branches
+  // around its loads and stores (branches there make the compiler wait for
+  // every load in flight), and the few extra loads hit in cache.
+  const int last = nk - 1;
+  issue(0, 0);
+  issue(1, min(1, last));
+  stash(0, 0);
+  issue(0, min(2, last));
+  lds_barrier();
+
   const int fr = lane & 15;
   const int fg = lane >> 4;
-  for (int kb = 0; kb < nk; ++kb) {
-    const int cur = kb & 1;
-    const bool more = (kb + 1) < nk;
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        rw[j] = ldg16(gw[j] + static_cast<size_t>(kb + 1) * WSTEP);
-        rx[j] = ldg16(gx[j] + (kb + 1) * BK);
-      }
-    }
+  // one K stage; P = kb & 1 is a compile-time constant so that the register
+  // sets are fixed and no load result is copied (a copy would wait for it)
+  auto stage_body = [&](auto par, int kb) {
+    constexpr int P = decltype(par)::value;
+    // an odd stage count leaves one past-the-end stage in the last pair: skip
+    // its MFMA work (this branch holds no loads, so the wait counts of the
+    // loads in flight stay exact)
+    if (kb < nk) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int c = s * 4 + fg;
@@ -449,26 +491,30 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int R = wn * 64 + i * 16 + fr;
-        a[i] = *reinterpret_cast<const u32x4*>(&sW[cur][swz(R, c)]);
+        a[i] = *reinterpret_cast<const u32x4*>(&sW[P][swz(R, c)]);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int R = wm * 64 + j * 16 + fr;
-        b[j] = *reinterpret_cast<const u32x4*>(&sX[cur][swz(R, c)]);
+        b[j] = *reinterpret_cast<const u32x4*>(&sX[P][swz(R, c)]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
     }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<u32x4*>(&sW[cur ^ 1][so[j]]) = rw[j];
-        *reinterpret_cast<u32x4*>(&sX[cur ^ 1][so[j]]) = rx[j];
-      }
     }
-    __syncthreads();
+    // stage kb+1 has been in register set 1-P since two stages ago (after the
+    // last stage this writes a buffer nobody reads); kept after the MFMA work
+    // so that its loads get two stages of compute to arrive
+    __builtin_amdgcn_sched_barrier(0);
+    stash(1 - P, 1 - P);
+    lds_barrier();
+    issue(1 - P, min(kb + 3, last));
+  };
+  for (int kb = 0; kb < nk; kb += 2) {
+    stage_body(std::integral_constant<int, 0>{}, kb);
+    stage_body(std::integral_constant<int, 1>{}, kb + 1);
   }
 
   // epilogue: lane holds token column fr of each 16x16 tile and weight rows
@@ -501,6 +547,189 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
   }
 }
 
+// Weights-in-registers tiled kernel (many rows per expert): a workgroup tile
+// is 256 weight rows x 128 token rows; wave w owns weight rows 64w .. 64w+63
+// and all 128 tokens (4 x 8 MFMA tiles). Each wave loads its own weight
+// fragments straight into registers (never shared, so no LDS traffic for
+// weights; with fragment-order weights every load is one contiguous KiB);
+// only the token rows, shared by the four waves, are staged through LDS. Per
+// 64-wide K stage that is 16 KiB of LDS writes and 64 KiB of reads for
+// 4.2 MFLOP, against 32 + 64 KiB for 2.1 MFLOP when both operands go
+// through LDS. Weights are fetched 1.5 stages ahead (a ring of four 32-wide
+// K steps), tokens two stages ahead.
+// GATE_UP: wave w's rows are w1 rows n+32w .. n+32w+31 then the same rows of
+// w3 (n = nt*128), so gate and up of one h column sit in the same lane.
+// Needs N % 256 == 0 (down) or ffn % 128 == 0 (gate/up). Used with
+// fragment-order weights; with the standard layout each weight load would be
+// 16 rows x 64 bytes, and staging both operands through LDS is faster there.
+template <typename F, int... Is>
+__device__ __forceinline__ void unrolled(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+
+constexpr int lcm4(int r) { return (r % 4 == 0) ? r : (r % 2 == 0 ? 2 * r : 4 * r); }
+
+template <bool GATE_UP, bool PACKED, int RING, int OCC>
+__global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
+    const uint16_t* __restrict__ act, const uint16_t* __restrict__ wa,
+    const uint16_t* __restrict__ wb, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_asg, int K, int N, int E, int ktop,
+    void* __restrict__ out, int ntn) {
+  int e, beg, M, m0, nt;
+  if (!decode_tile(offsets, E, ntn, e, beg, M, m0, nt)) return;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][BM * BK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int fr = lane & 15;
+  const int fg = lane >> 4;
+  constexpr int ST = kStep32<PACKED>();
+
+  // weight fragment addresses: a wave-uniform part per row tile (scalar
+  // registers) plus one per-lane offset
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint16_t* wbase[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int row;
+    const uint16_t* base;
+    if constexpr (GATE_UP) {
+      row = nt * 128 + wv * 32 + (i & 1) * 16;
+      base = (i < 2) ? wa : wb;
+    } else {
+      row = nt * 256 + wv * 64 + i * 16;
+      base = wa;
+    }
+    wbase[i] = base + wofs<PACKED>(e, row, 0, N, K);
+  }
+  const int wlane = static_cast<int>(wofs<PACKED>(0, fr, fg * 8, N, K));
+
+  // token chunk j of this thread: row (tid >> 3) + 32 j of the tile, 16-byte
+  // chunk tid & 7; all four share one swizzled LDS column (rows differ by 32)
+  int xrow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int mm = min(m0 + (tid >> 3) + 32 * j, M - 1);
+    if constexpr (GATE_UP) {
+      xrow[j] = sorted_asg[beg + mm] / ktop;
+    } else {
+      xrow[j] = beg + mm;
+    }
+  }
+  const int xcol = (tid & 7) * 8;
+  const int sox0 = swz(tid >> 3, tid & 7);
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / BK;
+  const int last = nk - 1;
+  const int nsteps = 2 * nk;  // 32-wide K steps
+  // weights: a ring of RING K32 slots; the loads of step t+RING are issued
+  // as soon as step t has used its slot ((RING-1)/2 stages of lead time)
+  u32x4 wr[RING][4];   // [slot][row tile]
+  u32x4 rx[2][4];   // token chunks in flight (two stages)
+  auto issue_w = [&](int slot, int t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wr[slot][i] = ldw<PACKED>(wbase[i] + static_cast<size_t>(t) * ST + wlane);
+  };
+  auto issue_x = [&](int set, int kb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      rx[set][j] = ldg16(act + static_cast<int64_t>(xrow[j]) * K + kb * BK + xcol);
+  };
+  auto stash = [&](int set, int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(&sX[buf][sox0 + j * 32 * BK]) = rx[set][j];
+  };
+
+  // prologue: tokens of stage 0 in LDS, tokens of stages 1 and 2 and weights
+  // of steps 0..3 in flight (indices past the end clamp to the last one)
+#pragma unroll
+  for (int t = 0; t < RING; ++t) issue_w(t, min(t, nsteps - 1));
+  issue_x(0, 0);
+  issue_x(1, min(1, last));
+  stash(0, 0);
+  issue_x(0, min(2, last));
+  lds_barrier();
+
+  // K32 step t (T = t mod U, compile-time, U a multiple of 4 and of RING):
+  // stage kb = t / 2 lives in LDS buffer kb mod 2, half t mod 2 of it
+  constexpr int U = lcm4(RING);
+  int t0 = 0;
+  auto step_body = [&](auto tm) {
+    constexpr int T = decltype(tm)::value;
+    constexpr int SLOT = T % RING;
+    constexpr int P = (T >> 1) & 1;  // LDS buffer / token register set of this stage
+    constexpr int S = T & 1;         // which 32-wide half of the 64-wide stage
+    const int t = t0 + T;
+    const int kb = t >> 1;
+    if (t < nsteps) {
+      const int c = S * 4 + fg;
+#pragma unroll
+      for (int jh = 0; jh < 2; ++jh) {  // token fragments four at a time
+        u32x4 b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b[j] = *reinterpret_cast<const u32x4*>(&sX[P][swz((jh * 4 + j) * 16 + fr, c)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][jh * 4 + j] = mfma16x16x32(wr[SLOT][i], b[j], acc[i][jh * 4 + j]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(SLOT, min(t + RING, nsteps - 1));
+    if constexpr (S == 1) {
+      // end of stage kb: tokens of stage kb+1 (in registers since two stages
+      // ago) go to the other buffer; tokens of stage kb+3 start loading
+      stash(1 - P, 1 - P);
+      lds_barrier();
+      issue_x(1 - P, min(kb + 3, last));
+    }
+  };
+  for (; t0 < nsteps; t0 += U) unrolled(step_body, std::make_integer_sequence<int, U>{});
+
+  // epilogue: lane holds token column fr of each 16x16 tile and weight rows
+  // 4*fg .. 4*fg+3 of it
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = m0 + j * 16 + fr;
+    if (m >= M) continue;
+    if constexpr (GATE_UP) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int n = nt * 128 + wave * 32 + i * 16 + 4 * fg;
+        const f32x4 gt = acc[i][j];
+        const f32x4 up = acc[i + 2][j];
+        uint2 v;
+        v.x = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
+        v.y = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + static_cast<size_t>(beg + m) * N +
+                                  n) = v;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = nt * 256 + wave * 64 + i * 16 + 4 * fg;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + static_cast<size_t>(beg + m) * N + n) =
+            acc[i][j];
+      }
+    }
+  }
+}
+
+// weight ring depth and workgroups per CU of wtiled_kernel
+constexpr int kWRing = 8, kWOcc = 1;
+
 inline unsigned tiled_grid(int64_t A, int E, int ntn) {
   const int64_t mt = (A + BM - 1) / BM + E;
   const int64_t tiles = mt * ntn;
@@ -521,6 +750,11 @@ hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, cons
       hipLaunchKernelGGL((gate_up_stream_kernel<kGateUpRT, kGateUpU, PACKED, kStreamNT<PACKED>>),
                          dim3(ffn / rows, E), dim3(kWave * kStreamWaves), 0, s, x, w1, w3,
                          offsets, sorted_asg, d, ffn, k, h);
+  } else if (PACKED && ffn % 128 == 0) {
+    const int ntn = ffn / 128;
+    hipLaunchKernelGGL((wtiled_kernel<true, PACKED, kWRing, kWOcc>), dim3(tiled_grid(A, E, ntn)),
+                       dim3(kTiledThreads), 0, s, x, w1, w3, offsets, sorted_asg, d, ffn, E, k,
+                       static_cast<void*>(h), ntn);
   } else {
     const int ntn = ffn / 64;
     hipLaunchKernelGGL((tiled_kernel<true, PACKED>), dim3(tiled_grid(A, E, ntn)),
@@ -549,6 +783,12 @@ hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const i
                          dim3(kWave * kStreamWaves), 0, s, h, w2, offsets, ffn, d,
                          static_cast<int>(A), nsplit, part);
     }
+  } else if (PACKED && d % 256 == 0) {
+    const int ntn = d / 256;
+    hipLaunchKernelGGL((wtiled_kernel<false, PACKED, kWRing, kWOcc>), dim3(tiled_grid(A, E, ntn)),
+                       dim3(kTiledThreads), 0, s, h, w2, w2, offsets,
+                       static_cast<const int32_t*>(nullptr), ffn, d, E, 1,
+                       static_cast<void*>(part), ntn);
   } else {
     const int ntn = (d + BN - 1) / BN;
     hipLaunchKernelGGL((tiled_kernel<false, PACKED>), dim3(tiled_grid(A, E, ntn)),
