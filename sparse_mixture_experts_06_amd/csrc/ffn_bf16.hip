@@ -555,8 +555,8 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
 // only the token rows, shared by the four waves, are staged through LDS. Per
 // 64-wide K stage that is 16 KiB of LDS writes and 64 KiB of reads for
 // 4.2 MFLOP, against 32 + 64 KiB for 2.1 MFLOP when both operands go
-// through LDS. Weights are fetched 1.5 stages ahead (a ring of four 32-wide
-// K steps), tokens two stages ahead.
+// through LDS. Weights are fetched 3.5 stages ahead (a ring of eight 32-wide
+// K steps), tokens two stages ahead (two register sets).
 // GATE_UP: wave w's rows are w1 rows n+32w .. n+32w+31 then the same rows of
 // w3 (n = nt*128), so gate and up of one h column sit in the same lane.
 // Needs N % 256 == 0 (down) or ffn % 128 == 0 (gate/up). Used with
@@ -567,9 +567,10 @@ __device__ __forceinline__ void unrolled(F&& f, std::integer_sequence<int, Is...
   (f(std::integral_constant<int, Is>{}), ...);
 }
 
-constexpr int lcm4(int r) { return (r % 4 == 0) ? r : (r % 2 == 0 ? 2 * r : 4 * r); }
+constexpr int gcd_i(int a, int b) { return b == 0 ? a : gcd_i(b, a % b); }
+constexpr int lcm_i(int a, int b) { return a / gcd_i(a, b) * b; }
 
-template <bool GATE_UP, bool PACKED, int RING, int OCC>
+template <bool GATE_UP, bool PACKED, int RING, int OCC, int XSETS>
 __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ wa,
     const uint16_t* __restrict__ wb, const int32_t* __restrict__ offsets,
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
   // weights: a ring of RING K32 slots; the loads of step t+RING are issued
   // as soon as step t has used its slot ((RING-1)/2 stages of lead time)
   u32x4 wr[RING][4];   // [slot][row tile]
-  u32x4 rx[2][4];   // token chunks in flight (two stages)
+  u32x4 rx[XSETS][4];   // token chunks in flight (XSETS stages)
   auto issue_w = [&](int slot, int t) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -650,25 +651,28 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
       *reinterpret_cast<u32x4*>(&sX[buf][sox0 + j * 32 * BK]) = rx[set][j];
   };
 
-  // prologue: tokens of stage 0 in LDS, tokens of stages 1 and 2 and weights
-  // of steps 0..3 in flight (indices past the end clamp to the last one)
+  // prologue: tokens of stage 0 in LDS, tokens of stages 1..XSETS and the
+  // weights of steps 0..RING-1 in flight (indices past the end clamp to the
+  // last one); token stage s lives in register set s mod XSETS
 #pragma unroll
   for (int t = 0; t < RING; ++t) issue_w(t, min(t, nsteps - 1));
   issue_x(0, 0);
-  issue_x(1, min(1, last));
+#pragma unroll
+  for (int q = 1; q < XSETS; ++q) issue_x(q, min(q, last));
   stash(0, 0);
-  issue_x(0, min(2, last));
+  issue_x(0, min(XSETS, last));
   lds_barrier();
 
-  // K32 step t (T = t mod U, compile-time, U a multiple of 4 and of RING):
-  // stage kb = t / 2 lives in LDS buffer kb mod 2, half t mod 2 of it
-  constexpr int U = lcm4(RING);
+  // K32 step t (T = t mod U, compile-time; U a multiple of 4, of RING and of
+  // 2*XSETS): stage kb = t / 2 lives in LDS buffer kb mod 2, half t mod 2 of it
+  constexpr int U = lcm_i(lcm_i(4, RING), 2 * XSETS);
   int t0 = 0;
   auto step_body = [&](auto tm) {
     constexpr int T = decltype(tm)::value;
     constexpr int SLOT = T % RING;
-    constexpr int P = (T >> 1) & 1;  // LDS buffer / token register set of this stage
+    constexpr int P = (T >> 1) & 1;  // LDS buffer of this stage
     constexpr int S = T & 1;         // which 32-wide half of the 64-wide stage
+    constexpr int XN = ((T >> 1) + 1) % XSETS;  // token set of the next stage
     const int t = t0 + T;
     const int kb = t >> 1;
     if (t < nsteps) {
@@ -689,11 +693,11 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
     __builtin_amdgcn_sched_barrier(0);
     issue_w(SLOT, min(t + RING, nsteps - 1));
     if constexpr (S == 1) {
-      // end of stage kb: tokens of stage kb+1 (in registers since two stages
-      // ago) go to the other buffer; tokens of stage kb+3 start loading
-      stash(1 - P, 1 - P);
+      // end of stage kb: tokens of stage kb+1 (in registers for XSETS stages)
+      // go to the other buffer; tokens of stage kb+1+XSETS start loading
+      stash(XN, 1 - P);
       lds_barrier();
-      issue_x(1 - P, min(kb + 3, last));
+      issue_x(XN, min(kb + 1 + XSETS, last));
     }
   };
   for (; t0 < nsteps; t0 += U) unrolled(step_body, std::make_integer_sequence<int, U>{});
@@ -728,7 +732,7 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
 }
 
 // weight ring depth and workgroups per CU of wtiled_kernel
-constexpr int kWRing = 8, kWOcc = 1;
+constexpr int kWRing = 8, kWOcc = 1, kWXSets = 2;
 
 inline unsigned tiled_grid(int64_t A, int E, int ntn) {
   const int64_t mt = (A + BM - 1) / BM + E;
@@ -752,7 +756,7 @@ hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, cons
                          offsets, sorted_asg, d, ffn, k, h);
   } else if (PACKED && ffn % 128 == 0) {
     const int ntn = ffn / 128;
-    hipLaunchKernelGGL((wtiled_kernel<true, PACKED, kWRing, kWOcc>), dim3(tiled_grid(A, E, ntn)),
+    hipLaunchKernelGGL((wtiled_kernel<true, PACKED, kWRing, kWOcc, kWXSets>), dim3(tiled_grid(A, E, ntn)),
                        dim3(kTiledThreads), 0, s, x, w1, w3, offsets, sorted_asg, d, ffn, E, k,
                        static_cast<void*>(h), ntn);
   } else {
@@ -785,7 +789,7 @@ hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const i
     }
   } else if (PACKED && d % 256 == 0) {
     const int ntn = d / 256;
-    hipLaunchKernelGGL((wtiled_kernel<false, PACKED, kWRing, kWOcc>), dim3(tiled_grid(A, E, ntn)),
+    hipLaunchKernelGGL((wtiled_kernel<false, PACKED, kWRing, kWOcc, kWXSets>), dim3(tiled_grid(A, E, ntn)),
                        dim3(kTiledThreads), 0, s, h, w2, w2, offsets,
                        static_cast<const int32_t*>(nullptr), ffn, d, E, 1,
                        static_cast<void*>(part), ntn);
