@@ -30,6 +30,13 @@ HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arc
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Per-file extra flags. ffn_dma.hip places its MFMAs, fragment reads and
+# direct-to-LDS loads by hand (groups closed by scheduling barriers); with the
+# machine scheduler on, its reordering makes the register allocator rotate the
+# 256 accumulators of a wave through copies every K step.
+FILE_FLAGS = {"ffn_dma.hip": ["-mllvm", "-enable-misched=0"]}
+
+
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -50,6 +57,12 @@ def _run(cmd, verbose):
     return out
 
 
+def compile_command(src: str, out: str, extra=()) -> list:
+    """The hipcc command build() uses for one source file (plus `extra`)."""
+    return [_hipcc(), *HIPFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, src,
+            "-o", out]
+
+
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
@@ -61,7 +74,7 @@ def build(verbose: bool = False) -> str:
     for src in sources:
         obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
-        jobs.append([hipcc, *HIPFLAGS, "-c", src, "-o", obj])
+        jobs.append(compile_command(src, obj, ["-c"]))
     workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(workers) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))

@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -41,8 +44,28 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// element offset of w[e][n][k] (k a multiple of 8) of an [E, N, K] weight in
+// the standard layout (PACKED false) or in fragment order (PACKED true: 16-row
+// x 32-k fragments of 1 KiB in MFMA lane order, ordered expert, row tile, k step)
+template <bool PACKED>
+__device__ __forceinline__ size_t wofs(int e, int n, int k, int N, int K) {
+  if constexpr (PACKED) {
+    return ((static_cast<size_t>(e) * (N >> 4) + (n >> 4)) * static_cast<size_t>(K >> 5) +
+            (k >> 5)) * 512 + ((((k & 31) >> 3) << 4) + (n & 15)) * 8;
+  } else {
+    return (static_cast<size_t>(e) * N + n) * K + k;
+  }
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+// f(integral_constant<int, I>) for I in Is, in order: a loop unrolled with the
+// index as a compile-time constant (fixed register sets, immediate offsets)
+template <typename F, int... Is>
+__device__ __forceinline__ void unrolled(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
 }
 
 // Workgroup barrier for handing LDS data between waves. __syncthreads() also
@@ -82,6 +105,13 @@ hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const u
                             const int32_t* offsets, int64_t A, int d, int ffn, int E, float* part,
                             hipStream_t s);
 int down_splits(int variant, int64_t A);
+
+// gate/up for many rows per expert with fragment-order weights and
+// direct-to-LDS loads (ffn_dma.hip): the sizes it is used for, and its launcher
+bool dma_gate_up_ok(int64_t A, int k, int d, int ffn, int E);
+hipError_t launch_gate_up_dma(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
+                              const int32_t* offsets, const int32_t* sorted_asg, int64_t A, int d,
+                              int ffn, int E, int k, uint16_t* h, hipStream_t s);
 // standard [E, R, C] bf16 -> fragment order (16-row x 32-column fragments)
 hipError_t launch_pack_bf16(const uint16_t* w, int E, int R, int C, uint16_t* out, hipStream_t s);
 

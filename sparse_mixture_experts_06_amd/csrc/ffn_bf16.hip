@@ -46,17 +46,6 @@
 namespace moe {
 namespace {
 
-// element offset of w[e][n][k] (k a multiple of 8) in either layout
-template <bool PACKED>
-__device__ __forceinline__ size_t wofs(int e, int n, int k, int N, int K) {
-  if constexpr (PACKED) {
-    return ((static_cast<size_t>(e) * (N >> 4) + (n >> 4)) * static_cast<size_t>(K >> 5) +
-            (k >> 5)) * 512 + ((((k & 31) >> 3) << 4) + (n & 15)) * 8;
-  } else {
-    return (static_cast<size_t>(e) * N + n) * K + k;
-  }
-}
-
 // elements between one lane's values of consecutive 32-wide k steps
 template <bool PACKED>
 constexpr int kStep32() { return PACKED ? 512 : 32; }
@@ -562,10 +551,6 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
 // Needs N % 256 == 0 (down) or ffn % 128 == 0 (gate/up). Used with
 // fragment-order weights; with the standard layout each weight load would be
 // 16 rows x 64 bytes, and staging both operands through LDS is faster there.
-template <typename F, int... Is>
-__device__ __forceinline__ void unrolled(F&& f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
 
 constexpr int gcd_i(int a, int b) { return b == 0 ? a : gcd_i(b, a % b); }
 constexpr int lcm_i(int a, int b) { return a / gcd_i(a, b) * b; }
@@ -754,6 +739,8 @@ hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, cons
       hipLaunchKernelGGL((gate_up_stream_kernel<kGateUpRT, kGateUpU, PACKED, kStreamNT<PACKED>>),
                          dim3(ffn / rows, E), dim3(kWave * kStreamWaves), 0, s, x, w1, w3,
                          offsets, sorted_asg, d, ffn, k, h);
+  } else if (PACKED && dma_gate_up_ok(A, k, d, ffn, E)) {
+    return launch_gate_up_dma(x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s);
   } else if (PACKED && ffn % 128 == 0) {
     const int ntn = ffn / 128;
     hipLaunchKernelGGL((wtiled_kernel<true, PACKED, kWRing, kWOcc, kWXSets>), dim3(tiled_grid(A, E, ntn)),
@@ -813,7 +800,7 @@ int choose_ffn_variant(int requested, int64_t A, int E) {
 
 int down_splits(int variant, int64_t A) {
   // the streaming down kernel splits K two ways while its float32 partials
-  // stay small; the tiled kernel writes the final sums directly
+  // stay small; the tiled kernels write the final sums directly
   return (variant == 1 && A <= 4096) ? 2 : 1;
 }
 

@@ -1,0 +1,275 @@
+// Expert gate/up projection for many rows per expert (prefill) with
+// fragment-order weights: the first grouped GEMM of the Mixtral sparse-MoE
+// block (nnterp Mixtral page, support(): the down projection receives
+// act(gate) * up with act = SiLU; the experts are one stacked module), fused
+// with that activation, as in ffn_bf16.hip:
+//
+//   h[p, n] = silu(sum_i x[r,i] w1[e,n,i]) * (sum_i x[r,i] w3[e,n,i]),
+//   r = sorted_asg[p] / k for p in expert e's grouped rows; h is bf16.
+//
+// Tile: 256 weight rows (w1 and w3 rows n .. n+127, n = 128 nt) x 256 token
+// rows per workgroup of 4 waves; wave (wn, wm) owns 64 w1 rows and the same
+// 64 w3 rows (so gate and up of one h column meet in one lane) and tokens
+// 128 wm .. 128 wm + 127: an 8 x 8 grid of 16x16 MFMA tiles (256 accumulator
+// registers). K advances in 32-wide steps. Both operands go global -> LDS
+// with the 16-byte direct-to-LDS buffer loads, no register staging: one load
+// instruction moves one 1 KiB MFMA fragment (weights: one contiguous KiB of
+// the fragment-order matrix; tokens: 16 gathered rows x 64 bytes) and writes
+// it to LDS in lane order, so each ds_read_b128 of a fragment reads one
+// contiguous KiB (no bank conflicts). A step's 32 fragments (16 weight, 16
+// token) fill one 32 KiB LDS buffer; four buffers hold steps t .. t+3. The
+// loads of step t+4 go out during step t, right after the barrier that frees
+// step t's buffer, so each has three steps of MFMA work to land. The only
+// waits are one "vmcnt <= 16" (this wave's loads of step t+1 done) and one
+// barrier per step.
+//
+// Per step a wave runs 16 groups of 4 MFMAs; group g also reads one fragment
+// of step t+1 into the second register set (weights at even g, tokens at odd
+// g) and, for g < 8, issues one of the wave's 8 loads for step t+4. Groups
+// are closed by scheduling barriers and this file is built with the machine
+// scheduler off: that keeps the interleaving as written, and it lets the
+// register allocator keep every accumulator in one place (the scheduler's
+// reordering otherwise makes it rotate the 256 accumulators through copies).
+//
+// Token tiles that run past an expert's rows: each wave computes only its
+// token fragments that hold a row (rounded up to an even count; a template
+// parameter, so the loop stays branch-free), and still issues all loads and
+// barriers with the other waves.
+//
+// All loads go through buffer descriptors bounded to the source array, so an
+// offset outside it reads zeros instead of faulting (the host checks that the
+// byte offsets fit in 31 bits; inside the kernel they are in range by
+// construction: token rows are clamped to the expert's last row).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+constexpr int DT = 256;             // weight rows and token rows per tile
+constexpr int kFragE = 512;         // bf16 elements per 16x32 fragment (1 KiB)
+constexpr int kBufE = 32 * kFragE;  // one step: 16 weight + 16 token fragments
+constexpr int kDmaThreads = 256;
+// buffer descriptor word 3 (gfx9): 32-bit data format, for raw dword loads
+constexpr int kRsrcWord3 = 0x00020000;
+
+// s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt not waited on
+constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// workgroup -> (expert e, its first grouped row beg and row count M, token
+// tile m0, weight tile nt). Tiles are listed expert by expert, n-tile by
+// n-tile, m-tile by m-tile; workgroup b runs on XCD b % 8 and takes logical
+// tile (b % 8) * per + b / 8, so the m-tiles sharing a weight tile run
+// together in one XCD's L2. Surplus workgroups of the worst-case grid return.
+__device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offsets, int E, int ntn,
+                                               int& e, int& beg, int& M, int& m0, int& nt) {
+  int total = 0;
+  for (int i = 0; i < E; ++i) {
+    const int Mi = offsets[i + 1] - offsets[i];
+    total += ((Mi + DT - 1) / DT) * ntn;
+  }
+  const int per = (total + 7) / 8;
+  const int q = blockIdx.x >> 3;
+  if (q >= per) return false;
+  int L = (blockIdx.x & 7) * per + q;
+  if (L >= total) return false;
+  for (int i = 0; i < E; ++i) {
+    const int Mi = offsets[i + 1] - offsets[i];
+    const int mt = (Mi + DT - 1) / DT;
+    const int cnt = mt * ntn;
+    if (L < cnt) {
+      e = i;
+      beg = offsets[i];
+      M = Mi;
+      nt = L / mt;
+      m0 = (L % mt) * DT;
+      return true;
+    }
+    L -= cnt;
+  }
+  return false;
+}
+
+// x [T, d] bf16, w1/w3 fragment order [E, ffn, d], h [A, ffn] bf16
+__global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
+    const uint16_t* __restrict__ x, int64_t T, const uint16_t* __restrict__ w1,
+    const uint16_t* __restrict__ w3, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_asg, int d, int ffn, int E, int ktop,
+    uint16_t* __restrict__ h, int ntn) {
+  int e, beg, M, m0, nt;
+  if (!decode_tile256(offsets, E, ntn, e, beg, M, m0, nt)) return;
+
+  // one array per buffer: distinct objects let the compiler see that a
+  // fragment read does not depend on the loads in flight to other buffers
+  __shared__ __attribute__((aligned(1024))) uint16_t buf0[kBufE];
+  __shared__ __attribute__((aligned(1024))) uint16_t buf1[kBufE];
+  __shared__ __attribute__((aligned(1024))) uint16_t buf2[kBufE];
+  __shared__ __attribute__((aligned(1024))) uint16_t buf3[kBufE];
+  auto bufp = [&](auto bi) -> uint16_t* {
+    constexpr int B = decltype(bi)::value;
+    if constexpr (B == 0) return buf0;
+    else if constexpr (B == 1) return buf1;
+    else if constexpr (B == 2) return buf2;
+    else return buf3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wn = w & 1, wm = w >> 1;
+  const int fr = lane & 15, fg = lane >> 4;
+
+  // this wave loads weight fragments 4w .. 4w+3 and token fragments 4w .. 4w+3
+  // of every step. Weight fragment f is the w1 (f & 4 == 0) or w3 row tile
+  // nt*128 + (f >> 3)*64 + (f & 3)*16, read by wave wn = f >> 3 as its
+  // fragment f & 7: waves with odd w load only w3, the others only w1.
+  const size_t wslice = static_cast<size_t>(ffn) * d;  // elements of one expert matrix
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(((w & 1) ? w3 : w1) + e * wslice), 0, static_cast<int>(wslice * 2),
+      kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), 0, static_cast<int>(T * d * 2), kRsrcWord3);
+  int aoff[4], boff[4];  // byte offsets of step 0: weights wave-uniform, tokens per lane
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int f = 4 * w + q;
+    const int row = nt * 128 + (f >> 3) * 64 + q * 16;
+    aoff[q] = __builtin_amdgcn_readfirstlane(static_cast<int>(wofs<true>(0, row, 0, ffn, d) * 2));
+    const int mm = min(m0 + f * 16 + fr, M - 1);
+    boff[q] = ((sorted_asg[beg + mm] / ktop) * d + fg * 8) * 2;
+  }
+  const int lane16 = lane * 16;
+
+  const int nsteps = d / 32;  // a multiple of 4
+  const int last = nsteps - 1;
+  auto load_a = [&](uint16_t* L, int q, int t) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr)(L + (4 * w + q) * kFragE), 16, lane16,
+                                             aoff[q] + t * (kFragE * 2), 0, 0);
+  };
+  auto load_b = [&](uint16_t* L, int q, int t) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_ptr)(L + (16 + 4 * w + q) * kFragE), 16,
+                                             boff[q], t * 64, 0, 0);
+  };
+  auto load_step = [&](auto bi, int t) {
+    uint16_t* L = bufp(bi);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_a(L, q, t);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_b(L, q, t);
+  };
+  unrolled([&](auto bi) { load_step(bi, min(decltype(bi)::value, last)); },
+           std::make_integer_sequence<int, 4>{});
+
+  // fragments of this wave's token tiles that hold a row, rounded up to even
+  const int valid = M - m0 - wm * 128;
+  const int jv = valid >= 128 ? 8 : valid <= 0 ? 0 : (((valid + 15) >> 4) + 1) & ~1;
+
+  auto run = [&](auto jvc) {
+    constexpr int JV = decltype(jvc)::value;
+    u32x4 fa[2][8], fb[2][8];
+    f32x4 acc[8][JV > 0 ? JV : 1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < JV; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // fragment k of the step in buffer bi into register set si: k < 8 is the
+    // wave's weight tile k, k >= 8 its token tile k - 8
+    auto rd = [&](auto bi, auto si, int k) {
+      constexpr int S = decltype(si)::value;
+      const uint16_t* L = bufp(bi);
+      if (k < 8)
+        fa[S][k] = *reinterpret_cast<const u32x4*>(L + (wn * 8 + k) * kFragE + lane * 8);
+      else if (k - 8 < JV)
+        fb[S][k - 8] = *reinterpret_cast<const u32x4*>(L + (16 + wm * 8 + (k - 8)) * kFragE + lane * 8);
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(24));  // this wave's loads of step 0
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) rd(I0{}, I0{}, k);
+
+    int t0 = 0;
+    auto step = [&](auto tm) {
+      // step t0 + T lives in buffer T and register set T % 2 (t0 % 4 == 0)
+      constexpr int T = decltype(tm)::value;
+      constexpr int CUR = T & 1, NXT = CUR ^ 1;
+      using NBUF = std::integral_constant<int, (T + 1) & 3>;
+      const int t = t0 + T;
+      // own loads of step t+1 done (those of t+2, t+3 may still fly); the
+      // barrier publishes step t+1 and frees buffer T (step t is in registers)
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(16));
+      lds_barrier();
+      const int tl = min(t + 4, last);
+      unrolled([&](auto gm) {
+        constexpr int g = decltype(gm)::value;
+        constexpr int i = g >> 1, j0 = (g & 1) * 4;
+        unrolled([&](auto jm) {
+          constexpr int j = j0 + decltype(jm)::value;
+          if constexpr (j < JV) acc[i][j] = mfma16x16x32(fa[CUR][i], fb[CUR][j], acc[i][j]);
+        }, std::make_integer_sequence<int, 4>{});
+        rd(NBUF{}, std::integral_constant<int, NXT>{}, (g & 1) * 8 + (g >> 1));
+        if constexpr (g < 4) load_a(bufp(tm), g, tl);
+        else if constexpr (g < 8) load_b(bufp(tm), g - 4, tl);
+        __builtin_amdgcn_sched_barrier(0);
+      }, std::make_integer_sequence<int, 16>{});
+    };
+    for (; t0 < nsteps; t0 += 4) unrolled(step, std::make_integer_sequence<int, 4>{});
+
+    // epilogue: lane holds token column fr of each 16x16 tile and weight rows
+    // 4*fg .. 4*fg+3 of it; gate in tiles 0-3, up in tiles 4-7
+#pragma unroll
+    for (int j = 0; j < JV; ++j) {
+      const int m = m0 + wm * 128 + j * 16 + fr;
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = nt * 128 + wn * 64 + i * 16 + 4 * fg;
+        f32x4 gt = acc[i][j];
+        f32x4 up = acc[i + 4][j];
+        // an empty asm with VGPR constraints (no instruction) fixes the
+        // accumulators' register class for the allocator
+        asm volatile("" : "+v"(gt), "+v"(up));
+        uint2 v;
+        v.x = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
+        v.y = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
+        *reinterpret_cast<uint2*>(h + static_cast<size_t>(beg + m) * ffn + n) = v;
+      }
+    }
+  };
+  switch (jv) {
+    case 8: run(std::integral_constant<int, 8>{}); break;
+    case 6: run(std::integral_constant<int, 6>{}); break;
+    case 4: run(std::integral_constant<int, 4>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
+  }
+}
+
+constexpr int64_t kMax31 = (int64_t(1) << 31) - 1;
+
+}  // namespace
+
+bool dma_gate_up_ok(int64_t A, int k, int d, int ffn, int E) {
+  if (d % 128 != 0 || ffn % 128 != 0) return false;
+  // every tile costs a full pass over its weight rows whatever its token
+  // count, so a part-filled last tile per expert is cheap only when experts
+  // average several full 256-row tiles; below that the 128-row tiles win
+  if (A < static_cast<int64_t>(3 * DT) * E) return false;
+  // byte offsets inside the buffer descriptors are 31-bit
+  return static_cast<int64_t>(ffn) * d * 2 <= kMax31 && (A / k) * d * 2 <= kMax31;
+}
+
+hipError_t launch_gate_up_dma(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
+                              const int32_t* offsets, const int32_t* sorted_asg, int64_t A, int d,
+                              int ffn, int E, int k, uint16_t* h, hipStream_t s) {
+  const int ntn = ffn / 128;
+  const int64_t tiles = ((A + DT - 1) / DT + E) * ntn;  // upper bound
+  hipLaunchKernelGGL(gate_up_dma_kernel, dim3(static_cast<unsigned>((tiles + 7) / 8 * 8)),
+                     dim3(kDmaThreads), 0, s, x, A / k, w1, w3, offsets, sorted_asg, d, ffn, E, k,
+                     h, ntn);
+  return hipGetLastError();
+}
+
+}  // namespace moe

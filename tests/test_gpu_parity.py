@@ -203,6 +203,39 @@ def test_exact_logit_ties_pick_lower_index(m):
     assert (w == 0.5).all()
 
 
+@pytest.mark.parametrize("d,ffn", [(128, 256), (256, 128)])
+def test_prefill_gate_up_tail_tiles(m, d, ffn):
+    """The 256x256-tile gate/up kernel (fragment-order weights, tiled family,
+    used once A >= 768 E) on hand-made routing whose per-expert row counts
+    leave last tiles holding 16, 48, 80, 128, 130 and 250 rows (every
+    token-fragment count the kernel specialises: 2, 4, 6, 8 and 0 for the idle
+    half), an empty expert and an exact multiple of 256; one (d = 128) and two
+    (d = 256) unrolled trips of its K loop. Oracle within the bf16 bar, and
+    bit-identical to the standard-layout kernel (same MFMA sequence)."""
+    counts = [784, 816, 848, 896, 898, 0, 1024, 1018]
+    E, k = len(counts), 2
+    A = sum(counts)
+    assert A >= 768 * E
+    inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=45 + d)
+    sasg = np.random.default_rng(46).permutation(A).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    print(f"[parity] prefill gate/up tails d={d} ffn={ffn} A={A}", flush=True)
+    dev = to_device(inp)
+    o_t = torch.from_numpy(offs).cuda()
+    s_t = torch.from_numpy(sasg).cuda()
+    pw = m.PackedWeights(dev["w1"], dev["w3"], dev["w2"])
+    m.moe_set_ffn_variant(2)
+    try:
+        y_p = m.moe_expert_ffn(dev["x"], pw.w1, pw.w3, pw.w2, o_t, s_t, k, packed=True)
+        y_s = m.moe_expert_ffn(dev["x"], dev["w1"], dev["w3"], dev["w2"], o_t, s_t, k)
+        torch.cuda.synchronize()
+    finally:
+        m.moe_set_ffn_variant(0)
+    assert torch.equal(y_p, y_s)
+    ref = oracle.expert_ffn(inp["x"], inp["w1"], inp["w3"], inp["w2"], offs, sasg, k)
+    assert rel_err(host(y_p), ref) <= OUT_TOL[gen.BF16]
+
+
 # ---------------------------------------------------------------- full size --
 FULL = ["decode_8x7b", "prefill_8x7b", "skew_8x7b", "prefill_8x22b"]
 
