@@ -36,7 +36,9 @@ METRIC = ("MoE-layer tokens/sec at 1 GPU; % of HBM BW peak (decode) / bf16 MFMA 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 STAGES = ("route", "permute", "gate_up", "down", "combine")
-FFN_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_06_amd", "csrc", "ffn_bf16.hip")
+# the gate/up kernels' sources: traffic counters are only reported while they are unchanged
+FFN_SOURCES = [os.path.join(ROOT, "sparse_mixture_experts_06_amd", "csrc", f)
+               for f in ("ffn_bf16.hip", "ffn_dma.hip", "common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -115,23 +117,30 @@ def algorithmic_work(cfg, counts):
     return layer_bytes, layer_flops, gate_up_bytes, gate_up_flops
 
 
+def ffn_sources_sha():
+    h = hashlib.sha256()
+    for path in FFN_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_entry(workload):
     """rocprofv3 FETCH/WRITE bytes of the gate/up kernel, if they were taken
     on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        with open(FFN_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = ffn_sources_sha()
     except (OSError, ValueError):
         return None
     ent = rec.get("workloads", {}).get(workload)
-    if not ent or rec.get("ffn_bf16_sha256") != sha:
+    if not ent or rec.get("ffn_sources_sha256") != sha:
         return None
     return ent.get("hbm_bytes_per_launch")
 
 
-GATE_UP_KERNELS = ("gate_up_stream_kernel", "tiled_kernel<true")
+GATE_UP_KERNELS = ("gate_up_stream_kernel", "gate_up_dma_kernel", "tiled_kernel<true")
 
 
 def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
@@ -158,16 +167,15 @@ def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
     w_factor = w_cal[-1] / calib
     fetch = sum(f_gu) / len(f_gu) / f_factor * 1024
     write = sum(w_gu) / len(w_gu) / w_factor * 1024
-    with open(FFN_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = ffn_sources_sha()
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        if rec.get("ffn_bf16_sha256") != sha:
+        if rec.get("ffn_sources_sha256") != sha:
             rec = {}
     except (OSError, ValueError):
         rec = {}
-    rec["ffn_bf16_sha256"] = sha
+    rec["ffn_sources_sha256"] = sha
     rec.setdefault("workloads", {})[workload] = {
         "hbm_bytes_per_launch": int(fetch + write), "fetch_bytes": int(fetch),
         "write_bytes": int(write), "fetch_counter_per_byte": round(f_factor, 5),
