@@ -8,10 +8,11 @@
 //   r = sorted_asg[p] / k for p in expert e's grouped rows; h is bf16.
 //
 // Tile: 256 weight rows (w1 and w3 rows n .. n+127, n = 128 nt) x 256 token
-// rows per workgroup of 4 waves; wave (wn, wm) owns 64 w1 rows and the same
-// 64 w3 rows (so gate and up of one h column meet in one lane) and tokens
-// 128 wm .. 128 wm + 127: an 8 x 8 grid of 16x16 MFMA tiles (256 accumulator
-// registers). K advances in 32-wide steps. Both operands go global -> LDS
+// rows per workgroup of 8 waves, two per SIMD (so one wave's MFMAs run while
+// the other waits on a load issue or the barrier); wave (wn, wm), wn = 0..3,
+// wm = 0..1, owns 32 w1 rows and the same 32 w3 rows (so gate and up of one h
+// column meet in one lane) and tokens 128 wm .. 128 wm + 127: a 4 x 8 grid of
+// 16x16 MFMA tiles (128 accumulator registers). K advances in 32-wide steps. Both operands go global -> LDS
 // with the 16-byte direct-to-LDS buffer loads, no register staging: one load
 // instruction moves one 1 KiB MFMA fragment (weights: one contiguous KiB of
 // the fragment-order matrix; tokens: 16 gathered rows x 64 bytes) and writes
@@ -20,16 +21,17 @@
 // token) fill one 32 KiB LDS buffer; four buffers hold steps t .. t+3. The
 // loads of step t+4 go out during step t, right after the barrier that frees
 // step t's buffer, so each has three steps of MFMA work to land. The only
-// waits are one "vmcnt <= 16" (this wave's loads of step t+1 done) and one
+// waits are one "vmcnt <= 8" (this wave's loads of step t+1 done) and one
 // barrier per step.
 //
-// Per step a wave runs 16 groups of 4 MFMAs; group g also reads one fragment
-// of step t+1 into the second register set (weights at even g, tokens at odd
-// g) and, for g < 8, issues one of the wave's 8 loads for step t+4. Groups
-// are closed by scheduling barriers and this file is built with the machine
-// scheduler off: that keeps the interleaving as written, and it lets the
-// register allocator keep every accumulator in one place (the scheduler's
-// reordering otherwise makes it rotate the 256 accumulators through copies).
+// Per step a wave runs 8 groups of 4 MFMAs; groups 0-3 also read three
+// fragments each of step t+1 into the second register set (in the order the
+// next step uses them) and issue one of the wave's 4 loads for step t+4.
+// Groups are closed by scheduling barriers and this file is built with the
+// machine scheduler off: that keeps the interleaving as written, and it lets
+// the register allocator keep every accumulator in one place (the
+// scheduler's reordering otherwise makes it rotate the accumulators through
+// copies).
 //
 // Token tiles that run past an expert's rows: each wave computes only its
 // token fragments that hold a row (rounded up to an even count; a template
@@ -50,7 +52,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int DT = 256;             // weight rows and token rows per tile
 constexpr int kFragE = 512;         // bf16 elements per 16x32 fragment (1 KiB)
 constexpr int kBufE = 32 * kFragE;  // one step: 16 weight + 16 token fragments
-constexpr int kDmaThreads = 256;
+constexpr int kDmaThreads = 512;
 // buffer descriptor word 3 (gfx9): 32-bit data format, for raw dword loads
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -117,26 +119,25 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wn = w & 1, wm = w >> 1;
+  const int wn = w & 3, wm = w >> 2;
   const int fr = lane & 15, fg = lane >> 4;
 
-  // this wave loads weight fragments 4w .. 4w+3 and token fragments 4w .. 4w+3
-  // of every step. Weight fragment f is the w1 (f & 4 == 0) or w3 row tile
-  // nt*128 + (f >> 3)*64 + (f & 3)*16, read by wave wn = f >> 3 as its
-  // fragment f & 7: waves with odd w load only w3, the others only w1.
+  // LDS weight fragment f (of 16) is wave wn = f >> 2's tile f & 3: w1 rows
+  // for f & 3 < 2, else w3 rows, nt*128 + (f >> 2)*32 + (f & 1)*16. Wave w
+  // loads weight fragments 2w, 2w+1 (all w1 for even w, all w3 for odd w) and
+  // token fragments 2w, 2w+1 of every step.
   const size_t wslice = static_cast<size_t>(ffn) * d;  // elements of one expert matrix
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(((w & 1) ? w3 : w1) + e * wslice), 0, static_cast<int>(wslice * 2),
       kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x), 0, static_cast<int>(T * d * 2), kRsrcWord3);
-  int aoff[4], boff[4];  // byte offsets of step 0: weights wave-uniform, tokens per lane
+  int aoff[2], boff[2];  // byte offsets of step 0: weights wave-uniform, tokens per lane
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int f = 4 * w + q;
-    const int row = nt * 128 + (f >> 3) * 64 + q * 16;
+  for (int q = 0; q < 2; ++q) {
+    const int row = nt * 128 + (w >> 1) * 32 + q * 16;
     aoff[q] = __builtin_amdgcn_readfirstlane(static_cast<int>(wofs<true>(0, row, 0, ffn, d) * 2));
-    const int mm = min(m0 + f * 16 + fr, M - 1);
+    const int mm = min(m0 + (2 * w + q) * 16 + fr, M - 1);
     boff[q] = ((sorted_asg[beg + mm] / ktop) * d + fg * 8) * 2;
   }
   const int lane16 = lane * 16;
@@ -144,19 +145,19 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
   const int nsteps = d / 32;  // a multiple of 4
   const int last = nsteps - 1;
   auto load_a = [&](uint16_t* L, int q, int t) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr)(L + (4 * w + q) * kFragE), 16, lane16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr)(L + (2 * w + q) * kFragE), 16, lane16,
                                              aoff[q] + t * (kFragE * 2), 0, 0);
   };
   auto load_b = [&](uint16_t* L, int q, int t) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_ptr)(L + (16 + 4 * w + q) * kFragE), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_ptr)(L + (16 + 2 * w + q) * kFragE), 16,
                                              boff[q], t * 64, 0, 0);
   };
   auto load_step = [&](auto bi, int t) {
     uint16_t* L = bufp(bi);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) load_a(L, q, t);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) load_b(L, q, t);
+    load_a(L, 0, t);
+    load_a(L, 1, t);
+    load_b(L, 0, t);
+    load_b(L, 1, t);
   };
   unrolled([&](auto bi) { load_step(bi, min(decltype(bi)::value, last)); },
            std::make_integer_sequence<int, 4>{});
@@ -167,28 +168,28 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
 
   auto run = [&](auto jvc) {
     constexpr int JV = decltype(jvc)::value;
-    u32x4 fa[2][8], fb[2][8];
-    f32x4 acc[8][JV > 0 ? JV : 1];
+    u32x4 fa[2][4], fb[2][8];
+    f32x4 acc[4][JV > 0 ? JV : 1];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < JV; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // fragment k of the step in buffer bi into register set si: k < 8 is the
-    // wave's weight tile k, k >= 8 its token tile k - 8
+    // fragment k of the step in buffer bi into register set si: k < 4 is the
+    // wave's weight tile k, k >= 4 its token tile k - 4
     auto rd = [&](auto bi, auto si, int k) {
       constexpr int S = decltype(si)::value;
       const uint16_t* L = bufp(bi);
-      if (k < 8)
-        fa[S][k] = *reinterpret_cast<const u32x4*>(L + (wn * 8 + k) * kFragE + lane * 8);
-      else if (k - 8 < JV)
-        fb[S][k - 8] = *reinterpret_cast<const u32x4*>(L + (16 + wm * 8 + (k - 8)) * kFragE + lane * 8);
+      if (k < 4)
+        fa[S][k] = *reinterpret_cast<const u32x4*>(L + (wn * 4 + k) * kFragE + lane * 8);
+      else if (k - 4 < JV)
+        fb[S][k - 4] = *reinterpret_cast<const u32x4*>(L + (16 + wm * 8 + (k - 4)) * kFragE + lane * 8);
     };
 
     using I0 = std::integral_constant<int, 0>;
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(24));  // this wave's loads of step 0
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(12));  // this wave's loads of step 0
     lds_barrier();
 #pragma unroll
-    for (int k = 0; k < 16; ++k) rd(I0{}, I0{}, k);
+    for (int k = 0; k < 12; ++k) rd(I0{}, I0{}, k);
 
     int t0 = 0;
     auto step = [&](auto tm) {
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
       const int t = t0 + T;
       // own loads of step t+1 done (those of t+2, t+3 may still fly); the
       // barrier publishes step t+1 and frees buffer T (step t is in registers)
-      __builtin_amdgcn_s_waitcnt(vmcnt_le(16));
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(8));
       lds_barrier();
       const int tl = min(t + 4, last);
       unrolled([&](auto gm) {
@@ -209,25 +210,32 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
           constexpr int j = j0 + decltype(jm)::value;
           if constexpr (j < JV) acc[i][j] = mfma16x16x32(fa[CUR][i], fb[CUR][j], acc[i][j]);
         }, std::make_integer_sequence<int, 4>{});
-        rd(NBUF{}, std::integral_constant<int, NXT>{}, (g & 1) * 8 + (g >> 1));
-        if constexpr (g < 4) load_a(bufp(tm), g, tl);
-        else if constexpr (g < 8) load_b(bufp(tm), g - 4, tl);
+        if constexpr (g < 4) {
+          // next step's fragments in the order it uses them: tokens 0-3,
+          // weight 0, tokens 4-7, weights 1-3
+          constexpr int order[12] = {4, 5, 6, 7, 0, 8, 9, 10, 11, 1, 2, 3};
+          unrolled([&](auto rm) {
+            rd(NBUF{}, std::integral_constant<int, NXT>{}, order[3 * g + decltype(rm)::value]);
+          }, std::make_integer_sequence<int, 3>{});
+          if constexpr (g < 2) load_a(bufp(tm), g, tl);
+          else load_b(bufp(tm), g - 2, tl);
+        }
         __builtin_amdgcn_sched_barrier(0);
-      }, std::make_integer_sequence<int, 16>{});
+      }, std::make_integer_sequence<int, 8>{});
     };
     for (; t0 < nsteps; t0 += 4) unrolled(step, std::make_integer_sequence<int, 4>{});
 
     // epilogue: lane holds token column fr of each 16x16 tile and weight rows
-    // 4*fg .. 4*fg+3 of it; gate in tiles 0-3, up in tiles 4-7
+    // 4*fg .. 4*fg+3 of it; gate in tiles 0-1, up in tiles 2-3
 #pragma unroll
     for (int j = 0; j < JV; ++j) {
       const int m = m0 + wm * 128 + j * 16 + fr;
       if (m >= M) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = nt * 128 + wn * 64 + i * 16 + 4 * fg;
+      for (int i = 0; i < 2; ++i) {
+        const int n = nt * 128 + wn * 32 + i * 16 + 4 * fg;
         f32x4 gt = acc[i][j];
-        f32x4 up = acc[i + 4][j];
+        f32x4 up = acc[i + 2][j];
         // an empty asm with VGPR constraints (no instruction) fixes the
         // accumulators' register class for the allocator
         asm volatile("" : "+v"(gt), "+v"(up));
