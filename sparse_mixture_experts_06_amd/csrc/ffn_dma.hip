@@ -263,8 +263,8 @@ bool dma_gate_up_ok(int64_t A, int k, int d, int ffn, int E) {
   if (d % 128 != 0 || ffn % 128 != 0) return false;
   // every tile costs a full pass over its weight rows whatever its token
   // count, so a part-filled last tile per expert is cheap only when experts
-  // average several full 256-row tiles; below that the 128-row tiles win
-  if (A < static_cast<int64_t>(3 * DT) * E) return false;
+  // average two or more full 256-row tiles; below that the 128-row tiles win
+  if (A < static_cast<int64_t>(2 * DT) * E) return false;
   // byte offsets inside the buffer descriptors are 31-bit
   return static_cast<int64_t>(ffn) * d * 2 <= kMax31 && (A / k) * d * 2 <= kMax31;
 }
