@@ -12,26 +12,30 @@
 // the other waits on a load issue or the barrier); wave (wn, wm), wn = 0..3,
 // wm = 0..1, owns 32 w1 rows and the same 32 w3 rows (so gate and up of one h
 // column meet in one lane) and tokens 128 wm .. 128 wm + 127: a 4 x 8 grid of
-// 16x16 MFMA tiles (128 accumulator registers). K advances in 32-wide steps. Both operands go global -> LDS
-// with the 16-byte direct-to-LDS buffer loads, no register staging: one load
-// instruction moves one 1 KiB MFMA fragment (weights: one contiguous KiB of
-// the fragment-order matrix; tokens: 16 gathered rows x 64 bytes) and writes
-// it to LDS in lane order, so each ds_read_b128 of a fragment reads one
-// contiguous KiB (no bank conflicts). A step's 32 fragments (16 weight, 16
-// token) fill one 32 KiB LDS buffer; four buffers hold steps t .. t+3. The
-// loads of step t+4 go out during step t, right after the barrier that frees
-// step t's buffer, so each has three steps of MFMA work to land. The only
-// waits are one "vmcnt <= 8" (this wave's loads of step t+1 done) and one
-// barrier per step.
+// 16x16 MFMA tiles (128 accumulator registers). K advances in 32-wide steps.
+//
+// Both operands go global -> LDS with the 16-byte direct-to-LDS buffer loads,
+// no register staging. Weights: one load instruction moves one 1 KiB MFMA
+// fragment (one contiguous KiB of the fragment-order matrix) into LDS in lane
+// order; four 16 KiB buffers hold the weight fragments of steps t .. t+3.
+// Tokens: one load instruction moves 8 gathered rows x 128 bytes, whole cache
+// lines covering two K steps (half the L2 requests of 16 rows x 64 bytes,
+// which measured 13-15% slower); two 32 KiB buffers hold 64-wide K stages of
+// the 256 rows, row-major, with the 16-byte chunk c of row r stored in slot
+// c ^ ((r / 2) % 8), so that every MFMA fragment read (16 rows, one chunk)
+// touches 16 distinct bank groups. Weight loads of step t+4 go out in step t
+// (three steps of lead), token loads of stage (t+3)/2 in odd steps t (two
+// steps of lead), tokens before weights so that the in-order load counter
+// never makes a wait cover a younger weight load. The only waits are one
+// "vmcnt <= 4" (odd steps) or "<= 8" (even steps) and one barrier per step.
 //
 // Per step a wave runs 8 groups of 4 MFMAs; groups 0-3 also read three
 // fragments each of step t+1 into the second register set (in the order the
-// next step uses them) and issue one of the wave's 4 loads for step t+4.
-// Groups are closed by scheduling barriers and this file is built with the
-// machine scheduler off: that keeps the interleaving as written, and it lets
-// the register allocator keep every accumulator in one place (the
-// scheduler's reordering otherwise makes it rotate the accumulators through
-// copies).
+// next step uses them) and issue the step's loads. Groups are closed by
+// scheduling barriers and this file is built with the machine scheduler off:
+// that keeps the interleaving as written, and it lets the register allocator
+// keep every accumulator in one place (the scheduler's reordering otherwise
+// makes it rotate the accumulators through copies).
 //
 // Token tiles that run past an expert's rows: each wave computes only its
 // token fragments that hold a row (rounded up to an even count; a template
@@ -51,7 +55,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int DT = 256;             // weight rows and token rows per tile
 constexpr int kFragE = 512;         // bf16 elements per 16x32 fragment (1 KiB)
-constexpr int kBufE = 32 * kFragE;  // one step: 16 weight + 16 token fragments
+constexpr int kWBufE = 16 * kFragE; // one K32 step of the 16 weight fragments (16 KiB)
+constexpr int kTBufE = DT * 64;     // one K64 stage of the 256 token rows (32 KiB)
 constexpr int kDmaThreads = 512;
 // buffer descriptor word 3 (gfx9): 32-bit data format, for raw dword loads
 constexpr int kRsrcWord3 = 0x00020000;
@@ -104,67 +109,87 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
 
   // one array per buffer: distinct objects let the compiler see that a
   // fragment read does not depend on the loads in flight to other buffers
-  __shared__ __attribute__((aligned(1024))) uint16_t buf0[kBufE];
-  __shared__ __attribute__((aligned(1024))) uint16_t buf1[kBufE];
-  __shared__ __attribute__((aligned(1024))) uint16_t buf2[kBufE];
-  __shared__ __attribute__((aligned(1024))) uint16_t buf3[kBufE];
-  auto bufp = [&](auto bi) -> uint16_t* {
+  __shared__ __attribute__((aligned(1024))) uint16_t wb0[kWBufE];
+  __shared__ __attribute__((aligned(1024))) uint16_t wb1[kWBufE];
+  __shared__ __attribute__((aligned(1024))) uint16_t wb2[kWBufE];
+  __shared__ __attribute__((aligned(1024))) uint16_t wb3[kWBufE];
+  __shared__ __attribute__((aligned(1024))) uint16_t tb0[kTBufE];
+  __shared__ __attribute__((aligned(1024))) uint16_t tb1[kTBufE];
+  auto wbufp = [&](auto bi) -> uint16_t* {
     constexpr int B = decltype(bi)::value;
-    if constexpr (B == 0) return buf0;
-    else if constexpr (B == 1) return buf1;
-    else if constexpr (B == 2) return buf2;
-    else return buf3;
+    if constexpr (B == 0) return wb0;
+    else if constexpr (B == 1) return wb1;
+    else if constexpr (B == 2) return wb2;
+    else return wb3;
   };
-
+  auto tbufp = [&](auto bi) -> uint16_t* {
+    constexpr int B = decltype(bi)::value;
+    if constexpr (B == 0) return tb0;
+    else return tb1;
+  };
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wn = w & 3, wm = w >> 2;
   const int fr = lane & 15, fg = lane >> 4;
-
   // LDS weight fragment f (of 16) is wave wn = f >> 2's tile f & 3: w1 rows
   // for f & 3 < 2, else w3 rows, nt*128 + (f >> 2)*32 + (f & 1)*16. Wave w
-  // loads weight fragments 2w, 2w+1 (all w1 for even w, all w3 for odd w) and
-  // token fragments 2w, 2w+1 of every step.
+  // loads weight fragments 2w, 2w+1 (all w1 for even w, all w3 for odd w).
   const size_t wslice = static_cast<size_t>(ffn) * d;  // elements of one expert matrix
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(((w & 1) ? w3 : w1) + e * wslice), 0, static_cast<int>(wslice * 2),
-      kRsrcWord3);
+      const_cast<uint16_t*>(((w & 1) ? w3 : w1) + e * wslice), 0, static_cast<int>(wslice * 2), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x), 0, static_cast<int>(T * d * 2), kRsrcWord3);
-  int aoff[2], boff[2];  // byte offsets of step 0: weights wave-uniform, tokens per lane
+  int aoff[2];  // byte offsets of step 0 (wave-uniform)
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int row = nt * 128 + (w >> 1) * 32 + q * 16;
     aoff[q] = __builtin_amdgcn_readfirstlane(static_cast<int>(wofs<true>(0, row, 0, ffn, d) * 2));
-    const int mm = min(m0 + (2 * w + q) * 16 + fr, M - 1);
-    boff[q] = ((sorted_asg[beg + mm] / ktop) * d + fg * 8) * 2;
+  }
+  // token loads: wave w moves tile rows 32w .. 32w+31, 8 rows x 128 B per load; lane l puts row
+  // 32w + 8q + l/8, LDS slot l%8, which holds 16-byte chunk (l%8) ^ ((row/2) % 8) of the K64 stage
+  int toff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 32 * w + 8 * q + (lane >> 3);
+    const int mm = min(m0 + r, M - 1);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    toff[q] = ((sorted_asg[beg + mm] / ktop) * d + c * 8) * 2;
   }
   const int lane16 = lane * 16;
-
-  const int nsteps = d / 32;  // a multiple of 4
+  const int nsteps = d / 32;       // a multiple of 4
   const int last = nsteps - 1;
-  auto load_a = [&](uint16_t* L, int q, int t) {
+  const int last_stage = nsteps / 2 - 1;
+  auto load_w = [&](uint16_t* L, int q, int t) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr)(L + (2 * w + q) * kFragE), 16, lane16,
                                              aoff[q] + t * (kFragE * 2), 0, 0);
   };
-  auto load_b = [&](uint16_t* L, int q, int t) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_ptr)(L + (16 + 2 * w + q) * kFragE), 16,
-                                             boff[q], t * 64, 0, 0);
+  auto load_x = [&](uint16_t* L, int q, int s) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_ptr)(L + (32 * w + 8 * q) * 64), 16, toff[q],
+                                             s * 128, 0, 0);
   };
-  auto load_step = [&](auto bi, int t) {
-    uint16_t* L = bufp(bi);
-    load_a(L, 0, t);
-    load_a(L, 1, t);
-    load_b(L, 0, t);
-    load_b(L, 1, t);
-  };
-  unrolled([&](auto bi) { load_step(bi, min(decltype(bi)::value, last)); },
-           std::make_integer_sequence<int, 4>{});
+  // prologue: the loads steps -4 .. -1 would have issued in the steady state
+  // (weights of steps 0-3, token stages 0-1; odd steps tokens first), so the
+  // loop's wait counts hold from its first step
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  load_w(wbufp(I0{}), 0, 0); load_w(wbufp(I0{}), 1, 0);
+  load_x(tbufp(I0{}), 0, 0); load_x(tbufp(I0{}), 1, 0); load_x(tbufp(I0{}), 2, 0); load_x(tbufp(I0{}), 3, 0);
+  load_w(wbufp(I1{}), 0, min(1, last)); load_w(wbufp(I1{}), 1, min(1, last));
+  load_w(wbufp(I2{}), 0, min(2, last)); load_w(wbufp(I2{}), 1, min(2, last));
+  load_x(tbufp(I1{}), 0, min(1, last_stage)); load_x(tbufp(I1{}), 1, min(1, last_stage));
+  load_x(tbufp(I1{}), 2, min(1, last_stage)); load_x(tbufp(I1{}), 3, min(1, last_stage));
+  load_w(wbufp(I3{}), 0, min(3, last)); load_w(wbufp(I3{}), 1, min(3, last));
 
   // fragments of this wave's token tiles that hold a row, rounded up to even
   const int valid = M - m0 - wm * 128;
   const int jv = valid >= 128 ? 8 : valid <= 0 ? 0 : (((valid + 15) >> 4) + 1) & ~1;
+  // token fragment reads: row (wm*128 + 16j + fr), chunk 4*half + fg, swizzled slot
+  const int trow = (wm * 128 + fr) * 64;
+  const int tcol0 = ((fg) ^ ((fr >> 1) & 7)) * 8;
+  const int tcol1 = ((4 + fg) ^ ((fr >> 1) & 7)) * 8;
 
   auto run = [&](auto jvc) {
     constexpr int JV = decltype(jvc)::value;
@@ -174,35 +199,40 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < JV; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // fragment k of the step in buffer bi into register set si: k < 4 is the
-    // wave's weight tile k, k >= 4 its token tile k - 4
-    auto rd = [&](auto bi, auto si, int k) {
+    // fragment k of a step into register set si: k < 4 the wave's weight tile
+    // k (weight buffer wi), k >= 4 its token tile k - 4 (token buffer ti, half hh)
+    auto rd = [&](auto wi, auto ti, auto hh, auto si, int k) {
       constexpr int S = decltype(si)::value;
-      const uint16_t* L = bufp(bi);
-      if (k < 4)
-        fa[S][k] = *reinterpret_cast<const u32x4*>(L + (wn * 4 + k) * kFragE + lane * 8);
-      else if (k - 4 < JV)
-        fb[S][k - 4] = *reinterpret_cast<const u32x4*>(L + (16 + wm * 8 + (k - 4)) * kFragE + lane * 8);
+      constexpr int HH = decltype(hh)::value;
+      if (k < 4) {
+        fa[S][k] = *reinterpret_cast<const u32x4*>(wbufp(wi) + (wn * 4 + k) * kFragE + lane * 8);
+      } else if (k - 4 < JV) {
+        const uint16_t* TL = tbufp(ti);
+        fb[S][k - 4] = *reinterpret_cast<const u32x4*>(TL + trow + (k - 4) * 16 * 64 + (HH ? tcol1 : tcol0));
+      }
     };
-
-    using I0 = std::integral_constant<int, 0>;
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(12));  // this wave's loads of step 0
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(10));  // weights of step 0 and token stage 0
     lds_barrier();
 #pragma unroll
-    for (int k = 0; k < 12; ++k) rd(I0{}, I0{}, k);
+    for (int k = 0; k < 12; ++k) rd(I0{}, I0{}, I0{}, I0{}, k);
 
     int t0 = 0;
     auto step = [&](auto tm) {
-      // step t0 + T lives in buffer T and register set T % 2 (t0 % 4 == 0)
+      // step t = t0 + T: weights in wbuf T, tokens in tbuf T/2 half T%2 (t0 % 4 == 0)
       constexpr int T = decltype(tm)::value;
       constexpr int CUR = T & 1, NXT = CUR ^ 1;
-      using NBUF = std::integral_constant<int, (T + 1) & 3>;
+      using WN = std::integral_constant<int, (T + 1) & 3>;
+      using TN = std::integral_constant<int, ((T + 1) >> 1) & 1>;
+      using HN = std::integral_constant<int, (T + 1) & 1>;
       const int t = t0 + T;
-      // own loads of step t+1 done (those of t+2, t+3 may still fly); the
-      // barrier publishes step t+1 and frees buffer T (step t is in registers)
-      __builtin_amdgcn_s_waitcnt(vmcnt_le(8));
+      // own loads of step t+1 done: weights (issued in step t-3) and its token
+      // stage (issued in step t-2 for odd t, t-3 for even t; counted from the
+      // issue order above); the barrier publishes step t+1 and frees the
+      // buffers step t was read from (it is in registers)
+      __builtin_amdgcn_s_waitcnt(vmcnt_le((T & 1) ? 4 : 8));
       lds_barrier();
-      const int tl = min(t + 4, last);
+      const int tw = min(t + 4, last);
+      const int ts = min((t + 3) >> 1, last_stage);
       unrolled([&](auto gm) {
         constexpr int g = decltype(gm)::value;
         constexpr int i = g >> 1, j0 = (g & 1) * 4;
@@ -215,16 +245,22 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
           // weight 0, tokens 4-7, weights 1-3
           constexpr int order[12] = {4, 5, 6, 7, 0, 8, 9, 10, 11, 1, 2, 3};
           unrolled([&](auto rm) {
-            rd(NBUF{}, std::integral_constant<int, NXT>{}, order[3 * g + decltype(rm)::value]);
+            rd(WN{}, TN{}, HN{}, std::integral_constant<int, NXT>{}, order[3 * g + decltype(rm)::value]);
           }, std::make_integer_sequence<int, 3>{});
-          if constexpr (g < 2) load_a(bufp(tm), g, tl);
-          else load_b(bufp(tm), g - 2, tl);
+          if constexpr (T & 1) {
+            // tokens of stage (t+3)/2 into the buffer stage (t-1)/2 has left,
+            // then the weights of step t+4
+            using TB = std::integral_constant<int, ((T + 3) >> 1) & 1>;
+            if constexpr (g < 2) { load_x(tbufp(TB{}), 2 * g, ts); load_x(tbufp(TB{}), 2 * g + 1, ts); }
+            else load_w(wbufp(tm), g - 2, tw);
+          } else {
+            if constexpr (g < 2) load_w(wbufp(tm), g, tw);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }, std::make_integer_sequence<int, 8>{});
     };
     for (; t0 < nsteps; t0 += 4) unrolled(step, std::make_integer_sequence<int, 4>{});
-
     // epilogue: lane holds token column fr of each 16x16 tile and weight rows
     // 4*fg .. 4*fg+3 of it; gate in tiles 0-1, up in tiles 2-3
 #pragma unroll
@@ -254,7 +290,6 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
     default: run(std::integral_constant<int, 0>{}); break;
   }
 }
-
 constexpr int64_t kMax31 = (int64_t(1) << 31) - 1;
 
 }  // namespace
