@@ -116,8 +116,10 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* count
  * moe_permute. For MOE_BF16 / MOE_BF16_PACKED the gate/up products
  * accumulate in float32, the SwiGLU activation is rounded to bfloat16 (the
  * down projection's MFMA input) and the down projection accumulates in
- * float32 (on few rows per expert it splits K two ways and adds the two
- * float32 partial sums in a fixed order). ws must hold
+ * float32 (on few rows per expert, and on many where it packs the tiles
+ * better onto the GPU, it splits K two ways and adds the two float32 partial
+ * sums in a fixed order; the split depends on T, d, ffn, E and k only, so
+ * MOE_BF16 and MOE_BF16_PACKED give bit-identical y). ws must hold
  * moe_workspace_bytes(T, d, ffn, E, k, dtype) bytes. */
 int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
                    const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d,

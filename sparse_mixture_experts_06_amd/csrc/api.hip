@@ -22,14 +22,19 @@ struct Layout {
 
 inline bool is_bf16(int dtype) { return dtype == MOE_BF16 || dtype == MOE_BF16_PACKED; }
 
-// float32 partial results the down projection may leave (split K); sized for
-// the streaming kernels so that the workspace does not depend on the variant
-int ws_splits(int64_t A, int dtype) { return is_bf16(dtype) ? moe::down_splits(1, A) : 1; }
+// float32 partial results the down projection may leave (split K); the most
+// either kernel family leaves, so that the workspace does not depend on the
+// variant
+int ws_splits(int64_t A, int d, int ffn, int E, int dtype) {
+  if (!is_bf16(dtype)) return 1;
+  const int a = moe::down_splits(1, A, d, ffn, E), b = moe::down_splits(2, A, d, ffn, E);
+  return a > b ? a : b;
+}
 
 Layout layout(int64_t T, int d, int ffn, int E, int k, int dtype) {
   const size_t A = static_cast<size_t>(T) * static_cast<size_t>(k);
   const size_t hb = is_bf16(dtype) ? 2 : 4;
-  const size_t ns = static_cast<size_t>(ws_splits(static_cast<int64_t>(A), dtype));
+  const size_t ns = static_cast<size_t>(ws_splits(static_cast<int64_t>(A), d, ffn, E, dtype));
   Layout L;
   size_t o = 0;
   L.idx = o;     o = align256(o + A * 4);
@@ -62,7 +67,8 @@ int check_ffn_shape(int64_t T, int d, int ffn, int E, int k, int dtype) {
     if (d % 64 != 0 || ffn % 64 != 0) return MOE_ENOTSUP;
     // worst-case tile grid of the tiled kernels must fit a 1-D launch
     const int64_t mt = (A + 127) / 128 + E;
-    const int64_t n = (ffn / 64 > (d + 127) / 128) ? ffn / 64 : (d + 127) / 128;
+    // (the down grid doubles when it splits K)
+    const int64_t n = (ffn / 64 > 2 * ((d + 127) / 128)) ? ffn / 64 : 2 * ((d + 127) / 128);
     if (mt * n >= (int64_t(1) << 31)) return MOE_ENOTSUP;
   } else {
     const int64_t mt = (A + 15) / 16 + E;
@@ -88,7 +94,7 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
   if (is_bf16(dtype)) {
     const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
     const bool packed = dtype == MOE_BF16_PACKED;
-    *nsplit_out = moe::down_splits(variant, A);
+    *nsplit_out = moe::down_splits(variant, A, d, ffn, E);
     err = moe::launch_gate_up_bf16(variant, packed, static_cast<const uint16_t*>(x),
                                    static_cast<const uint16_t*>(w1),
                                    static_cast<const uint16_t*>(w3), offsets, sorted_asg, A, d,
@@ -176,7 +182,7 @@ int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, con
   char* base = static_cast<char*>(ws);
   const int64_t A = T * k;
   const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
-  const int nsplit = is_bf16(dtype) ? moe::down_splits(variant, A) : 1;
+  const int nsplit = is_bf16(dtype) ? moe::down_splits(variant, A, d, ffn, E) : 1;
   float* part = nsplit > 1 ? reinterpret_cast<float*>(base + L.y) : y;
   int used = 1;
   st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, part, base + L.h, s,

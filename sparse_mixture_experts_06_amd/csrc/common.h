@@ -95,8 +95,10 @@ hipError_t launch_permute(const int32_t* idx, int64_t A, int E, int32_t* counts,
 
 // bf16 experts: gate/up (+SiLU*mul) -> h [A, ffn] bf16, down -> y [A, d] f32.
 // `variant` is resolved (1 streaming, 2 tiled); `packed` selects the
-// fragment-order weight layout. The down kernel writes down_splits(variant, A)
-// float32 partial results [nsplit, A, d] whose sum (in split order) is y.
+// fragment-order weight layout. The down kernel writes
+// down_splits(variant, A, d, ffn, E) float32 partial results [nsplit, A, d]
+// whose sum (in split order) is y; the count depends on the sizes only, not
+// on the layout, so both layouts give bit-identical y.
 hipError_t launch_gate_up_bf16(int variant, bool packed, const uint16_t* x, const uint16_t* w1,
                                const uint16_t* w3, const int32_t* offsets,
                                const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
@@ -104,14 +106,20 @@ hipError_t launch_gate_up_bf16(int variant, bool packed, const uint16_t* x, cons
 hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const uint16_t* w2,
                             const int32_t* offsets, int64_t A, int d, int ffn, int E, float* part,
                             hipStream_t s);
-int down_splits(int variant, int64_t A);
+int down_splits(int variant, int64_t A, int d, int ffn, int E);
 
-// gate/up for many rows per expert with fragment-order weights and
-// direct-to-LDS loads (ffn_dma.hip): the sizes it is used for, and its launcher
+// gate/up and down for many rows per expert with fragment-order weights and
+// direct-to-LDS loads (ffn_dma.hip): the sizes they are used for, the K split
+// of the down projection (1 or 2) and the launchers
 bool dma_gate_up_ok(int64_t A, int k, int d, int ffn, int E);
 hipError_t launch_gate_up_dma(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
                               const int32_t* offsets, const int32_t* sorted_asg, int64_t A, int d,
                               int ffn, int E, int k, uint16_t* h, hipStream_t s);
+bool dma_down_ok(int64_t A, int d, int ffn, int E);
+int dma_down_splits(int64_t A, int d, int ffn, int E);
+hipError_t launch_down_dma(const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
+                           int64_t A, int d, int ffn, int E, int nsplit, float* part,
+                           hipStream_t s);
 // standard [E, R, C] bf16 -> fragment order (16-row x 32-column fragments)
 hipError_t launch_pack_bf16(const uint16_t* w, int E, int R, int C, uint16_t* out, hipStream_t s);
 

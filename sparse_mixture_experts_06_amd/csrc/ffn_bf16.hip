@@ -312,17 +312,18 @@ constexpr int BN = 128;  // weight rows per tile (MFMA A operand)
 constexpr int BK = 64;   // K per LDS stage: 8 chunks of 16 bytes per row
 constexpr int kTiledThreads = 256;
 
-// Maps this workgroup to (expert, first token row, n-tile). Tiles are counted
+// Maps this workgroup to (expert, first token row, n-tile, K split). Tiles are counted
 // from the device-side offsets, so no host synchronisation is needed; the
 // grid is sized for the worst case and surplus workgroups return. Workgroup b
 // runs on XCD b % 8, so XCD x is given the contiguous logical range
 // [x*per, (x+1)*per).
 __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets, int E, int ntn,
-                                            int& e, int& beg, int& M, int& m0, int& nt) {
+                                            int nsplit, int& e, int& beg, int& M, int& m0,
+                                            int& nt, int& sp) {
   int total = 0;
   for (int i = 0; i < E; ++i) {
     const int Mi = offsets[i + 1] - offsets[i];
-    total += ((Mi + BM - 1) / BM) * ntn;
+    total += ((Mi + BM - 1) / BM) * ntn * nsplit;
   }
   const int per = (total + 7) / 8;
   const int q = blockIdx.x >> 3;
@@ -332,13 +333,15 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
   for (int i = 0; i < E; ++i) {
     const int Mi = offsets[i + 1] - offsets[i];
     const int mt = (Mi + BM - 1) / BM;
-    const int cnt = mt * ntn;
+    const int cnt = mt * ntn * nsplit;
     if (L < cnt) {
       e = i;
       beg = offsets[i];
       M = Mi;
-      nt = L / mt;
       m0 = (L % mt) * BM;
+      const int r = L / mt;
+      nt = r % ntn;
+      sp = r / ntn;
       return true;
     }
     L -= cnt;
@@ -352,7 +355,9 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chu
 // the 128 weight rows of a tile are w1 rows [n, n+32), w3 rows [n, n+32),
 // w1 rows [n+32, n+64), w3 rows [n+32, n+64) with n = nt*64, so wave column
 // wn holds gate and up for the same 32 h-columns.
-// !GATE_UP: act = h (grouped rows), wa = w2, out = y f32 [A, N=d].
+// !GATE_UP: act = h (grouped rows), wa = w2, out = y f32 [A, N=d], or with
+// nsplit > 1 partial sums over K ranges [sp K/nsplit, (sp+1) K/nsplit) in
+// nsplit arrays pstride floats apart.
 //
 // Pipeline: the global loads of K stage s are issued two iterations before
 // stage s is written to LDS (two register sets alternate), so each load has
@@ -368,9 +373,12 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ wa,
     const uint16_t* __restrict__ wb, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_asg, int K, int N, int E, int ktop,
-    void* __restrict__ out, int ntn) {
-  int e, beg, M, m0, nt;
-  if (!decode_tile(offsets, E, ntn, e, beg, M, m0, nt)) return;
+    void* __restrict__ out, int ntn, int nsplit, int64_t pstride) {
+  int e, beg, M, m0, nt, sp;
+  if (!decode_tile(offsets, E, ntn, nsplit, e, beg, M, m0, nt, sp)) return;
+  // this tile's K range [k0, k0 + Kc); split K only for down (nsplit 1 for gate/up)
+  const int Kc = K / nsplit;
+  const int k0 = sp * Kc;
 
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][BN * BK];
   __shared__ __attribute__((aligned(16))) uint16_t sX[2][BM * BK];
@@ -413,7 +421,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
       Rw = (tid >> 3) + 32 * j;
       cw = tid & 7;
     }
-    gw[j] = wmat(Rw) + wofs<PACKED>(e, wrow(Rw), cw * 8, N, K);
+    gw[j] = wmat(Rw) + wofs<PACKED>(e, wrow(Rw), k0 + cw * 8, N, K);
     sow[j] = swz(Rw, cw);
     // token chunk j: LDS row Rx, chunk cx
     const int Rx = (tid >> 3) + 32 * j;
@@ -425,7 +433,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
     } else {
       row = beg + mm;
     }
-    gx[j] = act + row * K + cx * 8;
+    gx[j] = act + row * K + k0 + cx * 8;
     sox[j] = swz(Rx, cx);
   }
 
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
+  const int nk = Kc / BK;
   u32x4 rw[2][4], rx[2][4];
   auto issue = [&](int set, int kb) {
 #pragma unroll
@@ -529,8 +537,8 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
       for (int i = 0; i < 4; ++i) {
         const int n = nt * BN + wn * 64 + i * 16 + 4 * fg;
         if (n < N)
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + static_cast<size_t>(beg + m) * N +
-                                    n) = acc[i][j];
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + sp * pstride +
+                                    static_cast<size_t>(beg + m) * N + n) = acc[i][j];
       }
     }
   }
@@ -561,8 +569,8 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
     const uint16_t* __restrict__ wb, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_asg, int K, int N, int E, int ktop,
     void* __restrict__ out, int ntn) {
-  int e, beg, M, m0, nt;
-  if (!decode_tile(offsets, E, ntn, e, beg, M, m0, nt)) return;
+  int e, beg, M, m0, nt, sp;
+  if (!decode_tile(offsets, E, ntn, 1, e, beg, M, m0, nt, sp)) return;
 
   __shared__ __attribute__((aligned(16))) uint16_t sX[2][BM * BK];
 
@@ -719,9 +727,9 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
 // weight ring depth and workgroups per CU of wtiled_kernel
 constexpr int kWRing = 8, kWOcc = 1, kWXSets = 2;
 
-inline unsigned tiled_grid(int64_t A, int E, int ntn) {
+inline unsigned tiled_grid(int64_t A, int E, int ntn, int nsplit = 1) {
   const int64_t mt = (A + BM - 1) / BM + E;
-  const int64_t tiles = mt * ntn;
+  const int64_t tiles = mt * ntn * nsplit;
   return static_cast<unsigned>((tiles + 7) / 8 * 8);
 }
 
@@ -750,7 +758,7 @@ hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, cons
     const int ntn = ffn / 64;
     hipLaunchKernelGGL((tiled_kernel<true, PACKED>), dim3(tiled_grid(A, E, ntn)),
                        dim3(kTiledThreads), 0, s, x, w1, w3, offsets, sorted_asg, d, ffn, E, k,
-                       static_cast<void*>(h), ntn);
+                       static_cast<void*>(h), ntn, 1, int64_t(0));
   }
   return hipGetLastError();
 }
@@ -758,8 +766,8 @@ hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, cons
 template <bool PACKED>
 hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
                      int64_t A, int d, int ffn, int E, float* part, hipStream_t s) {
+  const int nsplit = down_splits(variant, A, d, ffn, E);
   if (variant == 1) {
-    const int nsplit = down_splits(1, A);
     constexpr int rows = 16 * kDownRT;
     if (d % rows != 0) {
       const unsigned blocks =
@@ -774,7 +782,9 @@ hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const i
                          dim3(kWave * kStreamWaves), 0, s, h, w2, offsets, ffn, d,
                          static_cast<int>(A), nsplit, part);
     }
-  } else if (PACKED && d % 256 == 0) {
+  } else if (PACKED && dma_down_ok(A, d, ffn, E)) {
+    return launch_down_dma(h, w2, offsets, A, d, ffn, E, nsplit, part, s);
+  } else if (PACKED && d % 256 == 0 && nsplit == 1) {
     const int ntn = d / 256;
     hipLaunchKernelGGL((wtiled_kernel<false, PACKED, kWRing, kWOcc, kWXSets>), dim3(tiled_grid(A, E, ntn)),
                        dim3(kTiledThreads), 0, s, h, w2, w2, offsets,
@@ -782,10 +792,10 @@ hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const i
                        static_cast<void*>(part), ntn);
   } else {
     const int ntn = (d + BN - 1) / BN;
-    hipLaunchKernelGGL((tiled_kernel<false, PACKED>), dim3(tiled_grid(A, E, ntn)),
+    hipLaunchKernelGGL((tiled_kernel<false, PACKED>), dim3(tiled_grid(A, E, ntn, nsplit)),
                        dim3(kTiledThreads), 0, s, h, w2, w2, offsets,
                        static_cast<const int32_t*>(nullptr), ffn, d, E, 1,
-                       static_cast<void*>(part), ntn);
+                       static_cast<void*>(part), ntn, nsplit, A * d);
   }
   return hipGetLastError();
 }
@@ -798,10 +808,14 @@ int choose_ffn_variant(int requested, int64_t A, int E) {
   return (A <= static_cast<int64_t>(32) * E) ? 1 : 2;
 }
 
-int down_splits(int variant, int64_t A) {
+int down_splits(int variant, int64_t A, int d, int ffn, int E) {
   // the streaming down kernel splits K two ways while its float32 partials
-  // stay small; the tiled kernels write the final sums directly
-  return (variant == 1 && A <= 4096) ? 2 : 1;
+  // stay small; the tiled kernels split K where the 256-row tiles of the
+  // direct-to-LDS kernel would leave the last round over the CUs part-empty
+  // (the 128-row kernels follow the same split, so y does not depend on the
+  // weight layout)
+  if (variant == 1) return A <= 4096 ? 2 : 1;
+  return dma_down_splits(A, d, ffn, E);
 }
 
 hipError_t launch_pack_bf16(const uint16_t* w, int E, int R, int C, uint16_t* out, hipStream_t s) {

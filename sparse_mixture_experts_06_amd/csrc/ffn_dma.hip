@@ -1,33 +1,39 @@
-// Expert gate/up projection for many rows per expert (prefill) with
-// fragment-order weights: the first grouped GEMM of the Mixtral sparse-MoE
-// block (nnterp Mixtral page, support(): the down projection receives
-// act(gate) * up with act = SiLU; the experts are one stacked module), fused
-// with that activation, as in ffn_bf16.hip:
+// Expert projections for many rows per expert (prefill) with fragment-order
+// weights: both grouped GEMMs of the Mixtral sparse-MoE block (nnterp Mixtral
+// page, support(): the down projection receives act(gate) * up with act =
+// SiLU; the experts are one stacked module), the first fused with that
+// activation, as in ffn_bf16.hip:
 //
-//   h[p, n] = silu(sum_i x[r,i] w1[e,n,i]) * (sum_i x[r,i] w3[e,n,i]),
-//   r = sorted_asg[p] / k for p in expert e's grouped rows; h is bf16.
+//   gate/up: h[p, n] = silu(sum_i x[r,i] w1[e,n,i]) * (sum_i x[r,i] w3[e,n,i]),
+//            r = sorted_asg[p] / k for p in expert e's grouped rows; h is bf16;
+//   down:    y[p, n] = sum_i h[p,i] w2[e,n,i], float32, optionally split in K
+//            into nsplit partial sums (written to part[sp]; their sum in split
+//            order is y).
 //
-// Tile: 256 weight rows (w1 and w3 rows n .. n+127, n = 128 nt) x 256 token
-// rows per workgroup of 8 waves, two per SIMD (so one wave's MFMAs run while
-// the other waits on a load issue or the barrier); wave (wn, wm), wn = 0..3,
-// wm = 0..1, owns 32 w1 rows and the same 32 w3 rows (so gate and up of one h
-// column meet in one lane) and tokens 128 wm .. 128 wm + 127: a 4 x 8 grid of
-// 16x16 MFMA tiles (128 accumulator registers). K advances in 32-wide steps.
+// Tile: 256 weight rows x 256 token rows per workgroup of 8 waves, two per
+// SIMD (so one wave's MFMAs run while the other waits on a load issue or the
+// barrier); wave (wn, wm), wn = 0..3, wm = 0..1, owns 64 weight rows and
+// tokens 128 wm .. 128 wm + 127: a 4 x 8 grid of 16x16 MFMA tiles (128
+// accumulator registers). For gate/up the 64 rows are 32 w1 rows and the same
+// 32 w3 rows (w1 and w3 rows n .. n+127 per tile, n = 128 nt), so gate and up
+// of one h column meet in one lane; for down they are w2 rows 256 nt + 64 wn
+// .. + 63. K advances in 32-wide steps.
 //
 // Both operands go global -> LDS with the 16-byte direct-to-LDS buffer loads,
 // no register staging. Weights: one load instruction moves one 1 KiB MFMA
 // fragment (one contiguous KiB of the fragment-order matrix) into LDS in lane
 // order; four 16 KiB buffers hold the weight fragments of steps t .. t+3.
-// Tokens: one load instruction moves 8 gathered rows x 128 bytes, whole cache
-// lines covering two K steps (half the L2 requests of 16 rows x 64 bytes,
-// which measured 13-15% slower); two 32 KiB buffers hold 64-wide K stages of
-// the 256 rows, row-major, with the 16-byte chunk c of row r stored in slot
-// c ^ ((r / 2) % 8), so that every MFMA fragment read (16 rows, one chunk)
-// touches 16 distinct bank groups. Weight loads of step t+4 go out in step t
-// (three steps of lead), token loads of stage (t+3)/2 in odd steps t (two
-// steps of lead), tokens before weights so that the in-order load counter
-// never makes a wait cover a younger weight load. The only waits are one
-// "vmcnt <= 4" (odd steps) or "<= 8" (even steps) and one barrier per step.
+// Tokens: one load instruction moves 8 token rows x 128 bytes (gathered rows
+// of x for gate/up, grouped rows of h for down), whole cache lines covering
+// two K steps (half the L2 requests of 16 rows x 64 bytes, which measured
+// 13-15% slower); two 32 KiB buffers hold 64-wide K stages of the 256 rows,
+// row-major, with the 16-byte chunk c of row r stored in slot c ^ ((r / 2) %
+// 8), so that every MFMA fragment read (16 rows, one chunk) touches 16
+// distinct bank groups. Weight loads of step t+4 go out in step t (three
+// steps of lead), token loads of stage (t+3)/2 in odd steps t (two steps of
+// lead), tokens before weights so that the in-order load counter never makes
+// a wait cover a younger weight load. The only waits are one "vmcnt <= 4"
+// (odd steps) or "<= 8" (even steps) and one barrier per step.
 //
 // Per step a wave runs 8 groups of 4 MFMAs; groups 0-3 also read three
 // fragments each of step t+1 into the second register set (in the order the
@@ -41,6 +47,10 @@
 // token fragments that hold a row (rounded up to an even count; a template
 // parameter, so the loop stays branch-free), and still issues all loads and
 // barriers with the other waves.
+//
+// Every output element is one float32 MFMA accumulation over its K range in
+// increasing K, 32 at a time: the order of the 128-row tiled kernels, whose
+// results this kernel reproduces bit for bit.
 //
 // All loads go through buffer descriptors bounded to the source array, so an
 // offset outside it reads zeros instead of faulting (the host checks that the
@@ -65,16 +75,18 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // workgroup -> (expert e, its first grouped row beg and row count M, token
-// tile m0, weight tile nt). Tiles are listed expert by expert, n-tile by
-// n-tile, m-tile by m-tile; workgroup b runs on XCD b % 8 and takes logical
-// tile (b % 8) * per + b / 8, so the m-tiles sharing a weight tile run
-// together in one XCD's L2. Surplus workgroups of the worst-case grid return.
+// tile m0, weight tile nt, K split sp). Tiles are listed expert by expert,
+// split by split, n-tile by n-tile, m-tile by m-tile; workgroup b runs on XCD
+// b % 8 and takes logical tile (b % 8) * per + b / 8, so the m-tiles sharing a
+// weight tile run together in one XCD's L2. Surplus workgroups of the
+// worst-case grid return.
 __device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offsets, int E, int ntn,
-                                               int& e, int& beg, int& M, int& m0, int& nt) {
+                                               int nsplit, int& e, int& beg, int& M, int& m0,
+                                               int& nt, int& sp) {
   int total = 0;
   for (int i = 0; i < E; ++i) {
     const int Mi = offsets[i + 1] - offsets[i];
-    total += ((Mi + DT - 1) / DT) * ntn;
+    total += ((Mi + DT - 1) / DT) * ntn * nsplit;
   }
   const int per = (total + 7) / 8;
   const int q = blockIdx.x >> 3;
@@ -84,13 +96,15 @@ __device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offse
   for (int i = 0; i < E; ++i) {
     const int Mi = offsets[i + 1] - offsets[i];
     const int mt = (Mi + DT - 1) / DT;
-    const int cnt = mt * ntn;
+    const int cnt = mt * ntn * nsplit;
     if (L < cnt) {
       e = i;
       beg = offsets[i];
       M = Mi;
-      nt = L / mt;
       m0 = (L % mt) * DT;
+      const int r = L / mt;
+      nt = r % ntn;
+      sp = r / ntn;
       return true;
     }
     L -= cnt;
@@ -98,14 +112,21 @@ __device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offse
   return false;
 }
 
-// x [T, d] bf16, w1/w3 fragment order [E, ffn, d], h [A, ffn] bf16
-__global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
-    const uint16_t* __restrict__ x, int64_t T, const uint16_t* __restrict__ w1,
-    const uint16_t* __restrict__ w3, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_asg, int d, int ffn, int E, int ktop,
-    uint16_t* __restrict__ h, int ntn) {
-  int e, beg, M, m0, nt;
-  if (!decode_tile256(offsets, E, ntn, e, beg, M, m0, nt)) return;
+// GATE_UP: act = x [act_rows = T, K = d] bf16, wa/wb = w1/w3 in fragment
+// order [E, N = ffn, d], out = h [A, ffn] bf16, nsplit = 1.
+// !GATE_UP: act = h [act_rows = A, K = ffn] bf16 in grouped order, wa = w2 in
+// fragment order [E, N = d, ffn], out = part [nsplit][A][d] float32, the
+// partial arrays pstride floats apart.
+template <bool GATE_UP>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64_t act_rows,
+                                         const uint16_t* __restrict__ wa,
+                                         const uint16_t* __restrict__ wb,
+                                         const int32_t* __restrict__ offsets,
+                                         const int32_t* __restrict__ sorted_asg, int K, int N,
+                                         int E, int ktop, void* __restrict__ out, int ntn,
+                                         int nsplit, int64_t pstride) {
+  int e, beg, M, m0, nt, sp;
+  if (!decode_tile256(offsets, E, ntn, nsplit, e, beg, M, m0, nt, sp)) return;
 
   // one array per buffer: distinct objects let the compiler see that a
   // fragment read does not depend on the loads in flight to other buffers
@@ -132,19 +153,23 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wn = w & 3, wm = w >> 2;
   const int fr = lane & 15, fg = lane >> 4;
-  // LDS weight fragment f (of 16) is wave wn = f >> 2's tile f & 3: w1 rows
-  // for f & 3 < 2, else w3 rows, nt*128 + (f >> 2)*32 + (f & 1)*16. Wave w
-  // loads weight fragments 2w, 2w+1 (all w1 for even w, all w3 for odd w).
-  const size_t wslice = static_cast<size_t>(ffn) * d;  // elements of one expert matrix
+  const int Kc = GATE_UP ? K : K / nsplit;  // this tile's K range: [k0, k0 + Kc)
+  const int k0 = GATE_UP ? 0 : sp * Kc;
+  // LDS weight fragment f (of 16) is wave wn = f >> 2's tile f & 3. Gate/up:
+  // w1 rows for f & 3 < 2, else w3 rows, nt*128 + (f >> 2)*32 + (f & 1)*16;
+  // wave w loads fragments 2w, 2w+1 (all w1 for even w, all w3 for odd w).
+  // Down: w2 rows nt*256 + 16 f; wave w loads fragments 2w, 2w+1.
+  const size_t wslice = static_cast<size_t>(N) * K;  // elements of one expert matrix
+  const uint16_t* wsrc = (GATE_UP && (w & 1)) ? wb : wa;
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(((w & 1) ? w3 : w1) + e * wslice), 0, static_cast<int>(wslice * 2), kRsrcWord3);
+      const_cast<uint16_t*>(wsrc + e * wslice), 0, static_cast<int>(wslice * 2), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(x), 0, static_cast<int>(T * d * 2), kRsrcWord3);
+      const_cast<uint16_t*>(act), 0, static_cast<int>(act_rows * K * 2), kRsrcWord3);
   int aoff[2];  // byte offsets of step 0 (wave-uniform)
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int row = nt * 128 + (w >> 1) * 32 + q * 16;
-    aoff[q] = __builtin_amdgcn_readfirstlane(static_cast<int>(wofs<true>(0, row, 0, ffn, d) * 2));
+    const int row = GATE_UP ? nt * 128 + (w >> 1) * 32 + q * 16 : nt * 256 + (2 * w + q) * 16;
+    aoff[q] = __builtin_amdgcn_readfirstlane(static_cast<int>(wofs<true>(0, row, k0, N, K) * 2));
   }
   // token loads: wave w moves tile rows 32w .. 32w+31, 8 rows x 128 B per load; lane l puts row
   // 32w + 8q + l/8, LDS slot l%8, which holds 16-byte chunk (l%8) ^ ((row/2) % 8) of the K64 stage
@@ -154,10 +179,11 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
     const int r = 32 * w + 8 * q + (lane >> 3);
     const int mm = min(m0 + r, M - 1);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    toff[q] = ((sorted_asg[beg + mm] / ktop) * d + c * 8) * 2;
+    const int src = GATE_UP ? sorted_asg[beg + mm] / ktop : beg + mm;
+    toff[q] = (src * K + k0 + c * 8) * 2;
   }
   const int lane16 = lane * 16;
-  const int nsteps = d / 32;       // a multiple of 4
+  const int nsteps = Kc / 32;      // a multiple of 4
   const int last = nsteps - 1;
   const int last_stage = nsteps / 2 - 1;
   auto load_w = [&](uint16_t* L, int q, int t) {
@@ -262,23 +288,34 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
     };
     for (; t0 < nsteps; t0 += 4) unrolled(step, std::make_integer_sequence<int, 4>{});
     // epilogue: lane holds token column fr of each 16x16 tile and weight rows
-    // 4*fg .. 4*fg+3 of it; gate in tiles 0-1, up in tiles 2-3
+    // 4*fg .. 4*fg+3 of it; gate/up: gate in tiles 0-1, up in tiles 2-3. An
+    // empty asm with VGPR constraints (no instruction) fixes the accumulators'
+    // register class for the allocator.
 #pragma unroll
     for (int j = 0; j < JV; ++j) {
       const int m = m0 + wm * 128 + j * 16 + fr;
       if (m >= M) continue;
+      if constexpr (GATE_UP) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int n = nt * 128 + wn * 32 + i * 16 + 4 * fg;
-        f32x4 gt = acc[i][j];
-        f32x4 up = acc[i + 2][j];
-        // an empty asm with VGPR constraints (no instruction) fixes the
-        // accumulators' register class for the allocator
-        asm volatile("" : "+v"(gt), "+v"(up));
-        uint2 v;
-        v.x = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
-        v.y = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
-        *reinterpret_cast<uint2*>(h + static_cast<size_t>(beg + m) * ffn + n) = v;
+        for (int i = 0; i < 2; ++i) {
+          const int n = nt * 128 + wn * 32 + i * 16 + 4 * fg;
+          f32x4 gt = acc[i][j];
+          f32x4 up = acc[i + 2][j];
+          asm volatile("" : "+v"(gt), "+v"(up));
+          uint2 v;
+          v.x = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
+          v.y = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + static_cast<size_t>(beg + m) * N +
+                                    n) = v;
+        }
+      } else {
+        float* y = static_cast<float*>(out) + sp * pstride + static_cast<size_t>(beg + m) * N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 v = acc[i][j];
+          asm volatile("" : "+v"(v));
+          *reinterpret_cast<f32x4*>(y + nt * 256 + wn * 64 + i * 16 + 4 * fg) = v;
+        }
       }
     }
   };
@@ -290,7 +327,26 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
     default: run(std::integral_constant<int, 0>{}); break;
   }
 }
+
+// x [T, d] bf16, w1/w3 fragment order [E, ffn, d], h [A, ffn] bf16
+__global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
+    const uint16_t* __restrict__ x, int64_t T, const uint16_t* __restrict__ w1,
+    const uint16_t* __restrict__ w3, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_asg, int d, int ffn, int E, int ktop,
+    uint16_t* __restrict__ h, int ntn) {
+  dma_tile<true>(x, T, w1, w3, offsets, sorted_asg, d, ffn, E, ktop, h, ntn, 1, 0);
+}
+
+// h [A, ffn] bf16 grouped, w2 fragment order [E, d, ffn], part [nsplit, A, d] f32
+__global__ __launch_bounds__(kDmaThreads, 1) void down_dma_kernel(
+    const uint16_t* __restrict__ h, int64_t A, const uint16_t* __restrict__ w2,
+    const int32_t* __restrict__ offsets, int d, int ffn, int E, float* __restrict__ part, int ntn,
+    int nsplit) {
+  dma_tile<false>(h, A, w2, w2, offsets, nullptr, ffn, d, E, 1, part, ntn, nsplit, A * d);
+}
+
 constexpr int64_t kMax31 = (int64_t(1) << 31) - 1;
+constexpr int64_t kCUs = 256;  // compute units of an MI355X
 
 }  // namespace
 
@@ -312,6 +368,36 @@ hipError_t launch_gate_up_dma(const uint16_t* x, const uint16_t* w1, const uint1
   hipLaunchKernelGGL(gate_up_dma_kernel, dim3(static_cast<unsigned>((tiles + 7) / 8 * 8)),
                      dim3(kDmaThreads), 0, s, x, A / k, w1, w3, offsets, sorted_asg, d, ffn, E, k,
                      h, ntn);
+  return hipGetLastError();
+}
+
+bool dma_down_ok(int64_t A, int d, int ffn, int E) {
+  if (d % 256 != 0 || ffn % 128 != 0) return false;
+  if (A < static_cast<int64_t>(2 * DT) * E) return false;  // as for gate/up
+  return static_cast<int64_t>(ffn) * d * 2 <= kMax31 && A * ffn * 2 <= kMax31;
+}
+
+int dma_down_splits(int64_t A, int d, int ffn, int E) {
+  if (!dma_down_ok(A, d, ffn, E) || ffn % 256 != 0) return 1;
+  // One workgroup per CU (128 KiB of LDS). Splitting K in two halves each
+  // tile's time and doubles the tile count; it pays when that packs the tiles
+  // into noticeably fewer rounds over the CUs, e.g. 2.25 rounds of tiles
+  // taking 3 round times unsplit and 2.5 split. The tile count is estimated
+  // from A with half a part-filled tile per expert (the device holds the true
+  // counts), so the choice depends on the sizes only.
+  const int64_t tiles = ((A + DT - 1) / DT + E / 2) * (d / 256);
+  const int64_t r1 = (tiles + kCUs - 1) / kCUs;      // round times, unsplit
+  const int64_t r2 = (2 * tiles + kCUs - 1) / kCUs;  // half-round times, split
+  return 10 * r2 <= 9 * 2 * r1 ? 2 : 1;
+}
+
+hipError_t launch_down_dma(const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
+                           int64_t A, int d, int ffn, int E, int nsplit, float* part,
+                           hipStream_t s) {
+  const int ntn = d / 256;
+  const int64_t tiles = ((A + DT - 1) / DT + E) * ntn * nsplit;  // upper bound
+  hipLaunchKernelGGL(down_dma_kernel, dim3(static_cast<unsigned>((tiles + 7) / 8 * 8)),
+                     dim3(kDmaThreads), 0, s, h, A, w2, offsets, d, ffn, E, part, ntn, nsplit);
   return hipGetLastError();
 }
 

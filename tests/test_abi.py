@@ -42,9 +42,16 @@ def test_workspace_bytes():
     n32 = f(32, 4096, 14336, 8, 2, moe.MOE_F32)                 # h f32, one y
     assert n32 >= A * 14336 * 4 + A * 4096 * 4
     assert f(64, 4096, 14336, 8, 2, moe.MOE_BF16) > n
-    # large batches use the tiled kernels, which leave y as one array
+    # large batches use the tiled kernels: 4096 tokens of 8x7B fill 2.25
+    # rounds of 256x256 tiles over the GPU's 256 CUs, so the down projection
+    # splits K in two (2.5 rounds of half-length tiles) and leaves two partial
+    # arrays; 8192 tokens at d = 6144 fill 6.4 rounds and leave y as one array
     big = 4096 * 2
-    assert f(4096, 4096, 14336, 8, 2, moe.MOE_BF16) < big * 14336 * 2 + 2 * big * 4096 * 4 + 2 ** 20
+    assert f(4096, 4096, 14336, 8, 2, moe.MOE_BF16) >= big * 14336 * 2 + 2 * big * 4096 * 4
+    big = 8192 * 2
+    assert f(8192, 6144, 16384, 8, 2, moe.MOE_BF16) < big * 16384 * 2 + 2 * big * 6144 * 4
+    # the K split needs ffn % 256 == 0 and d % 256 == 0
+    assert f(4096, 4096, 14208, 8, 2, moe.MOE_BF16) < 8192 * 14208 * 2 + 2 * 8192 * 4096 * 4
     assert f(0, 128, 256, 8, 2, moe.MOE_F32) > 0                # counts/offsets still live
     for bad in [(-1, 128, 256, 8, 2, 0), (4, 128, 256, 8, 9, 0), (4, 128, 256, 33, 2, 0),
                 (4, 0, 256, 8, 2, 0), (4, 128, 256, 8, 0, 0), (4, 128, 256, 8, 2, 7),

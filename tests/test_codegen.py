@@ -1,7 +1,8 @@
 """CPU-only checks of the machine code hipcc makes for the prefill gate/up
-kernel (csrc/ffn_dma.hip), compiled with the exact flags the build uses.
+and down kernels (csrc/ffn_dma.hip), compiled with the exact flags the build
+uses.
 
-Its main loop is scheduled by hand; the properties its speed rests on are
+Their main loop is scheduled by hand; the properties its speed rests on are
 properties of the generated gfx950 code, so they are checked there: every
 MFMA accumulates in place (destination = accumulator input), no accumulator
 is copied between register files inside the loop, nothing spills to scratch,
@@ -49,8 +50,27 @@ def _loops(text):
     return found
 
 
-def test_gate_up_loops_keep_accumulators_in_place(asm):
-    loops = _loops(asm)
+def _kernels(text):
+    """{kernel symbol: its code} for every kernel in the file."""
+    starts = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\w+):", text, re.M)]
+    out = {}
+    for i, (pos, name) in enumerate(starts):
+        end = starts[i + 1][0] if i + 1 < len(starts) else len(text)
+        out[name] = text[pos:end]
+    return out
+
+
+def test_both_kernels_are_present(asm):
+    names = list(_kernels(asm))
+    assert any("gate_up_dma_kernel" in n for n in names), names
+    assert any("down_dma_kernel" in n for n in names), names
+
+
+@pytest.mark.parametrize("kernel", ["gate_up_dma_kernel", "down_dma_kernel"])
+def test_loops_keep_accumulators_in_place(asm, kernel):
+    code = [c for n, c in _kernels(asm).items() if kernel in n]
+    assert len(code) == 1
+    loops = _loops(code[0])
     # one loop per token-fragment count the kernel is instantiated for (8, 6, 4, 2)
     assert len(loops) == 4
     for body in loops:
@@ -66,7 +86,7 @@ def test_gate_up_loops_keep_accumulators_in_place(asm):
         assert sum("buffer_load_dwordx4" in b and " lds" in b for b in body) == 16
 
 
-def test_gate_up_kernel_has_no_scratch_and_two_waves_per_simd(asm):
+def test_kernels_have_no_scratch_and_two_waves_per_simd(asm):
     sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)
     assert sizes and all(int(s) == 0 for s in sizes)
     # the 8-wave workgroup needs two waves per SIMD: at most 256 registers per lane each

@@ -203,15 +203,18 @@ def test_exact_logit_ties_pick_lower_index(m):
     assert (w == 0.5).all()
 
 
-@pytest.mark.parametrize("d,ffn", [(128, 256), (256, 128)])
-def test_prefill_gate_up_tail_tiles(m, d, ffn):
-    """The 256x256-tile gate/up kernel (fragment-order weights, tiled family,
-    used once A >= 512 E) on hand-made routing whose per-expert row counts
-    leave last tiles holding 16, 48, 80, 128, 130 and 250 rows (every
-    token-fragment count the kernel specialises: 2, 4, 6, 8 and 0 for the idle
-    half), an empty expert and an exact multiple of 256; one (d = 128) and two
-    (d = 256) unrolled trips of its K loop. Oracle within the bf16 bar, and
-    bit-identical to the standard-layout kernel (same MFMA sequence)."""
+@pytest.mark.parametrize("d,ffn", [(128, 256), (256, 128), (256, 256), (256, 512)])
+def test_prefill_tail_tiles(m, d, ffn):
+    """The 256x256-tile kernels (fragment-order weights, tiled family, used
+    once A >= 512 E: gate/up always, down when d % 256 == 0) on hand-made
+    routing whose per-expert row counts leave last tiles holding 16, 48, 80,
+    128, 130 and 250 rows (every token-fragment count the kernels specialise:
+    2, 4, 6, 8 and 0 for the idle half), an empty expert and an exact multiple
+    of 256; one or two unrolled trips of the K loops. With ffn % 256 == 0 and
+    these few tiles the down projection splits K in two (the workspace holds
+    the two partial arrays), otherwise it does not. Oracle within the bf16
+    bar, and bit-identical to the standard-layout kernels (same MFMA
+    sequence, same split)."""
     counts = [784, 816, 848, 896, 898, 0, 1024, 1018]
     E, k = len(counts), 2
     A = sum(counts)
@@ -219,7 +222,10 @@ def test_prefill_gate_up_tail_tiles(m, d, ffn):
     inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=45 + d)
     sasg = np.random.default_rng(46).permutation(A).astype(np.int32)
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    print(f"[parity] prefill gate/up tails d={d} ffn={ffn} A={A}", flush=True)
+    split = ffn % 256 == 0 and d % 256 == 0
+    ws = m.moe_workspace_bytes(A // k, d, ffn, E, k, torch.bfloat16)
+    assert (ws >= A * ffn * 2 + 2 * A * d * 4) == split
+    print(f"[parity] prefill tails d={d} ffn={ffn} A={A} split={split}", flush=True)
     dev = to_device(inp)
     o_t = torch.from_numpy(offs).cuda()
     s_t = torch.from_numpy(sasg).cuda()
