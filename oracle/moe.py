@@ -247,6 +247,37 @@ def forward(x, router, w1, w3, w2, k: int, bias=None):
 
 
 # --------------------------------------------------------------------------
+# the MLP half of the decoder block: pre-norm and residual around the layer
+# --------------------------------------------------------------------------
+def rms_norm(h, gamma, eps: float = 1e-5) -> np.ndarray:
+    """n[t, i] = gamma[i] * h[t, i] / sqrt(mean_i h[t, i]^2 + eps).
+
+    The MLP is called on post_attention_layernorm(h), a MixtralRMSNorm over
+    hidden_size (nnterp Mixtral page, "The Notes", the block in order, and the
+    module printout); eps is rms_norm_eps, 1e-5 (Transformers Mixtral page,
+    MixtralConfig). The pages print no formula; this is root-mean-square
+    normalisation over the hidden axis, scaled per channel by the norm's weight.
+    """
+    hd = widen(h)
+    g = widen(gamma)
+    ms = np.mean(hd * hd, axis=1, keepdims=True)
+    return g[None, :] * (hd / np.sqrt(ms + eps))
+
+
+def block_forward(h, gamma, router, w1, w3, w2, k: int, bias=None, eps: float = 1e-5):
+    """out = h + layer(rms_norm(h)) (nnterp page, Notes: out = h +
+    mlp(post_attention_layernorm(h)), and nothing norms the sublayer's output).
+    Returns forward()'s dict for the normed rows, with ``norm`` = the normed
+    rows, ``mlp`` = the layer's output and ``out`` = the block's."""
+    n = rms_norm(h, gamma, eps)
+    f = forward(n, router, w1, w3, w2, k, bias)
+    f["norm"] = n
+    f["mlp"] = f["out"]
+    f["out"] = widen(h) + f["mlp"]
+    return f
+
+
+# --------------------------------------------------------------------------
 # second, independent formulations
 # --------------------------------------------------------------------------
 def gate_matrix(idx, w, E: int) -> np.ndarray:

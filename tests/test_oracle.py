@@ -323,3 +323,57 @@ def test_skew_bias_concentrates_routing():
     # at most one slot per token can be expert 0, so its share is at most 1/k
     assert 0.45 < frac0 <= 0.5
     assert counts[0] > counts[1] > counts[2] and counts[7] == counts.min()
+
+
+# ------------------------------------------------- pre-norm and residual --
+def test_rms_norm_worked_example():
+    # row 0: mean square (9 + 16) / 2 = 25/2, rms 5/sqrt(2): [3, 4] -> [3, 4] * sqrt(2)/5,
+    #        times gamma [1, 2] -> [3 sqrt(2)/5, 8 sqrt(2)/5]
+    # row 1: mean square 1/4, rms 1/2: [1/2, -1/2] -> [1, -1], times gamma -> [1, -2]
+    h = np.array([[3.0, 4.0], [0.5, -0.5]])
+    g = np.array([1.0, 2.0])
+    got = oracle.rms_norm(h, g, eps=0.0)
+    r2 = math.sqrt(2.0)
+    want = np.array([[3 * r2 / 5, 8 * r2 / 5], [1.0, -2.0]])
+    assert np.allclose(got, want, rtol=1e-15, atol=0)
+    # eps sits under the square root: a row of ones becomes 1 / sqrt(1 + eps)
+    got = oracle.rms_norm(np.ones((1, 4)), np.ones(4), eps=1e-5)
+    assert np.allclose(got, 1.0 / math.sqrt(1.0 + 1e-5), rtol=1e-15, atol=0)
+
+
+def test_rms_norm_matches_library_routine():
+    rng = np.random.default_rng(5)
+    h = rng.standard_normal((7, 96)) * rng.uniform(0.1, 10.0, size=(7, 1))
+    g = rng.standard_normal(96)
+    ref = F.rms_norm(torch.from_numpy(h), (96,), torch.from_numpy(g), eps=1e-5).numpy()
+    assert np.allclose(oracle.rms_norm(h, g, 1e-5), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_rms_norm_invariants():
+    rng = np.random.default_rng(6)
+    h = rng.standard_normal((5, 64))
+    ones = np.ones(64)
+    base = oracle.rms_norm(h, ones, eps=0.0)
+    assert np.allclose(oracle.rms_norm(7.25 * h, ones, eps=0.0), base, rtol=1e-14, atol=0)
+    assert np.array_equal(oracle.rms_norm(-h, ones, eps=0.0), -base)
+    assert np.allclose(np.mean(base ** 2, axis=1), 1.0, rtol=1e-14, atol=0)
+
+
+def test_block_is_residual_plus_layer_on_normed_rows(tiny):
+    rng = np.random.default_rng(8)
+    gamma = rng.uniform(0.5, 1.5, tiny["d"])
+    b = oracle.block_forward(tiny["x"], gamma, tiny["router"], tiny["w1"], tiny["w3"], tiny["w2"],
+                             tiny["k"], tiny["bias"])
+    assert np.allclose(b["norm"], oracle.rms_norm(tiny["x"], gamma), rtol=1e-15, atol=0)
+    # experts with a zero down projection add nothing: the block returns its input
+    z = oracle.block_forward(tiny["x"], gamma, tiny["router"], tiny["w1"], tiny["w3"],
+                             np.zeros_like(tiny["w2"]), tiny["k"], tiny["bias"])
+    assert np.array_equal(z["out"], oracle.widen(tiny["x"]))
+    # routing is decided on the normed rows: a per-token rescale of h changes nothing
+    scaled = oracle.widen(tiny["x"]) * rng.uniform(0.5, 4.0, size=(tiny["T"], 1))
+    s = oracle.block_forward(scaled, gamma, tiny["router"], tiny["w1"], tiny["w3"], tiny["w2"],
+                             tiny["k"], tiny["bias"], eps=0.0)
+    b0 = oracle.block_forward(tiny["x"], gamma, tiny["router"], tiny["w1"], tiny["w3"],
+                              tiny["w2"], tiny["k"], tiny["bias"], eps=0.0)
+    assert np.array_equal(s["idx"], b0["idx"])
+    assert np.allclose(s["mlp"], b0["mlp"], rtol=1e-9, atol=1e-12)
