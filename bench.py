@@ -15,6 +15,9 @@ By default the expert weights are held in fragment order (moe_pack_weight,
 run once when the weights are loaded, outside the timed region); the rate
 with the standard [E, ffn, d] layout is measured too and reported beside it.
 
+--block times moe_block_forward instead: the RMS norm in front of the layer
+and the residual add after it (the MLP half of the decoder block).
+
 Prints one JSON line: tokens/s for the whole job, the dominant kernel's
 roofline position and the CPU oracle's throughput on a bounded sample.
 """
@@ -60,6 +63,10 @@ def parse():
                    help="expert weight layout of the timed steps")
     p.add_argument("--no-compare", action="store_true",
                    help="do not also time the other weight layout")
+    p.add_argument("--block", action="store_true",
+                   help="time the MLP half of the decoder block instead of the bare layer: "
+                        "RMS norm in front (eps 1e-5) and the residual add after "
+                        "(moe_block_forward)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first copy a buffer of this many MiB once (a known-size kernel that "
                         "calibrates hardware byte counters under a profiler)")
@@ -104,14 +111,19 @@ def upload(inp, torch):
     return {k: up(inp[k]) for k in ("x", "router", "w1", "w3", "w2", "bias")}
 
 
-def algorithmic_work(cfg, counts):
-    """Bytes and flops the layer must move/do (intermediates h and y excluded)."""
+def algorithmic_work(cfg, counts, block=False):
+    """Bytes and flops the layer must move/do (intermediates h and y excluded).
+    block: the norm weight is read and the normed rows are written (an output
+    of moe_block_forward), the norm and the residual add are ~4*T*d flops."""
     T, d, F, E, k = cfg["T"], cfg["d"], cfg["ffn"], cfg["E"], cfg["k"]
     wb = 2 if cfg["dtype"] == "bf16" else 4
     A = T * k
     active = sum(1 for c in counts if c > 0)
     layer_bytes = active * 3 * d * F * wb + T * d * wb + T * d * wb + E * d * 4
     layer_flops = 2 * A * 3 * d * F + 2 * T * E * d
+    if block:
+        layer_bytes += d * 4 + T * d * wb
+        layer_flops += 4 * T * d
     gate_up_bytes = active * 2 * d * F * wb + T * d * wb + A * F * wb
     gate_up_flops = 2 * A * 2 * d * F
     return layer_bytes, layer_flops, gate_up_bytes, gate_up_flops
@@ -186,10 +198,11 @@ def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
     print(json.dumps(rec["workloads"][workload]))
 
 
-def cpu_baseline(cfg, inp, budget_s=10.0):
+def cpu_baseline(cfg, inp, budget_s=10.0, gamma=None):
     """The float64 oracle on a bounded sample of the same workload: consecutive
     slices of n tokens of the batch (wrapping around), full routing and all their
-    experts, until budget_s of CPU time has been spent."""
+    experts, until budget_s of CPU time has been spent. With gamma, the block
+    (norm, layer, residual) instead of the bare layer."""
     import numpy as np
     import threadpoolctl
 
@@ -201,8 +214,12 @@ def cpu_baseline(cfg, inp, budget_s=10.0):
     while True:
         lo = (passes * n) % T
         hi = min(lo + n, T)
-        oracle.forward(inp["x"][lo:hi], inp["router"], inp["w1"], inp["w3"], inp["w2"],
-                       cfg["k"], inp["bias"])
+        if gamma is None:
+            oracle.forward(inp["x"][lo:hi], inp["router"], inp["w1"], inp["w3"], inp["w2"],
+                           cfg["k"], inp["bias"])
+        else:
+            oracle.block_forward(inp["x"][lo:hi], gamma, inp["router"], inp["w1"], inp["w3"],
+                                 inp["w2"], cfg["k"], inp["bias"])
         done += hi - lo
         passes += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -263,14 +280,23 @@ def main():
     out = torch.empty(T, d, dtype=wdt, device="cuda")
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     hip = Hip()
+    gamma = gen.make_norm_weight(d, cfg["seed"]) if args.block else None
+    if args.block:
+        g_dev = torch.from_numpy(gamma).cuda()
+        norm_out = torch.empty(T, d, dtype=wdt, device="cuda")
 
     def step(i, use_sets, is_packed, events=None):
         s = use_sets[i % 2]
         if events is not None:
             moe.moe_set_stage_events(events)
-        moe.moe_forward(s["x"], s["router"], s["w1"], s["w3"], s["w2"], k,
-                        logit_bias=s["bias"], out=out, ws=ws, counts_out=counts,
-                        packed=is_packed)
+        if args.block:
+            moe.moe_block_forward(s["x"], g_dev, s["router"], s["w1"], s["w3"], s["w2"], k,
+                                  eps=1e-5, logit_bias=s["bias"], out=out, norm_out=norm_out,
+                                  ws=ws, counts_out=counts, packed=is_packed)
+        else:
+            moe.moe_forward(s["x"], s["router"], s["w1"], s["w3"], s["w2"], k,
+                            logit_bias=s["bias"], out=out, ws=ws, counts_out=counts,
+                            packed=is_packed)
 
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device="cuda")
@@ -310,7 +336,7 @@ def main():
                  "ms_per_step": round(ms_std, 4)}
 
     cnt = counts.cpu().tolist()
-    layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt)
+    layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt, args.block)
     ms_step = wall * 1e3 / args.steps
     tok_s = T / (ms_step / 1e3)
     decode_like = (T * k) <= 32 * E  # the streaming kernels' regime: weight-bandwidth bound
@@ -334,8 +360,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg["dtype"], "data": "synthetic",
-        "config": {"workload": args.workload, "T": T, "d": d, "ffn": F, "E": E, "k": k,
-                   "seed": cfg["seed"], "logit_bias": cfg["bias"]},
+        "config": {"workload": args.workload + ("+block" if args.block else ""), "T": T, "d": d,
+                   "ffn": F, "E": E, "k": k, "seed": cfg["seed"], "logit_bias": cfg["bias"]},
         "roofline": roof,
         "layer": {"tflops": round(layer_tflops, 2),
                   "tflops_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
@@ -350,7 +376,7 @@ def main():
         rec["other_layout"] = other
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg, inp)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, gamma=gamma)
     print(json.dumps(rec), flush=True)
 
 

@@ -129,6 +129,17 @@ def make_inputs(T: int, d: int, ffn: int, E: int = 8, k: int = 2, dtype: str = B
                 T=T, d=d, ffn=ffn, E=E, k=k, dtype=dtype, seed=seed)
 
 
+def make_norm_weight(d: int, seed: int = 0) -> np.ndarray:
+    """Weight [d] float32 of the RMS norm in front of the layer: 1 + 0.1 * N(0, 1)
+    (no trained norm weights exist here; a norm's weight starts at one). Drawn
+    from its own stream, SeedSequence([seed, 1]), so the layer's inputs for
+    the same seed do not change."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1])))
+    a = np.empty(d, dtype=np.float32)
+    g.standard_normal(dtype=np.float32, out=a)
+    return np.float32(1.0) + np.float32(0.1) * a
+
+
 def make_config(name: str, seed: int | None = None, T: int | None = None) -> dict:
     """Inputs of a named workload; ``seed``/``T`` override the defaults."""
     cfg = dict(CONFIGS[name])

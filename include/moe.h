@@ -144,6 +144,28 @@ int moe_forward(const void* x, int dtype, const float* router, const float* logi
                 float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* The MLP half of the decoder block around the layer (nnterp Mixtral page,
+ * "The Notes", the block in order: out = h + mlp(post_attention_layernorm(h));
+ * the norm is a MixtralRMSNorm over hidden_size with eps = rms_norm_eps,
+ * 1e-5 in MixtralConfig):
+ *   r_t         = 1 / sqrt(sum_i hidden[t,i]^2 / d + eps)          (float32)
+ *   norm_out[t] = round((hidden[t,i] * r_t) * norm_weight[i])      (hidden's type)
+ *   out[t]      = hidden[t] + moe_forward(norm_out)[t]              (float32, then out_dtype)
+ * The router and the experts both read the stored norm_out, exactly as
+ * moe_forward would read it as x (same kernels, same results bit for bit),
+ * and the residual is added to the finished slot sum. hidden [T, d] and
+ * norm_out [T, d] have the element type of dtype (float32 for MOE_F32,
+ * bfloat16 for MOE_BF16 / MOE_BF16_PACKED); norm_weight [d] is float32;
+ * eps must be finite and >= 0 (a zero row with eps = 0 gives NaN). norm_out
+ * and out must not overlap hidden or each other (MOE_EINVAL). Every other
+ * argument, alignment rule and the workspace are as for moe_forward. */
+int moe_block_forward(const void* hidden, int dtype, const float* norm_weight, float eps,
+                      void* norm_out, const float* router, const float* logit_bias,
+                      const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
+                      int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
+                      float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* One-time weight preparation for the MOE_BF16_PACKED path: copies the
  * bfloat16 matrices w [E, rows, cols] (standard layout, cols contiguous) into
  * `out` (same size, E*rows*cols*2 bytes, must not overlap w) in fragment
@@ -164,7 +186,7 @@ int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* o
  * kernels (many rows per expert). Returns MOE_EINVAL for other values. */
 int moe_set_ffn_variant(int variant);
 
-/* Profiling: when n == 6, moe_forward records events[0] before the router,
+/* Profiling: when n == 6, moe_forward (and moe_block_forward) records events[0] before the router,
  * events[1] after it, then events[2..5] after the permutation, the gate/up
  * kernel, the down kernel and the combine, on its stream. Each events[i] is
  * a hipEvent_t the caller created. n == 0 (events may be NULL) turns it off.

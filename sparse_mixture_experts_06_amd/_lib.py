@@ -38,6 +38,9 @@ _SIGNATURES = {
     "moe_combine": (_c_int, [_vp, _vp, _vp, _c_i64, _c_int, _c_int, _vp, _c_int, _vp]),
     "moe_forward": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _c_int,
                              _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _c_sz, _vp]),
+    "moe_block_forward": (_c_int, [_vp, _c_int, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _vp, _c_int,
+                                   _vp, _vp, _vp, _vp, _c_sz, _vp]),
     "moe_pack_weight": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_set_ffn_variant": (_c_int, [_c_int]),
     "moe_set_stage_events": (_c_int, [_vp, _c_int]),
@@ -287,3 +290,41 @@ def moe_forward(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dt
                             _ptr(counts_out), _ptr(ws), ws.numel(), _stream(dev))
     _check("moe_forward", st)
     return out
+
+
+def moe_block_forward(hidden, norm_weight, router, w1, w3, w2, k: int, eps: float = 1e-5,
+                      logit_bias=None, out=None, out_dtype=None, norm_out=None, ws=None,
+                      topk_idx_out=None, topk_w_out=None, counts_out=None, packed=False):
+    """out = hidden + layer(RMSNorm(hidden)); returns (out, norm_out).
+    norm_weight [d] float32; norm_out [T, d] has hidden's dtype."""
+    T, d = hidden.shape
+    E, ffn, _ = w1.shape
+    dev = hidden.device
+    _need(norm_weight, "norm_weight", torch.float32, (d,), dev)
+    _need(router, "router", torch.float32, (E, d), dev)
+    for name, t, shp in (("w1", w1, (E, ffn, d)), ("w3", w3, (E, ffn, d)), ("w2", w2, (E, d, ffn))):
+        _need(t, name, hidden.dtype, shp, dev)
+    if logit_bias is not None:
+        _need(logit_bias, "logit_bias", torch.float32, (E,), dev)
+    if norm_out is None:
+        norm_out = torch.empty(T, d, dtype=hidden.dtype, device=dev)
+    _need(norm_out, "norm_out", hidden.dtype, (T, d), dev)
+    if out is None:
+        out = torch.empty(T, d, dtype=out_dtype or hidden.dtype, device=dev)
+    _need(out, "out", out.dtype, (T, d), dev)
+    if topk_idx_out is not None:
+        _need(topk_idx_out, "topk_idx_out", torch.int32, (T, k), dev)
+    if topk_w_out is not None:
+        _need(topk_w_out, "topk_w_out", torch.float32, (T, k), dev)
+    if counts_out is not None:
+        _need(counts_out, "counts_out", torch.int32, (E,), dev)
+    code = _weight_code(hidden.dtype, packed)
+    if ws is None:
+        ws = workspace(T, d, ffn, E, k, code, dev)
+    st = load().moe_block_forward(_ptr(hidden), code, _ptr(norm_weight), float(eps),
+                                  _ptr(norm_out), _ptr(router), _ptr(logit_bias), _ptr(w1),
+                                  _ptr(w3), _ptr(w2), T, d, ffn, E, k, _ptr(out),
+                                  _dtype_code(out.dtype), _ptr(topk_idx_out), _ptr(topk_w_out),
+                                  _ptr(counts_out), _ptr(ws), ws.numel(), _stream(dev))
+    _check("moe_block_forward", st)
+    return out, norm_out

@@ -203,11 +203,17 @@ int moe_combine(const float* y, const int32_t* asg_pos, const float* topk_w, int
                                         out_dtype == MOE_BF16, static_cast<hipStream_t>(stream)));
 }
 
-int moe_forward(const void* x, int dtype, const float* router, const float* logit_bias,
-                const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
-                int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
-                float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                void* stream) {
+}  // extern "C"
+
+namespace {
+
+// the fused path; with gamma non-null the router and experts read the RMS-normed
+// rows (written to norm_out) and the combine adds x back (the block's MLP half)
+int forward_impl(const void* x, int dtype, const float* gamma, float eps, void* norm_out,
+                 const float* router, const float* logit_bias, const void* w1, const void* w3,
+                 const void* w2, int64_t T, int d, int ffn, int E, int k, void* out,
+                 int out_dtype, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                 void* ws, size_t ws_bytes, void* stream) {
   int st = check_sizes(T, E, k);
   if (st != MOE_OK) return st;
   st = check_ffn_shape(T, d, ffn, E, k, dtype);
@@ -217,7 +223,8 @@ int moe_forward(const void* x, int dtype, const float* router, const float* logi
   const Layout L = layout(T, d, ffn, E, k, dtype);
   if (!ws || ws_bytes < L.total) return MOE_EWORKSPACE;
   if (is_bf16(dtype) && T > 0 &&
-      !(aligned16(x) && aligned16(w1) && aligned16(w3) && aligned16(w2) && aligned16(ws)))
+      !(aligned16(x) && aligned16(w1) && aligned16(w3) && aligned16(w2) && aligned16(ws) &&
+        (!norm_out || aligned16(norm_out))))
     return MOE_ENOTSUP;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -230,10 +237,11 @@ int moe_forward(const void* x, int dtype, const float* router, const float* logi
   int32_t* asg_pos = reinterpret_cast<int32_t*>(base + L.pos);
   void* h = base + L.h;
   float* y = reinterpret_cast<float*>(base + L.y);
+  const void* xin = gamma ? norm_out : x;  // what the experts read
 
   stage(0, s);
   if (T > 0 && moe::launch_route(x, is_bf16(dtype), router, logit_bias, T, d, E, k, nullptr,
-                                 idx, w, s) != hipSuccess)
+                                 idx, w, s, gamma, eps, norm_out) != hipSuccess)
     return MOE_EHIP;
   stage(1, s);
   if (moe::launch_permute(idx, T * k, E, counts, offsets, sorted_asg, asg_pos, s) != hipSuccess)
@@ -244,14 +252,58 @@ int moe_forward(const void* x, int dtype, const float* router, const float* logi
     return MOE_OK;
   }
   int nsplit = 1;
-  st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, h, s, true, &nsplit);
+  st = run_ffn(xin, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, h, s, true,
+               &nsplit);
   if (st != MOE_OK) return st;
   stage(4, s);
-  if (moe::launch_combine(y, nsplit, asg_pos, w, T, d, k, out, out_dtype == MOE_BF16, s) !=
-      hipSuccess)
+  if (moe::launch_combine(y, nsplit, asg_pos, w, T, d, k, out, out_dtype == MOE_BF16, s,
+                          gamma ? x : nullptr, is_bf16(dtype)) != hipSuccess)
     return MOE_EHIP;
   stage(5, s);
   return MOE_OK;
+}
+
+inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const char* p = static_cast<const char*>(a);
+  const char* q = static_cast<const char*>(b);
+  return p < q + nb && q < p + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const void* x, int dtype, const float* router, const float* logit_bias,
+                const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
+                int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
+                float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                void* stream) {
+  return forward_impl(x, dtype, nullptr, 0.0f, nullptr, router, logit_bias, w1, w3, w2, T, d,
+                      ffn, E, k, out, out_dtype, topk_idx_out, topk_w_out, counts_out, ws,
+                      ws_bytes, stream);
+}
+
+int moe_block_forward(const void* hidden, int dtype, const float* norm_weight, float eps,
+                      void* norm_out, const float* router, const float* logit_bias,
+                      const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
+                      int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
+                      float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return MOE_EINVAL;  // rejects NaN and infinity too
+  if (T > 0) {
+    if (!norm_weight || !norm_out || !hidden || !out) return MOE_EINVAL;
+    if (!valid_weight_dtype(dtype) || !valid_dtype(out_dtype) || d < 1) return MOE_EINVAL;
+    if (T > kMaxAssignments) return MOE_EINVAL;
+    const size_t xb = is_bf16(dtype) ? 2 : 4;
+    const size_t ob = out_dtype == MOE_BF16 ? 2 : 4;
+    const size_t n = static_cast<size_t>(T) * static_cast<size_t>(d);
+    if (overlap(norm_out, n * xb, hidden, n * xb) || overlap(out, n * ob, hidden, n * xb) ||
+        overlap(out, n * ob, norm_out, n * xb))
+      return MOE_EINVAL;
+  }
+  return forward_impl(hidden, dtype, norm_weight, eps, norm_out, router, logit_bias, w1, w3, w2,
+                      T, d, ffn, E, k, out, out_dtype, topk_idx_out, topk_w_out, counts_out, ws,
+                      ws_bytes, stream);
 }
 
 int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* out,

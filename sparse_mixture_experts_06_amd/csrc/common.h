@@ -85,9 +85,12 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------------------
 // internal launchers (host side); each returns hipSuccess or the launch error
 // ---------------------------------------------------------------------------
+// with gamma non-null the router reads the RMS-normed rows (eps) and stores
+// them, in x's type, to norm_out
 hipError_t launch_route(const void* x, int x_bf16, const float* router, const float* bias,
                         int64_t T, int d, int E, int k, float* logits_out, int32_t* idx,
-                        float* w, hipStream_t s);
+                        float* w, hipStream_t s, const float* gamma = nullptr, float eps = 0.0f,
+                        void* norm_out = nullptr);
 
 hipError_t launch_permute(const int32_t* idx, int64_t A, int E, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_asg, int32_t* asg_pos,
@@ -130,10 +133,13 @@ hipError_t launch_gate_up_f32(const float* x, const float* w1, const float* w3,
 hipError_t launch_down_f32(const float* h, const float* w2, const int32_t* offsets, int64_t A,
                            int d, int ffn, int E, float* y, hipStream_t s);
 
-// out[t] = sum_j w[t*k+j] * y[asg_pos[t*k+j]], with y the split-order sum of
-// nsplit partial arrays of A x d floats (A = T*k) starting at `part`
+// out[t] = sum_j w[t*k+j] * y[asg_pos[t*k+j]] (+ residual[t] when residual is
+// non-null, added after the slot sum; bf16 or float32 per res_bf16), with y
+// the split-order sum of nsplit partial arrays of A x d floats (A = T*k)
+// starting at `part`
 hipError_t launch_combine(const float* part, int nsplit, const int32_t* asg_pos, const float* w,
-                          int64_t T, int d, int k, void* out, int out_bf16, hipStream_t s);
+                          int64_t T, int d, int k, void* out, int out_bf16, hipStream_t s,
+                          const void* residual = nullptr, int res_bf16 = 0);
 // y[i] = sum_s part[s*n + i] in split order
 hipError_t launch_sum_partials(const float* part, int nsplit, int64_t n, float* y, hipStream_t s);
 

@@ -4,6 +4,14 @@
 // the router renormalizes its top 2 in float32; support(): router_logits is
 // the router's linear output, before the scoring).
 //
+// With a norm (NORM), the router and the experts read the normed stream
+// instead of x (nnterp Mixtral page, "The Notes": the block calls the MLP on
+// post_attention_layernorm(h), a MixtralRMSNorm with eps = rms_norm_eps,
+// MixtralConfig): a first pass over the token rows sums their squares, and
+// the second pass forms n[t,i] = (x[t,i] * r_t) * gamma[i] in float32 with
+// r_t = 1 / sqrt(sum_i x[t,i]^2 / d + eps), rounds it once to the input's
+// type, stores it to norm_out and feeds that stored value to the logits.
+//
 // Work split (latency first: a decode batch has only a few dozen tokens): a
 // workgroup of 256 threads takes kVals / EM tokens and splits the hidden
 // dimension across all its threads in 8-element chunks (16-byte loads), so
@@ -73,16 +81,41 @@ __device__ __forceinline__ float wave_reduce_scatter64(float (&v)[kVals], int la
   return v[0];
 }
 
+// normed value of x (float32) at hidden index i, rounded to the stored type
+template <bool BF16>
+__device__ __forceinline__ float norm1(float x, float r, float g) {
+  const float v = (x * r) * g;
+  if constexpr (BF16) return bf16_to_f32(f32_to_bf16(v));
+  return v;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store8(void* out, int64_t row, int d, int i, const float* v) {
+  if constexpr (BF16) {
+    u32x4 q;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) q[h] = pack_bf16x2(v[2 * h], v[2 * h + 1]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + row * d + i) = q;
+  } else {
+    float* p = static_cast<float*>(out) + row * d + i;
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
 // EM: compile-time bound on E (8 or 32); TB = kVals / EM tokens per block.
-// VEC: x and router rows are 16-byte aligned and d % 8 == 0.
-template <bool BF16, int EM, bool VEC>
+// VEC: x, router, gamma and norm_out rows are 16-byte aligned and d % 8 == 0.
+// NORM: route the RMS-normed rows (gamma [d] float32, eps) and store them.
+template <bool BF16, int EM, bool VEC, bool NORM>
 __global__ __launch_bounds__(kThreads, 1) void route_kernel(
     const void* __restrict__ x, const float* __restrict__ router, const float* __restrict__ bias,
     int64_t T, int d, int E, int k, float* __restrict__ logits_out, int32_t* __restrict__ idx,
-    float* __restrict__ wout) {
+    float* __restrict__ wout, const float* __restrict__ gamma, float eps,
+    void* __restrict__ norm_out) {
   constexpr int TB = kVals / EM;
   __shared__ float s_part[kWavesPerBlock][kVals];
   __shared__ float s_logit[kVals];
+  __shared__ float s_ss[kWavesPerBlock][TB];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -107,6 +140,52 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(
 #pragma unroll
   for (int e = 0; e < EM; ++e) rrow[e] = router + static_cast<int64_t>(e < E ? e : E - 1) * d;
 
+  // per-token factor r_t of the norm (first pass: sums of squares, reduced
+  // over the wave by a butterfly and over the waves in LDS in a fixed order)
+  float rs[TB];
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt) rs[tt] = 1.0f;
+  if constexpr (NORM) {
+    float ss[TB];
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) ss[tt] = 0.0f;
+    int i0 = 0;
+    if constexpr (VEC) {
+      for (int c = tid; c < d / 8; c += kThreads) {
+        float xv[TB][8];
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt) load8<BF16>(x, rows[tt], d, c * 8, xv[tt]);
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+          for (int v = 0; v < 8; ++v) ss[tt] = fmaf(xv[tt][v], xv[tt][v], ss[tt]);
+      }
+      i0 = d / 8 * 8;
+    }
+    for (int i = i0 + tid; i < d; i += kThreads) {
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        const float xs = load1<BF16>(x, rows[tt], d, i);
+        ss[tt] = fmaf(xs, xs, ss[tt]);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      float v = ss[tt];
+#pragma unroll
+      for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+      if (lane == 0) s_ss[wave][tt] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      float v = s_ss[0][tt];
+#pragma unroll
+      for (int w = 1; w < kWavesPerBlock; ++w) v += s_ss[w][tt];
+      rs[tt] = 1.0f / sqrtf(v / static_cast<float>(d) + eps);
+    }
+  }
+
   int tail_start = 0;
   if constexpr (VEC) {
     const int nvec = d / 8;
@@ -115,6 +194,13 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(
       float xv[TB][8];
 #pragma unroll
       for (int tt = 0; tt < TB; ++tt) load8<BF16>(x, rows[tt], d, i, xv[tt]);
+      float g8[8];
+      if constexpr (NORM) {
+        const float4 ga = *reinterpret_cast<const float4*>(gamma + i);
+        const float4 gb = *reinterpret_cast<const float4*>(gamma + i + 4);
+        g8[0] = ga.x; g8[1] = ga.y; g8[2] = ga.z; g8[3] = ga.w;
+        g8[4] = gb.x; g8[5] = gb.y; g8[6] = gb.z; g8[7] = gb.w;
+      }
       float4 ra[EM], rb[EM];
 #pragma unroll
       for (int e = 0; e < EM; ++e) {
@@ -123,6 +209,14 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(
       }
       // keep every load of the chunk ahead of the arithmetic (one round trip)
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NORM) {
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt) {
+#pragma unroll
+          for (int v = 0; v < 8; ++v) xv[tt][v] = norm1<BF16>(xv[tt][v], rs[tt], g8[v]);
+          if (live[tt]) store8<BF16>(norm_out, rows[tt], d, i, xv[tt]);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < EM; ++e) {
         const float r8[8] = {ra[e].x, ra[e].y, ra[e].z, ra[e].w, rb[e].x, rb[e].y, rb[e].z, rb[e].w};
@@ -141,6 +235,17 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(
     float xs[TB];
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) xs[tt] = live[tt] ? load1<BF16>(x, rows[tt], d, i) : 0.0f;
+    if constexpr (NORM) {
+      const float g = gamma[i];
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        xs[tt] = norm1<BF16>(xs[tt], rs[tt], g);
+        if (live[tt]) {
+          if constexpr (BF16) static_cast<uint16_t*>(norm_out)[rows[tt] * d + i] = f32_to_bf16(xs[tt]);
+          else static_cast<float*>(norm_out)[rows[tt] * d + i] = xs[tt];
+        }
+      }
+    }
 #pragma unroll
     for (int e = 0; e < EM; ++e) {
       const float r = rrow[e][i];
@@ -218,35 +323,53 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(
   for (int j = 0; j < k; ++j) wout[t * k + j] = wout[t * k + j] / psum;
 }
 
-template <bool BF16, int EM>
+template <bool BF16, int EM, bool NORM>
 hipError_t launch_em(const void* x, const float* router, const float* bias, int64_t T, int d,
-                     int E, int k, float* logits_out, int32_t* idx, float* w, hipStream_t s) {
+                     int E, int k, float* logits_out, int32_t* idx, float* w,
+                     const float* gamma, float eps, void* norm_out, hipStream_t s) {
   constexpr int64_t per_block = kVals / EM;
   const dim3 grid(static_cast<unsigned>((T + per_block - 1) / per_block));
   const dim3 block(kThreads);
-  const bool vec = (d % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(router) & 15) == 0);
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec = (d % 8 == 0) && a16(x) && a16(router) && (!NORM || (a16(gamma) && a16(norm_out)));
   if (vec)
-    hipLaunchKernelGGL((route_kernel<BF16, EM, true>), grid, block, 0, s, x, router, bias, T, d,
-                       E, k, logits_out, idx, w);
+    hipLaunchKernelGGL((route_kernel<BF16, EM, true, NORM>), grid, block, 0, s, x, router, bias, T,
+                       d, E, k, logits_out, idx, w, gamma, eps, norm_out);
   else
-    hipLaunchKernelGGL((route_kernel<BF16, EM, false>), grid, block, 0, s, x, router, bias, T,
-                       d, E, k, logits_out, idx, w);
+    hipLaunchKernelGGL((route_kernel<BF16, EM, false, NORM>), grid, block, 0, s, x, router, bias,
+                       T, d, E, k, logits_out, idx, w, gamma, eps, norm_out);
   return hipGetLastError();
+}
+
+template <bool BF16, bool NORM>
+hipError_t launch_bf(const void* x, const float* router, const float* bias, int64_t T, int d,
+                     int E, int k, float* logits_out, int32_t* idx, float* w,
+                     const float* gamma, float eps, void* norm_out, hipStream_t s) {
+  if (E <= 8)
+    return launch_em<BF16, 8, NORM>(x, router, bias, T, d, E, k, logits_out, idx, w, gamma, eps,
+                                    norm_out, s);
+  return launch_em<BF16, 32, NORM>(x, router, bias, T, d, E, k, logits_out, idx, w, gamma, eps,
+                                   norm_out, s);
 }
 
 }  // namespace
 
 hipError_t launch_route(const void* x, int x_bf16, const float* router, const float* bias,
                         int64_t T, int d, int E, int k, float* logits_out, int32_t* idx,
-                        float* w, hipStream_t s) {
+                        float* w, hipStream_t s, const float* gamma, float eps, void* norm_out) {
   if (T == 0) return hipSuccess;
-  if (x_bf16) {
-    if (E <= 8) return launch_em<true, 8>(x, router, bias, T, d, E, k, logits_out, idx, w, s);
-    return launch_em<true, 32>(x, router, bias, T, d, E, k, logits_out, idx, w, s);
+  if (gamma) {
+    if (x_bf16)
+      return launch_bf<true, true>(x, router, bias, T, d, E, k, logits_out, idx, w, gamma, eps,
+                                   norm_out, s);
+    return launch_bf<false, true>(x, router, bias, T, d, E, k, logits_out, idx, w, gamma, eps,
+                                  norm_out, s);
   }
-  if (E <= 8) return launch_em<false, 8>(x, router, bias, T, d, E, k, logits_out, idx, w, s);
-  return launch_em<false, 32>(x, router, bias, T, d, E, k, logits_out, idx, w, s);
+  if (x_bf16)
+    return launch_bf<true, false>(x, router, bias, T, d, E, k, logits_out, idx, w, nullptr, 0.0f,
+                                  nullptr, s);
+  return launch_bf<false, false>(x, router, bias, T, d, E, k, logits_out, idx, w, nullptr, 0.0f,
+                                 nullptr, s);
 }
 
 }  // namespace moe

@@ -141,3 +141,33 @@ def test_tuning_hooks_validate():
 def test_binding_raises_on_error_status():
     with pytest.raises(moe.MoeError):
         moe.moe_set_ffn_variant(7)
+
+
+def test_block_forward_rejects_bad_arguments():
+    fb = lib.moe_block_forward
+    ws = moe.moe_workspace_bytes(4, 128, 256, 8, 2, moe.MOE_BF16)
+    H = ctypes.c_void_p(1 << 40)               # hidden: 4 x 128 bf16 = 1 KiB
+    N = ctypes.c_void_p((1 << 40) + 4096)      # norm_out
+    O = ctypes.c_void_p((1 << 40) + 8192)      # out
+
+    def call(**kw):
+        return fb(kw.get("h", H), kw.get("dtype", moe.MOE_BF16), kw.get("g", BAD),
+                  ctypes.c_float(kw.get("eps", 1e-5)), kw.get("n", N), BAD, None, BAD, BAD, BAD,
+                  kw.get("T", 4), 128, 256, 8, 2, kw.get("o", O), kw.get("odt", moe.MOE_F32),
+                  None, None, None, BAD, ws, None)
+
+    assert call(eps=-1e-5) == moe.MOE_EINVAL
+    assert call(eps=float("nan")) == moe.MOE_EINVAL
+    assert call(eps=float("inf")) == moe.MOE_EINVAL
+    assert call(g=None) == moe.MOE_EINVAL
+    assert call(n=None) == moe.MOE_EINVAL
+    assert call(dtype=9) == moe.MOE_EINVAL
+    assert call(odt=4) == moe.MOE_EINVAL
+    # norm_out or out overlapping hidden, or each other
+    assert call(n=ctypes.c_void_p((1 << 40) + 512)) == moe.MOE_EINVAL
+    assert call(o=ctypes.c_void_p((1 << 40) + 1000)) == moe.MOE_EINVAL
+    assert call(o=ctypes.c_void_p((1 << 40) + 4096 + 64)) == moe.MOE_EINVAL
+    # the rest as for moe_forward: shape, workspace and alignment checks
+    assert fb(H, moe.MOE_BF16, BAD, ctypes.c_float(1e-5), N, BAD, None, BAD, BAD, BAD, 4, 128,
+              256, 8, 2, O, moe.MOE_F32, None, None, None, BAD, 0, None) == moe.MOE_EWORKSPACE
+    assert call(h=ctypes.c_void_p((1 << 40) + 8)) == moe.MOE_ENOTSUP

@@ -107,6 +107,67 @@ def test_steps_and_forward_match_oracle(m, name, cfg, variant):
         assert torch.equal(out_p, g["out"])
 
 
+BLOCK_CASES = ["tiny", "bf16_tiles", "bf16_ragged", "bf16_one_token", "bf16_skew", "bf16_E16_k4",
+               "f32_odd"]
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("name", BLOCK_CASES)
+def test_block_forward_matches_oracle(m, name, variant):
+    """out = h + layer(RMSNorm(h)): the normed rows against the oracle's norm
+    (within one rounding to the stored type), the layer on those stored rows
+    against the oracle under the rules of the plain layer, the residual add
+    exact, and the same routing and sums as moe_forward run on norm_out."""
+    cfg = dict(SMALL)[name]
+    if cfg["dtype"] == gen.F32 and variant == 2:
+        pytest.skip("the kernel family switch applies to bf16 only")
+    print(f"[parity] block {name} variant={variant}", flush=True)
+    m.moe_set_ffn_variant(variant)
+    inp = gen.make_inputs(**cfg)
+    dev = to_device(inp)
+    T, d, E, k = inp["T"], inp["d"], inp["E"], inp["k"]
+    gamma = gen.make_norm_weight(d, seed=inp["seed"])
+    g_t = torch.from_numpy(gamma).cuda()
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    out, nrm = m.moe_block_forward(dev["x"], g_t, dev["router"], dev["w1"], dev["w3"], dev["w2"],
+                                   k, eps=1e-5, logit_bias=dev["bias"], out_dtype=torch.float32,
+                                   topk_idx_out=idx, topk_w_out=w, counts_out=counts)
+    out_b, _ = m.moe_block_forward(dev["x"], g_t, dev["router"], dev["w1"], dev["w3"], dev["w2"],
+                                   k, eps=1e-5, logit_bias=dev["bias"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    # the normed rows: one rounding (bf16) or float32 error away from the oracle
+    n_ref = oracle.rms_norm(inp["x"], gamma, 1e-5)
+    n_gpu = host(nrm)
+    if inp["dtype"] == gen.BF16:
+        assert (np.abs(n_gpu - n_ref) <= bf16_half_ulp(n_ref) + 2.0 ** -20 * np.abs(n_ref)).all()
+        n_bits = nrm.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        assert (np.abs(n_gpu - n_ref) <= 1e-5 * np.abs(n_ref) + 1e-7).all()
+        n_bits = nrm.cpu().numpy()
+    # the layer on the stored rows, under the plain layer's rules
+    on_norm = dict(inp, x=n_bits)
+    logits64 = oracle.router_logits(n_bits, inp["router"], inp["bias"])
+    idx_g = host(idx)
+    check_routing(logits64, k, idx_g, host(w))
+    assert np.array_equal(host(counts), np.bincount(idx_g.ravel(), minlength=E))
+    mlp_ref = expected_output(on_norm, idx_g, None, np.arange(T), logits64)
+    mlp_gpu = host(out).astype(np.float64) - oracle.widen(inp["x"])
+    assert rel_err(mlp_gpu, mlp_ref) <= OUT_TOL[inp["dtype"]]
+    # same kernels as moe_forward on norm_out, then the residual added in float32
+    idx_f = torch.empty_like(idx)
+    w_f = torch.empty_like(w)
+    out_f = m.moe_forward(nrm, dev["router"], dev["w1"], dev["w3"], dev["w2"], k,
+                          logit_bias=dev["bias"], out_dtype=torch.float32, topk_idx_out=idx_f,
+                          topk_w_out=w_f)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx) and torch.equal(w_f, w)
+    assert torch.equal(out, out_f + dev["x"].float())
+    assert torch.equal(out_b, out.to(torch.bfloat16))
+    m.moe_set_ffn_variant(0)
+
+
 def _pack_reference(w):
     """Fragment order as include/moe.h defines it, by plain index arithmetic."""
     E, R, C = w.shape
