@@ -278,6 +278,35 @@ def block_forward(h, gamma, router, w1, w3, w2, k: int, bias=None, eps: float = 
 
 
 # --------------------------------------------------------------------------
+# weight-only int8 expert weights
+# --------------------------------------------------------------------------
+def quantize_int8(w):
+    """Per-output-row symmetric int8 codes of a weight [..., rows, cols].
+
+    ZeroModels Mixtral page, "Lower memory": checkpoints may load weight-only
+    quantized to int8 with bfloat16 activations. The pages give no scheme;
+    the reading taken is one float32 scale per output row,
+      scale = max_k |w[n, k]| / 127,  q[n, k] = round_half_even(w[n, k] / scale)
+    (q = 0 for an all-zero row), clipped to [-127, 127]. The scale and the
+    integer codes are decided in float32, as the quantizer on the device
+    decides them (correctly rounded division), so the two agree exactly.
+    Returns (q int8, scale float32 [..., rows]).
+    """
+    wf = widen(w).astype(np.float32)  # bfloat16 and float32 inputs are exact here
+    amax = np.abs(wf).max(axis=-1)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint(wf / scale[..., None])
+    q = np.where(scale[..., None] > 0, q, 0.0)
+    return np.clip(q, -127, 127).astype(np.int8), scale
+
+
+def dequantize_int8(q, scale) -> np.ndarray:
+    """The weights the int8 layer computes with: scale[n] * q[n, k], float64 (exact)."""
+    return np.asarray(q, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+# --------------------------------------------------------------------------
 # second, independent formulations
 # --------------------------------------------------------------------------
 def gate_matrix(idx, w, E: int) -> np.ndarray:

@@ -377,3 +377,43 @@ def test_block_is_residual_plus_layer_on_normed_rows(tiny):
                               tiny["w2"], tiny["k"], tiny["bias"], eps=0.0)
     assert np.array_equal(s["idx"], b0["idx"])
     assert np.allclose(s["mlp"], b0["mlp"], rtol=1e-9, atol=1e-12)
+
+
+# ------------------------------------------------------ int8 expert weights --
+def test_quantize_int8_worked_example():
+    # row 0: max |w| = 127 -> scale 1 exactly; -63.5 and 0.5 are halfway cases and go to even
+    # row 1: max |w| = 127/4 -> scale 1/4; w / scale = [4, -2, 127, 1] exactly
+    # row 2: all zero -> scale 0 and codes 0
+    w = np.array([[[127.0, -63.5, 0.5, 1.0], [1.0, -0.5, 31.75, 0.25], [0.0, 0.0, 0.0, 0.0]]],
+                 np.float32)
+    q, s = oracle.quantize_int8(w)
+    assert s.tolist() == [[1.0, 0.25, 0.0]]
+    assert q.tolist() == [[[127, -64, 0, 1], [4, -2, 127, 1], [0, 0, 0, 0]]]
+    assert q.dtype == np.int8 and s.dtype == np.float32
+
+
+def test_quantize_int8_error_bound_and_symmetry():
+    rng = np.random.default_rng(11)
+    w = gen.f32_to_bf16_bits(rng.standard_normal((3, 32, 96)).astype(np.float32) * 0.05)
+    q, s = oracle.quantize_int8(w)
+    wd = oracle.widen(w)
+    err = np.abs(wd - oracle.dequantize_int8(q, s))
+    # round to nearest: within half a step, plus the float32 rounding of w / scale
+    # (|w / scale| <= 127, so at most 127 * 2^-24 < 2^-16 of a step)
+    assert (err <= s[..., None] * (0.5 + 2.0 ** -16)).all()
+    assert err.max() > 0.45 * s.max()  # and the bound is not vacuous
+    # the largest magnitude of each row becomes +-127
+    assert (np.abs(q).max(axis=-1) == 127).all()
+    q2, s2 = oracle.quantize_int8(gen.f32_to_bf16_bits(-gen.bf16_bits_to_f32(w)))
+    assert np.array_equal(s2, s) and np.array_equal(q2, -q)
+
+
+def test_quantize_int8_matches_library_rounding():
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((2, 16, 64)) * 0.02).astype(np.float32)
+    q, s = oracle.quantize_int8(w)
+    wt = torch.from_numpy(w)
+    st = wt.abs().amax(dim=-1) / torch.tensor(127.0, dtype=torch.float32)
+    qt = torch.clamp(torch.round(wt / st[..., None]), -127, 127).to(torch.int8)
+    assert np.array_equal(s, st.numpy())
+    assert np.array_equal(q, qt.numpy())
