@@ -41,7 +41,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 STAGES = ("route", "permute", "gate_up", "down", "combine")
 # the gate/up kernels' sources: traffic counters are only reported while they are unchanged
 FFN_SOURCES = [os.path.join(ROOT, "sparse_mixture_experts_06_amd", "csrc", f)
-               for f in ("ffn_bf16.hip", "ffn_dma.hip", "common.h")]
+               for f in ("ffn_bf16.hip", "ffn_dma.hip", "ffn_int8.hip", "common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -63,6 +63,9 @@ def parse():
                    help="expert weight layout of the timed steps")
     p.add_argument("--no-compare", action="store_true",
                    help="do not also time the other weight layout")
+    p.add_argument("--weights", choices=("bf16", "int8"), default="bf16",
+                   help="expert weight format: bf16, or weight-only int8 codes with float32 row "
+                        "scales (moe_quantize_weight, once at load time)")
     p.add_argument("--block", action="store_true",
                    help="time the MLP half of the decoder block instead of the bare layer: "
                         "RMS norm in front (eps 1e-5) and the residual add after "
@@ -111,20 +114,27 @@ def upload(inp, torch):
     return {k: up(inp[k]) for k in ("x", "router", "w1", "w3", "w2", "bias")}
 
 
-def algorithmic_work(cfg, counts, block=False):
+def algorithmic_work(cfg, counts, block=False, int8=False):
     """Bytes and flops the layer must move/do (intermediates h and y excluded).
     block: the norm weight is read and the normed rows are written (an output
-    of moe_block_forward), the norm and the residual add are ~4*T*d flops."""
+    of moe_block_forward), the norm and the residual add are ~4*T*d flops.
+    int8: expert weights are 1-byte codes plus a float32 scale per row."""
     T, d, F, E, k = cfg["T"], cfg["d"], cfg["ffn"], cfg["E"], cfg["k"]
     wb = 2 if cfg["dtype"] == "bf16" else 4
     A = T * k
     active = sum(1 for c in counts if c > 0)
-    layer_bytes = active * 3 * d * F * wb + T * d * wb + T * d * wb + E * d * 4
+    if int8:
+        layer_w = active * (3 * d * F + (2 * F + d) * 4)
+        gate_up_w = active * (2 * d * F + 2 * F * 4)
+    else:
+        layer_w = active * 3 * d * F * wb
+        gate_up_w = active * 2 * d * F * wb
+    layer_bytes = layer_w + T * d * wb + T * d * wb + E * d * 4
     layer_flops = 2 * A * 3 * d * F + 2 * T * E * d
     if block:
         layer_bytes += d * 4 + T * d * wb
         layer_flops += 4 * T * d
-    gate_up_bytes = active * 2 * d * F * wb + T * d * wb + A * F * wb
+    gate_up_bytes = gate_up_w + T * d * wb + A * F * wb
     gate_up_flops = 2 * A * 2 * d * F
     return layer_bytes, layer_flops, gate_up_bytes, gate_up_flops
 
@@ -152,7 +162,8 @@ def traffic_entry(workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-GATE_UP_KERNELS = ("gate_up_stream_kernel", "gate_up_dma_kernel", "tiled_kernel<true")
+GATE_UP_KERNELS = ("gate_up_stream_kernel", "gate_up_dma_kernel", "tiled_kernel<true",
+                   "gate_up_w8_kernel")
 
 
 def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
@@ -198,6 +209,14 @@ def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
     print(json.dumps(rec["workloads"][workload]))
 
 
+def oracle_quantized(name, inp):
+    """Dequantized weights of the oracle's int8 quantization of inp[name]
+    (float64), and the scales."""
+    import oracle
+    q, sc = oracle.quantize_int8(inp[name])
+    return oracle.dequantize_int8(q, sc), sc
+
+
 def cpu_baseline(cfg, inp, budget_s=10.0, gamma=None):
     """The float64 oracle on a bounded sample of the same workload: consecutive
     slices of n tokens of the batch (wrapping around), full routing and all their
@@ -236,7 +255,9 @@ def cpu_baseline(cfg, inp, budget_s=10.0, gamma=None):
 def main():
     args = parse()
     if args.pmc_summary:
-        pmc_summary(args.workload, args.pmc_summary[0], args.pmc_summary[1],
+        key = args.workload + ("+block" if args.block else "") + \
+            ("+int8" if args.weights == "int8" else "")
+        pmc_summary(key, args.pmc_summary[0], args.pmc_summary[1],
                     args.calib_copy_mib or 1024)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -262,8 +283,18 @@ def main():
     inp = gen.make_inputs(**cfg)
     dev = upload(inp, torch)
     std_sets = [dev, dict(dev, w1=dev["w1"].clone(), w3=dev["w3"].clone(), w2=dev["w2"].clone())]
-    packed = args.layout == "packed" and cfg["dtype"] == "bf16"
-    if packed:
+    int8 = args.weights == "int8"
+    if int8 and cfg["dtype"] != "bf16":
+        raise SystemExit("int8 weights go with bfloat16 activations")
+    packed = args.layout == "packed" and cfg["dtype"] == "bf16" and not int8
+    if int8:
+        q_sets = []
+        for st in std_sets:
+            qw = moe.QuantizedWeights(st["w1"], st["w3"], st["w2"])
+            q_sets.append(dict(st, w1=qw.w1, w3=qw.w3, w2=qw.w2))
+        std_sets = None
+        sets = q_sets
+    elif packed:
         pk_sets = []
         for st in std_sets:
             pw = moe.PackedWeights(st["w1"], st["w3"], st["w2"])
@@ -336,7 +367,8 @@ def main():
                  "ms_per_step": round(ms_std, 4)}
 
     cnt = counts.cpu().tolist()
-    layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt, args.block)
+    workload_key = args.workload + ("+block" if args.block else "") + ("+int8" if int8 else "")
+    layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt, args.block, int8)
     ms_step = wall * 1e3 / args.steps
     tok_s = T / (ms_step / 1e3)
     decode_like = (T * k) <= 32 * E  # the streaming kernels' regime: weight-bandwidth bound
@@ -352,7 +384,7 @@ def main():
     roof.update({"kernel": "gate_up (w1/w3 grouped GEMM + SiLU*mul)",
                  "avg_us": round(stage_ms["gate_up"] * 1e3, 2),
                  "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops,
-                 "traffic": traffic_entry(args.workload)})
+                 "traffic": traffic_entry(workload_key)})
     layer_tflops = layer_flops / (ms_step / 1e3) / 1e12
     layer_gbs = layer_bytes / (ms_step / 1e3) / 1e9
     rec = {
@@ -360,7 +392,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg["dtype"], "data": "synthetic",
-        "config": {"workload": args.workload + ("+block" if args.block else ""), "T": T, "d": d,
+        "config": {"workload": workload_key, "T": T, "d": d,
                    "ffn": F, "E": E, "k": k, "seed": cfg["seed"], "logit_bias": cfg["bias"]},
         "roofline": roof,
         "layer": {"tflops": round(layer_tflops, 2),
@@ -370,13 +402,21 @@ def main():
                   "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
                   "expert_counts": cnt},
     }
-    rec["weights_layout"] = ("fragment order (moe_pack_weight once at load time)" if packed
+    rec["weights_layout"] = ("weight-only int8, float32 row scales (moe_quantize_weight once at "
+                             "load time)" if int8 else
+                             "fragment order (moe_pack_weight once at load time)" if packed
                              else "standard [E, ffn, d]")
     if other is not None:
         rec["other_layout"] = other
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg, inp, gamma=gamma)
+        base_inp = inp
+        if int8:  # the oracle computes with the weights the int8 codes stand for
+            base_inp = dict(inp)
+            for name in ("w1", "w3", "w2"):
+                q, sc = oracle_quantized(name, inp)
+                base_inp[name] = q
+        rec["cpu_baseline"] = cpu_baseline(cfg, base_inp, gamma=gamma)
     print(json.dumps(rec), flush=True)
 
 

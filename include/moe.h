@@ -64,11 +64,14 @@ enum moe_status {
   MOE_EHIP = 4        /* the HIP runtime reported an error */
 };
 
-/* Element types. MOE_BF16_PACKED is accepted only as the `dtype` of
- * moe_expert_ffn and moe_forward: x is bfloat16 as for MOE_BF16, and w1, w3
- * and w2 are the bfloat16 weights rearranged by moe_pack_weight (same
- * values, fragment order); everything else is unchanged. */
-enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_BF16_PACKED = 2 };
+/* Element types. MOE_BF16_PACKED and MOE_INT8_PACKED are accepted only as
+ * the `dtype` of moe_expert_ffn, moe_forward and moe_block_forward: x is
+ * bfloat16 as for MOE_BF16, and w1, w3 and w2 are, for MOE_BF16_PACKED, the
+ * bfloat16 weights rearranged by moe_pack_weight (same values, fragment
+ * order) and, for MOE_INT8_PACKED, weight-only int8 matrices made by
+ * moe_quantize_weight (codes plus float32 row scales); everything else is
+ * unchanged. */
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_BF16_PACKED = 2, MOE_INT8_PACKED = 3 };
 
 #define MOE_MAX_EXPERTS 32
 
@@ -178,6 +181,30 @@ int moe_block_forward(const void* hidden, int dtype, const float* norm_weight, f
  * both pointers 16-byte aligned, else MOE_ENOTSUP. */
 int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* out,
                     void* stream);
+
+/* Weight-only int8 quantization for the MOE_INT8_PACKED path (ZeroModels
+ * Mixtral page, "Lower memory": weight-only int8 with bfloat16 activations).
+ * For each output row n of w [E, rows, cols] (bfloat16, standard layout):
+ *   scale[e][n] = max_k |w[e][n][k]| / 127                  (float32)
+ *   q[e][n][k]  = round_half_even(w[e][n][k] / scale[e][n]) (int8, |q| <= 127;
+ *                 0 for an all-zero row)
+ * computed in float32 (the division correctly rounded). `out` receives
+ * moe_quantized_weight_bytes(E, rows, cols) bytes: the codes in 16-row x
+ * 64-column blocks of 1 KiB (block (e, row tile rt, column step s) at byte
+ * ((e*rows/16 + rt)*cols/64 + s)*1024; in it, row r's columns 64s + 8g + i sit
+ * at byte (16g + r)*16 + i and columns 64s + 32 + 8g + i at (16g + r)*16 + 8
+ * + i, for g < 4, i < 8), then, from the next multiple of 256 bytes, the
+ * float32 scales [E, rows]. Quantize w1 and w3 with rows = ffn, cols = d, and
+ * w2 with rows = d, cols = ffn. The layer then computes with the weights
+ * scale * q: each expert's products accumulate in float32 over bfloat16
+ * activations and codes, and the row's scale multiplies the finished sum.
+ * dtype must be MOE_BF16; rows % 16 == 0 and cols % 64 == 0 and 16-byte
+ * aligned, non-overlapping buffers, else MOE_ENOTSUP / MOE_EINVAL. With int8
+ * weights the streaming expert kernels run at every batch size (the format
+ * is meant for the weight-bandwidth-bound decode case). */
+size_t moe_quantized_weight_bytes(int E, int rows, int cols);
+int moe_quantize_weight(const void* w, int dtype, int E, int rows, int cols, void* out,
+                        void* stream);
 
 /* ---- tuning and profiling hooks (process-wide, not thread-safe) ---------- */
 

@@ -6,14 +6,16 @@ first use (or by load()), and every call raises if it has not been built;
 there is no fallback.
 """
 from ._lib import (MOE_BF16, MOE_BF16_PACKED, MOE_EHIP, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE,
-                   MOE_F32, MOE_MAX_EXPERTS, MOE_OK, MoeError, PackedWeights, header_functions,
+                   MOE_F32, MOE_INT8_PACKED, MOE_MAX_EXPERTS, MOE_OK, MoeError, PackedWeights,
+                   QuantizedMatrix, QuantizedWeights, header_functions, moe_quantize_weight,
                    load, moe_block_forward, moe_combine, moe_expert_ffn, moe_forward, moe_pack_weight,
                    moe_permute,
                    moe_route, moe_set_ffn_variant, moe_set_stage_events, moe_workspace_bytes,
                    strerror, workspace)
 
 __all__ = ["MOE_BF16", "MOE_BF16_PACKED", "MOE_EHIP", "MOE_EINVAL", "MOE_ENOTSUP",
-           "MOE_EWORKSPACE", "MOE_F32", "MOE_MAX_EXPERTS", "MOE_OK", "MoeError", "PackedWeights",
+           "MOE_EWORKSPACE", "MOE_F32", "MOE_INT8_PACKED", "MOE_MAX_EXPERTS", "MOE_OK", "MoeError",
+           "PackedWeights", "QuantizedMatrix", "QuantizedWeights", "moe_quantize_weight",
            "header_functions", "load", "moe_block_forward", "moe_combine", "moe_expert_ffn", "moe_forward",
            "moe_pack_weight", "moe_permute", "moe_route", "moe_set_ffn_variant",
            "moe_set_stage_events", "moe_workspace_bytes", "strerror", "workspace"]

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
-MOE_F32, MOE_BF16, MOE_BF16_PACKED = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_BF16_PACKED, MOE_INT8_PACKED = 0, 1, 2, 3
 MOE_MAX_EXPERTS = 32
 
 _c_i64 = ctypes.c_int64
@@ -42,6 +42,8 @@ _SIGNATURES = {
                                    _vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _vp, _c_int,
                                    _vp, _vp, _vp, _vp, _c_sz, _vp]),
     "moe_pack_weight": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_quantized_weight_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
+    "moe_quantize_weight": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_set_ffn_variant": (_c_int, [_c_int]),
     "moe_set_stage_events": (_c_int, [_vp, _c_int]),
 }
@@ -97,8 +99,12 @@ def _dtype_code(t: torch.dtype) -> int:
     raise ValueError(f"unsupported dtype {t} (float32 or bfloat16)")
 
 
-def _weight_code(t: torch.dtype, packed: bool) -> int:
+def _weight_code(t: torch.dtype, packed: bool, w=None) -> int:
     code = _dtype_code(t)
+    if isinstance(w, QuantizedMatrix):
+        if code != MOE_BF16:
+            raise ValueError("int8 weights take bfloat16 activations")
+        return MOE_INT8_PACKED
     if packed:
         if code != MOE_BF16:
             raise ValueError("packed weights are bfloat16 only")
@@ -109,6 +115,8 @@ def _weight_code(t: torch.dtype, packed: bool) -> int:
 def _ptr(t):
     if t is None:
         return None
+    if isinstance(t, QuantizedMatrix):
+        t = t.blob
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
@@ -119,6 +127,8 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def _need(t, name, dtype, shape, device):
+    if isinstance(t, QuantizedMatrix):  # int8 codes + scales: shape and device only
+        dtype = t.dtype
     if t.dtype != dtype:
         raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -153,6 +163,61 @@ def moe_pack_weight(w, out=None):
     st = load().moe_pack_weight(_ptr(w), MOE_BF16, E, rows, cols, _ptr(out), _stream(w.device))
     _check("moe_pack_weight", st)
     return out
+
+
+class QuantizedMatrix:
+    """Weight-only int8 matrix made by moe_quantize_weight: the uint8 blob the
+    library reads (codes in 16 x 64 blocks, then float32 row scales) and the
+    logical shape (E, rows, cols) of the matrix it stands for."""
+
+    dtype = "int8-blob"
+
+    def __init__(self, blob, shape):
+        self.blob = blob
+        self.shape = tuple(int(v) for v in shape)
+        self.device = blob.device
+
+    def codes(self) -> torch.Tensor:
+        """The int8 codes in standard [E, rows, cols] order (a copy)."""
+        E, rows, cols = self.shape
+        q = self.blob[:E * rows * cols].view(torch.int8)
+        q = q.view(E, rows // 16, cols // 64, 4, 16, 2, 8)  # e, rt, s, g, r, half, i
+        return q.permute(0, 1, 4, 2, 5, 3, 6).reshape(E, rows, cols).contiguous()
+
+    def scales(self) -> torch.Tensor:
+        """float32 [E, rows]."""
+        E, rows, cols = self.shape
+        off = (E * rows * cols + 255) // 256 * 256
+        return self.blob[off:off + E * rows * 4].view(torch.float32).view(E, rows)
+
+
+def moe_quantize_weight(w, out=None) -> QuantizedMatrix:
+    """Weight-only int8 copy of bf16 weights w [E, rows, cols] (see moe.h)."""
+    if w.dtype != torch.bfloat16 or w.dim() != 3:
+        raise ValueError("moe_quantize_weight takes a bfloat16 tensor [E, rows, cols]")
+    E, rows, cols = w.shape
+    n = int(load().moe_quantized_weight_bytes(E, rows, cols))
+    if n == 0:
+        raise ValueError("moe_quantize_weight needs rows % 16 == 0 and cols % 64 == 0")
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=w.device)
+    if out.dtype != torch.uint8 or out.numel() < n or out.device != w.device:
+        raise ValueError(f"out: a uint8 tensor of at least {n} bytes on {w.device}")
+    st = load().moe_quantize_weight(_ptr(w), MOE_BF16, E, rows, cols, _ptr(out),
+                                    _stream(w.device))
+    _check("moe_quantize_weight", st)
+    return QuantizedMatrix(out, (E, rows, cols))
+
+
+class QuantizedWeights:
+    """w1, w3, w2 as weight-only int8 matrices (moe_quantize_weight), for
+    moe_forward / moe_expert_ffn / moe_block_forward in place of the bf16
+    tensors."""
+
+    def __init__(self, w1, w3, w2):
+        self.w1 = moe_quantize_weight(w1)
+        self.w3 = moe_quantize_weight(w3)
+        self.w2 = moe_quantize_weight(w2)
 
 
 class PackedWeights:
@@ -233,7 +298,7 @@ def moe_expert_ffn(x, w1, w3, w2, offsets, sorted_asg, k: int, y=None, ws=None, 
     if y is None:
         y = torch.empty(T * k, d, dtype=torch.float32, device=dev)
     _need(y, "y", torch.float32, (T * k, d), dev)
-    code = _weight_code(x.dtype, packed)
+    code = _weight_code(x.dtype, packed, w1)
     if ws is None:
         ws = workspace(T, d, ffn, E, k, code, dev)
     st = load().moe_expert_ffn(_ptr(x), code, _ptr(w1), _ptr(w3), _ptr(w2),
@@ -281,7 +346,7 @@ def moe_forward(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dt
         _need(topk_w_out, "topk_w_out", torch.float32, (T, k), dev)
     if counts_out is not None:
         _need(counts_out, "counts_out", torch.int32, (E,), dev)
-    code = _weight_code(x.dtype, packed)
+    code = _weight_code(x.dtype, packed, w1)
     if ws is None:
         ws = workspace(T, d, ffn, E, k, code, dev)
     st = load().moe_forward(_ptr(x), code, _ptr(router), _ptr(logit_bias),
@@ -318,7 +383,7 @@ def moe_block_forward(hidden, norm_weight, router, w1, w3, w2, k: int, eps: floa
         _need(topk_w_out, "topk_w_out", torch.float32, (T, k), dev)
     if counts_out is not None:
         _need(counts_out, "counts_out", torch.int32, (E,), dev)
-    code = _weight_code(hidden.dtype, packed)
+    code = _weight_code(hidden.dtype, packed, w1)
     if ws is None:
         ws = workspace(T, d, ffn, E, k, code, dev)
     st = load().moe_block_forward(_ptr(hidden), code, _ptr(norm_weight), float(eps),

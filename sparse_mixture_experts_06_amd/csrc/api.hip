@@ -20,7 +20,10 @@ struct Layout {
   size_t idx, w, counts, offsets, sorted, pos, h, y, total;
 };
 
-inline bool is_bf16(int dtype) { return dtype == MOE_BF16 || dtype == MOE_BF16_PACKED; }
+// bfloat16 activations (x, h): bf16 weights in either layout, or int8 weights
+inline bool is_bf16(int dtype) {
+  return dtype == MOE_BF16 || dtype == MOE_BF16_PACKED || dtype == MOE_INT8_PACKED;
+}
 
 // float32 partial results the down projection may leave (split K); the most
 // either kernel family leaves, so that the workspace does not depend on the
@@ -51,7 +54,9 @@ Layout layout(int64_t T, int d, int ffn, int E, int k, int dtype) {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 inline bool valid_dtype(int t) { return t == MOE_F32 || t == MOE_BF16; }
-inline bool valid_weight_dtype(int t) { return valid_dtype(t) || t == MOE_BF16_PACKED; }
+inline bool valid_weight_dtype(int t) {
+  return valid_dtype(t) || t == MOE_BF16_PACKED || t == MOE_INT8_PACKED;
+}
 
 int check_sizes(int64_t T, int E, int k) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E) return MOE_EINVAL;
@@ -91,7 +96,16 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
             int k, float* part, void* h, hipStream_t s, bool with_events, int* nsplit_out) {
   const int64_t A = T * k;
   hipError_t err;
-  if (is_bf16(dtype)) {
+  if (dtype == MOE_INT8_PACKED) {
+    // int8 weights: the streaming kernels at every batch size
+    *nsplit_out = moe::down_splits(1, A, d, ffn, E);
+    err = moe::launch_gate_up_int8(static_cast<const uint16_t*>(x), w1, w3, offsets, sorted_asg,
+                                   d, ffn, E, k, static_cast<uint16_t*>(h), s);
+    if (err != hipSuccess) return MOE_EHIP;
+    if (with_events) stage(3, s);
+    err = moe::launch_down_int8(static_cast<const uint16_t*>(h), w2, offsets, A, d, ffn, E,
+                                *nsplit_out, part, s);
+  } else if (is_bf16(dtype)) {
     const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
     const bool packed = dtype == MOE_BF16_PACKED;
     *nsplit_out = moe::down_splits(variant, A, d, ffn, E);
@@ -182,7 +196,9 @@ int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, con
   char* base = static_cast<char*>(ws);
   const int64_t A = T * k;
   const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
-  const int nsplit = is_bf16(dtype) ? moe::down_splits(variant, A, d, ffn, E) : 1;
+  const int nsplit = dtype == MOE_INT8_PACKED ? moe::down_splits(1, A, d, ffn, E)
+                     : is_bf16(dtype)          ? moe::down_splits(variant, A, d, ffn, E)
+                                               : 1;
   float* part = nsplit > 1 ? reinterpret_cast<float*>(base + L.y) : y;
   int used = 1;
   st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, part, base + L.h, s,
@@ -304,6 +320,28 @@ int moe_block_forward(const void* hidden, int dtype, const float* norm_weight, f
   return forward_impl(hidden, dtype, norm_weight, eps, norm_out, router, logit_bias, w1, w3, w2,
                       T, d, ffn, E, k, out, out_dtype, topk_idx_out, topk_w_out, counts_out, ws,
                       ws_bytes, stream);
+}
+
+size_t moe_quantized_weight_bytes(int E, int rows, int cols) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || rows < 1 || cols < 1) return 0;
+  if (rows % 16 != 0 || cols % 64 != 0) return 0;
+  return moe::int8_weight_bytes(E, rows, cols);
+}
+
+int moe_quantize_weight(const void* w, int dtype, int E, int rows, int cols, void* out,
+                        void* stream) {
+  if (dtype != MOE_BF16) return MOE_EINVAL;
+  if (E < 1 || E > MOE_MAX_EXPERTS || rows < 1 || cols < 1) return MOE_EINVAL;
+  if (rows % 16 != 0 || cols % 64 != 0) return MOE_ENOTSUP;
+  if (!w || !out) return MOE_EINVAL;
+  if (!aligned16(w) || !aligned16(out)) return MOE_ENOTSUP;
+  const size_t in_bytes = static_cast<size_t>(E) * rows * cols * 2;
+  const size_t out_bytes = moe::int8_weight_bytes(E, rows, cols);
+  const char* a = static_cast<const char*>(w);
+  const char* b = static_cast<const char*>(out);
+  if (a < b + out_bytes && b < a + in_bytes) return MOE_EINVAL;  // must not overlap
+  return hip_status(moe::launch_quantize_int8(static_cast<const uint16_t*>(w), E, rows, cols, out,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* out,

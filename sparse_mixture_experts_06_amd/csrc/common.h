@@ -123,6 +123,17 @@ int dma_down_splits(int64_t A, int d, int ffn, int E);
 hipError_t launch_down_dma(const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
                            int64_t A, int d, int ffn, int E, int nsplit, float* part,
                            hipStream_t s);
+// weight-only int8 experts (ffn_int8.hip): bytes of one quantized matrix
+// (codes, then float32 row scales at the next 256-byte boundary), the
+// quantizer, and the streaming gate/up and down kernels that read it
+size_t int8_weight_bytes(int E, int rows, int cols);
+hipError_t launch_quantize_int8(const uint16_t* w, int E, int rows, int cols, void* out,
+                                hipStream_t s);
+hipError_t launch_gate_up_int8(const uint16_t* x, const void* w1, const void* w3,
+                               const int32_t* offsets, const int32_t* sorted_asg, int d, int ffn,
+                               int E, int k, uint16_t* h, hipStream_t s);
+hipError_t launch_down_int8(const uint16_t* h, const void* w2, const int32_t* offsets, int64_t A,
+                            int d, int ffn, int E, int nsplit, float* part, hipStream_t s);
 // standard [E, R, C] bf16 -> fragment order (16-row x 32-column fragments)
 hipError_t launch_pack_bf16(const uint16_t* w, int E, int R, int C, uint16_t* out, hipStream_t s);
 

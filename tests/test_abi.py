@@ -87,7 +87,7 @@ def test_expert_ffn_rejects_bad_arguments():
                          kw.get("ws", BAD), kw.get("wsb", ws), None]
     assert f(*args(d=100)) == moe.MOE_ENOTSUP                  # bf16 needs d % 64 == 0
     assert f(*args(ffn=96)) == moe.MOE_ENOTSUP                 # and ffn % 64 == 0
-    assert f(*args(dtype=3)) == moe.MOE_EINVAL
+    assert f(*args(dtype=9)) == moe.MOE_EINVAL
     assert f(*args(x=None)) == moe.MOE_EINVAL
     assert f(*args(ws=None)) == moe.MOE_EWORKSPACE
     assert f(*args(wsb=ws - 1)) == moe.MOE_EWORKSPACE
@@ -116,6 +116,35 @@ def test_combine_and_forward_reject_bad_arguments():
     assert call(x=None) == moe.MOE_EINVAL
     assert call(wsb=0) == moe.MOE_EWORKSPACE
     assert call(x=MISALIGNED) == moe.MOE_ENOTSUP
+
+
+def test_quantize_weight_rejects_bad_arguments():
+    qz = lib.moe_quantize_weight
+    n = lib.moe_quantized_weight_bytes
+    assert n(8, 64, 128) == 8 * 64 * 128 + 8 * 64 * 4          # codes, then scales at 256 B
+    assert n(1, 16, 64) == 1024 + 64
+    assert n(8, 40, 128) == 0 and n(8, 64, 96) == 0 and n(0, 64, 128) == 0
+    assert qz(BAD, moe.MOE_F32, 8, 64, 128, BAD, None) == moe.MOE_EINVAL     # bf16 only
+    assert qz(BAD, moe.MOE_BF16, 8, 40, 128, BAD, None) == moe.MOE_ENOTSUP   # rows % 16
+    assert qz(BAD, moe.MOE_BF16, 8, 64, 96, BAD, None) == moe.MOE_ENOTSUP    # cols % 64
+    assert qz(None, moe.MOE_BF16, 8, 64, 128, BAD, None) == moe.MOE_EINVAL
+    assert qz(MISALIGNED, moe.MOE_BF16, 8, 64, 128, ctypes.c_void_p(1 << 40), None) == moe.MOE_ENOTSUP
+    assert qz(ctypes.c_void_p(1 << 40), moe.MOE_BF16, 1, 64, 128,
+              ctypes.c_void_p((1 << 40) + 4096), None) == moe.MOE_EINVAL   # overlapping buffers
+
+
+def test_int8_weights_share_the_bf16_rules():
+    f = lib.moe_expert_ffn
+    ws = moe.moe_workspace_bytes(4, 128, 256, 8, 2, moe.MOE_INT8_PACKED)
+    assert ws == moe.moe_workspace_bytes(4, 128, 256, 8, 2, moe.MOE_BF16)    # h is bf16 too
+    base = [BAD, moe.MOE_INT8_PACKED, BAD, BAD, BAD, BAD, BAD, 4, 128, 256, 8, 2, BAD, BAD, ws,
+            None]
+    bad_d = list(base)
+    bad_d[8] = 100
+    assert f(*bad_d) == moe.MOE_ENOTSUP
+    mis = list(base)
+    mis[0] = MISALIGNED
+    assert f(*mis) == moe.MOE_ENOTSUP
 
 
 def test_pack_weight_rejects_bad_arguments():

@@ -168,6 +168,77 @@ def test_block_forward_matches_oracle(m, name, variant):
     m.moe_set_ffn_variant(0)
 
 
+INT8_CASES = ["bf16_tiles", "bf16_ragged", "bf16_one_token", "bf16_skew", "bf16_E16_k4",
+              "bf16_E32_k1"]
+
+
+def _quantized(inp):
+    """The oracle's int8 codes and scales of w1, w3, w2 and the weights they stand for."""
+    out = {}
+    for name in ("w1", "w3", "w2"):
+        q, s = oracle.quantize_int8(inp[name])
+        out[name] = (q, s, oracle.dequantize_int8(q, s))
+    return out
+
+
+def test_int8_quantizer_matches_oracle(m):
+    """Codes and scales bit-exact against the oracle (both decide in float32),
+    including an all-zero row, a row with halfway cases and the largest |q|."""
+    print("[parity] int8 quantizer", flush=True)
+    rng = np.random.default_rng(13)
+    w = (rng.standard_normal((3, 48, 192)) * 0.03).astype(np.float32)
+    w[1, 5, :] = 0.0
+    w[2, 7, :4] = [127.0, -63.5, 0.5, 1.0]
+    w[2, 7, 4:] = 0.25
+    bits = gen.f32_to_bf16_bits(w)
+    wt = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    qm = m.moe_quantize_weight(wt)
+    torch.cuda.synchronize()
+    q, sc = oracle.quantize_int8(bits)
+    assert np.array_equal(qm.scales().cpu().numpy(), sc)
+    assert np.array_equal(qm.codes().cpu().numpy(), q)
+    assert m.load().moe_quantized_weight_bytes(3, 48, 192) == qm.blob.numel()
+
+
+@pytest.mark.parametrize("name", INT8_CASES)
+def test_int8_forward_matches_oracle(m, name):
+    """The layer on int8 weights (codes and scales from the device quantizer)
+    against the oracle computing with its own dequantized weights, under the
+    plain layer's rules; the expert step alone too, and the block."""
+    cfg = dict(SMALL)[name]
+    print(f"[parity] int8 {name}", flush=True)
+    inp = gen.make_inputs(**cfg)
+    dev = to_device(inp)
+    T, E, k = inp["T"], inp["E"], inp["k"]
+    qw = m.QuantizedWeights(dev["w1"], dev["w3"], dev["w2"])
+    deq = _quantized(inp)
+    ref_inp = dict(inp, w1=deq["w1"][2], w3=deq["w3"][2], w2=deq["w2"][2])
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    out = m.moe_forward(dev["x"], dev["router"], qw.w1, qw.w3, qw.w2, k, logit_bias=dev["bias"],
+                        out_dtype=torch.float32, topk_idx_out=idx, topk_w_out=w)
+    counts, offsets, sasg, apos = m.moe_permute(idx, E)
+    y = m.moe_expert_ffn(dev["x"], qw.w1, qw.w3, qw.w2, offsets, sasg, k)
+    torch.cuda.synchronize()
+    logits64 = oracle.router_logits(inp["x"], inp["router"], inp["bias"])
+    idx_g = host(idx)
+    check_routing(logits64, k, idx_g, host(w))
+    y_ref = oracle.expert_ffn(inp["x"], ref_inp["w1"], ref_inp["w3"], ref_inp["w2"],
+                              host(offsets), host(sasg), k)
+    assert rel_err(host(y), y_ref) <= OUT_TOL[gen.BF16]
+    ref = expected_output(ref_inp, idx_g, None, np.arange(T), logits64)
+    assert rel_err(host(out), ref) <= OUT_TOL[gen.BF16]
+    # the block on int8 weights: same kernels after the norm
+    gamma = gen.make_norm_weight(inp["d"], seed=inp["seed"])
+    g_t = torch.from_numpy(gamma).cuda()
+    out_b, nrm = m.moe_block_forward(dev["x"], g_t, dev["router"], qw.w1, qw.w3, qw.w2, k,
+                                     logit_bias=dev["bias"], out_dtype=torch.float32)
+    out_f = m.moe_forward(nrm, dev["router"], qw.w1, qw.w3, qw.w2, k, logit_bias=dev["bias"],
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(out_b, out_f + dev["x"].float())
+
+
 def _pack_reference(w):
     """Fragment order as include/moe.h defines it, by plain index arithmetic."""
     E, R, C = w.shape
