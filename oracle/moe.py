@@ -292,7 +292,11 @@ def quantize_int8(w):
     decides them (correctly rounded division), so the two agree exactly.
     Returns (q int8, scale float32 [..., rows]).
     """
-    wf = widen(w).astype(np.float32)  # bfloat16 and float32 inputs are exact here
+    a = np.asarray(w)
+    if a.dtype in (np.uint16, np.int16):  # bfloat16 bits -> float32, exactly
+        wf = (a.view(np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    else:
+        wf = a.astype(np.float32)
     amax = np.abs(wf).max(axis=-1)
     scale = (amax / np.float32(127.0)).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):

@@ -417,3 +417,76 @@ def test_full_size_workload(m, name):
     assert torch.equal(out_p, out)
     assert np.array_equal(out_b.view(torch.int16).cpu().numpy().view(np.uint16),
                           gen.f32_to_bf16_bits(out.cpu().numpy()))
+
+
+def _tokens_output_int8(x, qs, idx, w, tokens):
+    """oracle.tokens_output with each expert's weights dequantized one expert at
+    a time from the oracle's own int8 codes and scales (full-size memory)."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    idx = np.asarray(idx)[tokens]
+    w = np.asarray(w, dtype=np.float64)[tokens]
+    xs = oracle.widen(np.asarray(x)[tokens])
+    out = np.zeros_like(xs)
+    E = qs["w1"][0].shape[0]
+    for e in range(E):
+        sel_t, sel_j = np.nonzero(idx == e)
+        if sel_t.size == 0:
+            continue
+        we = [oracle.dequantize_int8(qs[n][0][e], qs[n][1][e]) for n in ("w1", "w3", "w2")]
+        ye = oracle.swiglu(xs[sel_t], *we)
+        for r in range(sel_t.size):
+            out[sel_t[r]] += w[sel_t[r], sel_j[r]] * ye[r]
+    return out
+
+
+@pytest.mark.slow
+def test_full_size_decode_int8_and_block(m):
+    """Decode 8x7B shape: int8 weights (codes bit-exact, sampled outputs against
+    the oracle's dequantized weights) and the block (normed rows, routing on
+    them, sampled outputs), in the configurations the benchmark times."""
+    print("[parity] full-size decode_8x7b int8 + block", flush=True)
+    m.moe_set_ffn_variant(0)
+    inp = gen.make_config("decode_8x7b")
+    dev = to_device(inp)
+    T, E, k, d = inp["T"], inp["E"], inp["k"], inp["d"]
+    qw = m.QuantizedWeights(dev["w1"], dev["w3"], dev["w2"])
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    out = m.moe_forward(dev["x"], dev["router"], qw.w1, qw.w3, qw.w2, k, out_dtype=torch.float32,
+                        topk_idx_out=idx, topk_w_out=w)
+    torch.cuda.synchronize()
+    qs = {n: oracle.quantize_int8(inp[n]) for n in ("w1", "w3", "w2")}
+    for n, qm in (("w1", qw.w1), ("w3", qw.w3), ("w2", qw.w2)):
+        assert np.array_equal(qm.scales().cpu().numpy(), qs[n][1])
+        assert np.array_equal(qm.codes().cpu().numpy(), qs[n][0])
+    logits64 = oracle.router_logits(inp["x"], inp["router"], inp["bias"])
+    idx_g = host(idx)
+    near, _ = check_routing(logits64, k, idx_g, host(w))
+    idx_use = oracle.select_topk(logits64, k)
+    idx_use[near] = idx_g[near]
+    w_use = oracle.renormalised_weights_for(logits64, idx_use)
+    tokens = np.arange(T)
+    ref = _tokens_output_int8(inp["x"], qs, idx_use, w_use, tokens)
+    err = rel_err(host(out), ref)
+    print(f"[parity] int8 decode: max|err|/rms={err:.3e}", flush=True)
+    assert err <= OUT_TOL[gen.BF16]
+    del qw, qs
+    # the block with the bf16 weights in fragment order
+    gamma = gen.make_norm_weight(d, seed=inp["seed"])
+    pw = m.PackedWeights(dev["w1"], dev["w3"], dev["w2"])
+    out_b, nrm = m.moe_block_forward(dev["x"], torch.from_numpy(gamma).cuda(), dev["router"],
+                                     pw.w1, pw.w3, pw.w2, k, out_dtype=torch.float32,
+                                     topk_idx_out=idx, topk_w_out=w, packed=True)
+    torch.cuda.synchronize()
+    n_ref = oracle.rms_norm(inp["x"], gamma, 1e-5)
+    n_gpu = host(nrm)
+    assert (np.abs(n_gpu - n_ref) <= bf16_half_ulp(n_ref) + 2.0 ** -20 * np.abs(n_ref)).all()
+    n_bits = nrm.view(torch.int16).cpu().numpy().view(np.uint16)
+    logits_n = oracle.router_logits(n_bits, inp["router"], inp["bias"])
+    idx_b = host(idx)
+    check_routing(logits_n, k, idx_b, host(w))
+    mlp_ref = expected_output(dict(inp, x=n_bits), idx_b, None, tokens, logits_n)
+    mlp_gpu = host(out_b).astype(np.float64) - oracle.widen(inp["x"])
+    err_b = rel_err(mlp_gpu, mlp_ref)
+    print(f"[parity] block decode: max|err|/rms={err_b:.3e}", flush=True)
+    assert err_b <= OUT_TOL[gen.BF16]
