@@ -9,7 +9,9 @@ untimed steps run first, then exactly K steps are timed between two device
 synchronisations. Consecutive steps alternate between two copies of the
 expert weights, so no step can find the previous step's weights in the
 256 MB Infinity Cache. Per-kernel times come from HIP events the library
-records on its stream between the stages.
+records on its stream between the stages, on every 4th timed step (an event
+record leaves the GPU idle for a few microseconds, so recording them on every
+step would slow the decode step by about 5%).
 
 By default the expert weights are held in fragment order (moe_pack_weight,
 run once when the weights are loaded, outside the timed region); the rate
@@ -39,6 +41,7 @@ METRIC = ("MoE-layer tokens/sec at 1 GPU; % of HBM BW peak (decode) / bf16 MFMA 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 STAGES = ("route", "permute", "gate_up", "down", "combine")
+EVENT_EVERY = 4  # timed steps between two steps that record the per-stage HIP events
 # the gate/up kernels' sources: traffic counters are only reported while they are unchanged
 FFN_SOURCES = [os.path.join(ROOT, "sparse_mixture_experts_06_amd", "csrc", f)
                for f in ("ffn_bf16.hip", "ffn_dma.hip", "ffn_int8.hip", "common.h")]
@@ -318,8 +321,7 @@ def main():
 
     def step(i, use_sets, is_packed, events=None):
         s = use_sets[i % 2]
-        if events is not None:
-            moe.moe_set_stage_events(events)
+        moe.moe_set_stage_events(events)
         if args.block:
             moe.moe_block_forward(s["x"], g_dev, s["router"], s["w1"], s["w3"], s["w2"], k,
                                   eps=1e-5, logit_bias=s["bias"], out=out, norm_out=norm_out,
@@ -339,17 +341,21 @@ def main():
     for i in range(args.warmup):
         step(i, sets, packed)
     torch.cuda.synchronize()
-    evs = [[hip.event() for _ in range(6)] for _ in range(args.steps)]
+    # stage events on every EVENT_EVERY-th timed step: each event record makes the
+    # GPU idle a few microseconds between kernels, so recording all six on
+    # every step would itself slow the step down by about 5% at decode
+    ev_steps = list(range(0, args.steps, EVENT_EVERY))
+    evs = {i: [hip.event() for _ in range(6)] for i in ev_steps}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, sets, packed, evs[i])
+        step(i, sets, packed, evs.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     moe.moe_set_stage_events(None)
-    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs]))
+    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs.values()]))
                 for j, name in enumerate(STAGES)}
-    for e in evs:
+    for e in evs.values():
         for ev in e:
             hip.destroy(ev)
 
