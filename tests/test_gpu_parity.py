@@ -490,3 +490,39 @@ def test_full_size_decode_int8_and_block(m):
     err_b = rel_err(mlp_gpu, mlp_ref)
     print(f"[parity] block decode: max|err|/rms={err_b:.3e}", flush=True)
     assert err_b <= OUT_TOL[gen.BF16]
+
+
+@pytest.mark.slow
+def test_large_batch_crosses_the_31_bit_offsets(m):
+    """8x7B shapes at T = 40960 (A = 81920): h is 2.35 GB, so the down
+    projection's byte offsets no longer fit the direct-to-LDS kernels' 31-bit
+    buffer offsets and it runs on the 128-row kernel, while gate/up (x is
+    335 MB) stays on the 256-row kernel. Routing and permutation on every
+    token, outputs on sampled tokens including the last rows."""
+    print("[parity] large batch T=40960", flush=True)
+    m.moe_set_ffn_variant(0)
+    inp = gen.make_config("prefill_8x7b", T=40960)
+    dev = to_device(inp)
+    T, E, k = inp["T"], inp["E"], inp["k"]
+    assert T * k * inp["ffn"] * 2 > 2 ** 31 - 1
+    pw = m.PackedWeights(dev["w1"], dev["w3"], dev["w2"])
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    out = m.moe_forward(dev["x"], dev["router"], pw.w1, pw.w3, pw.w2, k, logit_bias=dev["bias"],
+                        out_dtype=torch.float32, topk_idx_out=idx, topk_w_out=w,
+                        counts_out=counts, packed=True)
+    c2, o2, s2, p2 = m.moe_permute(idx, E)
+    torch.cuda.synchronize()
+    logits64 = oracle.router_logits(inp["x"], inp["router"], inp["bias"])
+    idx_g = host(idx)
+    near, _ = check_routing(logits64, k, idx_g, host(w))
+    check_permutation(idx_g, E, host(c2), host(o2), host(s2), host(p2))
+    assert np.array_equal(host(counts), host(c2))
+    rng = np.random.default_rng(4321)
+    tokens = np.unique(np.concatenate([rng.choice(T, size=48, replace=False),
+                                       np.arange(T - 8, T), [0]]))
+    ref = expected_output(inp, idx_g, None, tokens, logits64)
+    err = rel_err(host(out)[tokens], ref)
+    print(f"[parity] large batch: counts={host(counts).tolist()} max|err|/rms={err:.3e}", flush=True)
+    assert err <= OUT_TOL[gen.BF16]
