@@ -111,18 +111,20 @@ hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const u
                             hipStream_t s);
 int down_splits(int variant, int64_t A, int d, int ffn, int E);
 
-// gate/up and down for many rows per expert with fragment-order weights and
-// direct-to-LDS loads (ffn_dma.hip): the sizes they are used for, the K split
-// of the down projection (1 or 2) and the launchers
+// gate/up and down for many rows per expert with direct-to-LDS loads
+// (ffn_dma.hip), for fragment-order (packed) or row-major weights: the sizes
+// they are used for, the K split of the down projection (1 or 2) and the
+// launchers
 bool dma_gate_up_ok(int64_t A, int k, int d, int ffn, int E);
-hipError_t launch_gate_up_dma(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
-                              const int32_t* offsets, const int32_t* sorted_asg, int64_t A, int d,
-                              int ffn, int E, int k, uint16_t* h, hipStream_t s);
+hipError_t launch_gate_up_dma(bool packed, const uint16_t* x, const uint16_t* w1,
+                              const uint16_t* w3, const int32_t* offsets,
+                              const int32_t* sorted_asg, int64_t A, int d, int ffn, int E, int k,
+                              uint16_t* h, hipStream_t s);
 bool dma_down_ok(int64_t A, int d, int ffn, int E);
 int dma_down_splits(int64_t A, int d, int ffn, int E);
-hipError_t launch_down_dma(const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
-                           int64_t A, int d, int ffn, int E, int nsplit, float* part,
-                           hipStream_t s);
+hipError_t launch_down_dma(bool packed, const uint16_t* h, const uint16_t* w2,
+                           const int32_t* offsets, int64_t A, int d, int ffn, int E, int nsplit,
+                           float* part, hipStream_t s);
 // weight-only int8 experts (ffn_int8.hip): bytes of one quantized matrix
 // (codes, then float32 row scales at the next 256-byte boundary), the
 // quantizer, and the streaming gate/up and down kernels that read it

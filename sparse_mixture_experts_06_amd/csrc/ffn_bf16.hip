@@ -747,8 +747,8 @@ hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, cons
       hipLaunchKernelGGL((gate_up_stream_kernel<kGateUpRT, kGateUpU, PACKED, kStreamNT<PACKED>>),
                          dim3(ffn / rows, E), dim3(kWave * kStreamWaves), 0, s, x, w1, w3,
                          offsets, sorted_asg, d, ffn, k, h);
-  } else if (PACKED && dma_gate_up_ok(A, k, d, ffn, E)) {
-    return launch_gate_up_dma(x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s);
+  } else if (dma_gate_up_ok(A, k, d, ffn, E)) {
+    return launch_gate_up_dma(PACKED, x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s);
   } else if (PACKED && ffn % 128 == 0) {
     const int ntn = ffn / 128;
     hipLaunchKernelGGL((wtiled_kernel<true, PACKED, kWRing, kWOcc, kWXSets>), dim3(tiled_grid(A, E, ntn)),
@@ -782,8 +782,8 @@ hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const i
                          dim3(kWave * kStreamWaves), 0, s, h, w2, offsets, ffn, d,
                          static_cast<int>(A), nsplit, part);
     }
-  } else if (PACKED && dma_down_ok(A, d, ffn, E)) {
-    return launch_down_dma(h, w2, offsets, A, d, ffn, E, nsplit, part, s);
+  } else if (dma_down_ok(A, d, ffn, E)) {
+    return launch_down_dma(PACKED, h, w2, offsets, A, d, ffn, E, nsplit, part, s);
   } else if (PACKED && d % 256 == 0 && nsplit == 1) {
     const int ntn = d / 256;
     hipLaunchKernelGGL((wtiled_kernel<false, PACKED, kWRing, kWOcc, kWXSets>), dim3(tiled_grid(A, E, ntn)),

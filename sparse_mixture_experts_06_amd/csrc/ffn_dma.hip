@@ -1,5 +1,5 @@
-// Expert projections for many rows per expert (prefill) with fragment-order
-// weights: both grouped GEMMs of the Mixtral sparse-MoE block (nnterp Mixtral
+// Expert projections for many rows per expert (prefill), with fragment-order
+// or row-major weights: both grouped GEMMs of the Mixtral sparse-MoE block (nnterp Mixtral
 // page, support(): the down projection receives act(gate) * up with act =
 // SiLU; the experts are one stacked module), the first fused with that
 // activation, as in ffn_bf16.hip:
@@ -47,6 +47,15 @@
 // token fragments that hold a row (rounded up to an even count; a template
 // parameter, so the loop stays branch-free), and still issues all loads and
 // barriers with the other waves.
+//
+// Row-major weights (template parameter PACKED false): the weight rows are
+// staged exactly as the token rows are (8 rows x 128 bytes per load, two
+// swizzled 32 KiB K64 stages, loads of stage (t+3)/2 in odd steps t, after
+// the token loads), and the weight fragments are read like the token
+// fragments; the only waits are "vmcnt <= 0" in odd steps and none in even
+// steps (the whole stage is in hand), plus the barrier. The MFMAs, their
+// operands and their order are those of the fragment-order kernel, so the
+// results of the two layouts are identical.
 //
 // Every output element is one float32 MFMA accumulation over its K range in
 // increasing K, 32 at a time: the order of the 128-row tiled kernels, whose
@@ -117,7 +126,7 @@ __device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offse
 // !GATE_UP: act = h [act_rows = A, K = ffn] bf16 in grouped order, wa = w2 in
 // fragment order [E, N = d, ffn], out = part [nsplit][A][d] float32, the
 // partial arrays pstride floats apart.
-template <bool GATE_UP>
+template <bool GATE_UP, bool PACKED>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64_t act_rows,
                                          const uint16_t* __restrict__ wa,
                                          const uint16_t* __restrict__ wb,
@@ -130,10 +139,13 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
 
   // one array per buffer: distinct objects let the compiler see that a
   // fragment read does not depend on the loads in flight to other buffers
-  __shared__ __attribute__((aligned(1024))) uint16_t wb0[kWBufE];
-  __shared__ __attribute__((aligned(1024))) uint16_t wb1[kWBufE];
-  __shared__ __attribute__((aligned(1024))) uint16_t wb2[kWBufE];
-  __shared__ __attribute__((aligned(1024))) uint16_t wb3[kWBufE];
+  // (fragment order: four K32 weight buffers; row-major: two K64 weight stages)
+  constexpr int kWB01 = PACKED ? kWBufE : kTBufE;
+  constexpr int kWB23 = PACKED ? kWBufE : 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t wb0[kWB01];
+  __shared__ __attribute__((aligned(1024))) uint16_t wb1[kWB01];
+  __shared__ __attribute__((aligned(1024))) uint16_t wb2[kWB23];
+  __shared__ __attribute__((aligned(1024))) uint16_t wb3[kWB23];
   __shared__ __attribute__((aligned(1024))) uint16_t tb0[kTBufE];
   __shared__ __attribute__((aligned(1024))) uint16_t tb1[kTBufE];
   auto wbufp = [&](auto bi) -> uint16_t* {
@@ -165,11 +177,22 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
       const_cast<uint16_t*>(wsrc + e * wslice), 0, static_cast<int>(wslice * 2), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(act), 0, static_cast<int>(act_rows * K * 2), kRsrcWord3);
-  int aoff[2];  // byte offsets of step 0 (wave-uniform)
+  int aoff[2];  // fragment order: byte offsets of step 0 (wave-uniform)
+  int woff[4];  // row-major: per-lane byte offsets of stage 0, placed as the token rows below
+  if constexpr (PACKED) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = GATE_UP ? nt * 128 + (w >> 1) * 32 + q * 16 : nt * 256 + (2 * w + q) * 16;
-    aoff[q] = __builtin_amdgcn_readfirstlane(static_cast<int>(wofs<true>(0, row, k0, N, K) * 2));
+    for (int q = 0; q < 2; ++q) {
+      const int row = GATE_UP ? nt * 128 + (w >> 1) * 32 + q * 16 : nt * 256 + (2 * w + q) * 16;
+      aoff[q] = __builtin_amdgcn_readfirstlane(static_cast<int>(wofs<true>(0, row, k0, N, K) * 2));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 32 * w + 8 * q + (lane >> 3);  // LDS row = 16 * fragment + fragment row
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int row = GATE_UP ? nt * 128 + (w >> 1) * 32 + 8 * q + (lane >> 3) : nt * 256 + r;
+      woff[q] = (row * K + k0 + c * 8) * 2;
+    }
   }
   // token loads: wave w moves tile rows 32w .. 32w+31, 8 rows x 128 B per load; lane l puts row
   // 32w + 8q + l/8, LDS slot l%8, which holds 16-byte chunk (l%8) ^ ((row/2) % 8) of the K64 stage
@@ -194,6 +217,10 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_ptr)(L + (32 * w + 8 * q) * 64), 16, toff[q],
                                              s * 128, 0, 0);
   };
+  auto load_ws = [&](uint16_t* L, int q, int s) {  // row-major weights, K64 stage s
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr)(L + (32 * w + 8 * q) * 64), 16, woff[q],
+                                             s * 128, 0, 0);
+  };
   // prologue: the loads steps -4 .. -1 would have issued in the steady state
   // (weights of steps 0-3, token stages 0-1; odd steps tokens first), so the
   // loop's wait counts hold from its first step
@@ -201,13 +228,22 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  load_w(wbufp(I0{}), 0, 0); load_w(wbufp(I0{}), 1, 0);
-  load_x(tbufp(I0{}), 0, 0); load_x(tbufp(I0{}), 1, 0); load_x(tbufp(I0{}), 2, 0); load_x(tbufp(I0{}), 3, 0);
-  load_w(wbufp(I1{}), 0, min(1, last)); load_w(wbufp(I1{}), 1, min(1, last));
-  load_w(wbufp(I2{}), 0, min(2, last)); load_w(wbufp(I2{}), 1, min(2, last));
-  load_x(tbufp(I1{}), 0, min(1, last_stage)); load_x(tbufp(I1{}), 1, min(1, last_stage));
-  load_x(tbufp(I1{}), 2, min(1, last_stage)); load_x(tbufp(I1{}), 3, min(1, last_stage));
-  load_w(wbufp(I3{}), 0, min(3, last)); load_w(wbufp(I3{}), 1, min(3, last));
+  // (row-major weights: both stages of both operands, stage by stage)
+  if constexpr (PACKED) {
+    load_w(wbufp(I0{}), 0, 0); load_w(wbufp(I0{}), 1, 0);
+    load_x(tbufp(I0{}), 0, 0); load_x(tbufp(I0{}), 1, 0); load_x(tbufp(I0{}), 2, 0); load_x(tbufp(I0{}), 3, 0);
+    load_w(wbufp(I1{}), 0, min(1, last)); load_w(wbufp(I1{}), 1, min(1, last));
+    load_w(wbufp(I2{}), 0, min(2, last)); load_w(wbufp(I2{}), 1, min(2, last));
+    load_x(tbufp(I1{}), 0, min(1, last_stage)); load_x(tbufp(I1{}), 1, min(1, last_stage));
+    load_x(tbufp(I1{}), 2, min(1, last_stage)); load_x(tbufp(I1{}), 3, min(1, last_stage));
+    load_w(wbufp(I3{}), 0, min(3, last)); load_w(wbufp(I3{}), 1, min(3, last));
+  } else {
+    const int s1 = min(1, last_stage);
+    load_x(tbufp(I0{}), 0, 0); load_x(tbufp(I0{}), 1, 0); load_x(tbufp(I0{}), 2, 0); load_x(tbufp(I0{}), 3, 0);
+    load_ws(wbufp(I0{}), 0, 0); load_ws(wbufp(I0{}), 1, 0); load_ws(wbufp(I0{}), 2, 0); load_ws(wbufp(I0{}), 3, 0);
+    load_x(tbufp(I1{}), 0, s1); load_x(tbufp(I1{}), 1, s1); load_x(tbufp(I1{}), 2, s1); load_x(tbufp(I1{}), 3, s1);
+    load_ws(wbufp(I1{}), 0, s1); load_ws(wbufp(I1{}), 1, s1); load_ws(wbufp(I1{}), 2, s1); load_ws(wbufp(I1{}), 3, s1);
+  }
 
   // fragments of this wave's token tiles that hold a row, rounded up to even
   const int valid = M - m0 - wm * 128;
@@ -216,6 +252,8 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   const int trow = (wm * 128 + fr) * 64;
   const int tcol0 = ((fg) ^ ((fr >> 1) & 7)) * 8;
   const int tcol1 = ((4 + fg) ^ ((fr >> 1) & 7)) * 8;
+  // row-major weight fragment reads: row (wn*64 + 16k + fr), same chunks and slots
+  const int wrow = (wn * 64 + fr) * 64;
 
   auto run = [&](auto jvc) {
     constexpr int JV = decltype(jvc)::value;
@@ -231,13 +269,17 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
       constexpr int S = decltype(si)::value;
       constexpr int HH = decltype(hh)::value;
       if (k < 4) {
-        fa[S][k] = *reinterpret_cast<const u32x4*>(wbufp(wi) + (wn * 4 + k) * kFragE + lane * 8);
+        if constexpr (PACKED)
+          fa[S][k] = *reinterpret_cast<const u32x4*>(wbufp(wi) + (wn * 4 + k) * kFragE + lane * 8);
+        else
+          fa[S][k] = *reinterpret_cast<const u32x4*>(wbufp(ti) + wrow + k * 16 * 64 + (HH ? tcol1 : tcol0));
       } else if (k - 4 < JV) {
         const uint16_t* TL = tbufp(ti);
         fb[S][k - 4] = *reinterpret_cast<const u32x4*>(TL + trow + (k - 4) * 16 * 64 + (HH ? tcol1 : tcol0));
       }
     };
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(10));  // weights of step 0 and token stage 0
+    // weights of step 0 and token stage 0 (row-major: stage 0 of both)
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(PACKED ? 10 : 8));
     lds_barrier();
 #pragma unroll
     for (int k = 0; k < 12; ++k) rd(I0{}, I0{}, I0{}, I0{}, k);
@@ -255,7 +297,9 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
       // stage (issued in step t-2 for odd t, t-3 for even t; counted from the
       // issue order above); the barrier publishes step t+1 and frees the
       // buffers step t was read from (it is in registers)
-      __builtin_amdgcn_s_waitcnt(vmcnt_le((T & 1) ? 4 : 8));
+      // (row-major weights: step t+1 of an odd step t is stage (t+1)/2 of
+      // both operands, whose loads went out in step t-2 with none since)
+      __builtin_amdgcn_s_waitcnt(vmcnt_le((T & 1) ? (PACKED ? 4 : 0) : 8));
       lds_barrier();
       const int tw = min(t + 4, last);
       const int ts = min((t + 3) >> 1, last_stage);
@@ -275,11 +319,12 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
           }, std::make_integer_sequence<int, 3>{});
           if constexpr (T & 1) {
             // tokens of stage (t+3)/2 into the buffer stage (t-1)/2 has left,
-            // then the weights of step t+4
+            // then the weights of step t+4 (row-major: of stage (t+3)/2)
             using TB = std::integral_constant<int, ((T + 3) >> 1) & 1>;
             if constexpr (g < 2) { load_x(tbufp(TB{}), 2 * g, ts); load_x(tbufp(TB{}), 2 * g + 1, ts); }
-            else load_w(wbufp(tm), g - 2, tw);
-          } else {
+            else if constexpr (PACKED) load_w(wbufp(tm), g - 2, tw);
+            else { load_ws(wbufp(TB{}), 2 * g - 4, ts); load_ws(wbufp(TB{}), 2 * g - 3, ts); }
+          } else if constexpr (PACKED) {
             if constexpr (g < 2) load_w(wbufp(tm), g, tw);
           }
         }
@@ -328,21 +373,23 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   }
 }
 
-// x [T, d] bf16, w1/w3 fragment order [E, ffn, d], h [A, ffn] bf16
+// x [T, d] bf16, w1/w3 [E, ffn, d] (fragment order or row-major), h [A, ffn] bf16
+template <bool PACKED>
 __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
     const uint16_t* __restrict__ x, int64_t T, const uint16_t* __restrict__ w1,
     const uint16_t* __restrict__ w3, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_asg, int d, int ffn, int E, int ktop,
     uint16_t* __restrict__ h, int ntn) {
-  dma_tile<true>(x, T, w1, w3, offsets, sorted_asg, d, ffn, E, ktop, h, ntn, 1, 0);
+  dma_tile<true, PACKED>(x, T, w1, w3, offsets, sorted_asg, d, ffn, E, ktop, h, ntn, 1, 0);
 }
 
-// h [A, ffn] bf16 grouped, w2 fragment order [E, d, ffn], part [nsplit, A, d] f32
+// h [A, ffn] bf16 grouped, w2 [E, d, ffn] (fragment order or row-major), part [nsplit, A, d] f32
+template <bool PACKED>
 __global__ __launch_bounds__(kDmaThreads, 1) void down_dma_kernel(
     const uint16_t* __restrict__ h, int64_t A, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ offsets, int d, int ffn, int E, float* __restrict__ part, int ntn,
     int nsplit) {
-  dma_tile<false>(h, A, w2, w2, offsets, nullptr, ffn, d, E, 1, part, ntn, nsplit, A * d);
+  dma_tile<false, PACKED>(h, A, w2, w2, offsets, nullptr, ffn, d, E, 1, part, ntn, nsplit, A * d);
 }
 
 constexpr int64_t kMax31 = (int64_t(1) << 31) - 1;
@@ -360,14 +407,19 @@ bool dma_gate_up_ok(int64_t A, int k, int d, int ffn, int E) {
   return static_cast<int64_t>(ffn) * d * 2 <= kMax31 && (A / k) * d * 2 <= kMax31;
 }
 
-hipError_t launch_gate_up_dma(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
-                              const int32_t* offsets, const int32_t* sorted_asg, int64_t A, int d,
-                              int ffn, int E, int k, uint16_t* h, hipStream_t s) {
+hipError_t launch_gate_up_dma(bool packed, const uint16_t* x, const uint16_t* w1,
+                              const uint16_t* w3, const int32_t* offsets,
+                              const int32_t* sorted_asg, int64_t A, int d, int ffn, int E, int k,
+                              uint16_t* h, hipStream_t s) {
   const int ntn = ffn / 128;
   const int64_t tiles = ((A + DT - 1) / DT + E) * ntn;  // upper bound
-  hipLaunchKernelGGL(gate_up_dma_kernel, dim3(static_cast<unsigned>((tiles + 7) / 8 * 8)),
-                     dim3(kDmaThreads), 0, s, x, A / k, w1, w3, offsets, sorted_asg, d, ffn, E, k,
-                     h, ntn);
+  const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8));
+  if (packed)
+    hipLaunchKernelGGL(gate_up_dma_kernel<true>, grid, dim3(kDmaThreads), 0, s, x, A / k, w1, w3,
+                       offsets, sorted_asg, d, ffn, E, k, h, ntn);
+  else
+    hipLaunchKernelGGL(gate_up_dma_kernel<false>, grid, dim3(kDmaThreads), 0, s, x, A / k, w1, w3,
+                       offsets, sorted_asg, d, ffn, E, k, h, ntn);
   return hipGetLastError();
 }
 
@@ -391,13 +443,18 @@ int dma_down_splits(int64_t A, int d, int ffn, int E) {
   return 10 * r2 <= 9 * 2 * r1 ? 2 : 1;
 }
 
-hipError_t launch_down_dma(const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
-                           int64_t A, int d, int ffn, int E, int nsplit, float* part,
-                           hipStream_t s) {
+hipError_t launch_down_dma(bool packed, const uint16_t* h, const uint16_t* w2,
+                           const int32_t* offsets, int64_t A, int d, int ffn, int E, int nsplit,
+                           float* part, hipStream_t s) {
   const int ntn = d / 256;
   const int64_t tiles = ((A + DT - 1) / DT + E) * ntn * nsplit;  // upper bound
-  hipLaunchKernelGGL(down_dma_kernel, dim3(static_cast<unsigned>((tiles + 7) / 8 * 8)),
-                     dim3(kDmaThreads), 0, s, h, A, w2, offsets, d, ffn, E, part, ntn, nsplit);
+  const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8));
+  if (packed)
+    hipLaunchKernelGGL(down_dma_kernel<true>, grid, dim3(kDmaThreads), 0, s, h, A, w2, offsets, d,
+                       ffn, E, part, ntn, nsplit);
+  else
+    hipLaunchKernelGGL(down_dma_kernel<false>, grid, dim3(kDmaThreads), 0, s, h, A, w2, offsets, d,
+                       ffn, E, part, ntn, nsplit);
   return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@ properties of the generated gfx950 code, so they are checked there: every
 MFMA accumulates in place (destination = accumulator input), no accumulator
 is copied between register files inside the loop, nothing spills to scratch,
 and the only memory waits in the loop are the one per K step that the design
-calls for ("vmcnt <= 4" in odd steps, "<= 8" in even ones, together with the
-barrier's lgkmcnt(0)).
+calls for, together with the barrier's lgkmcnt(0): "vmcnt <= 4" in odd steps
+and "<= 8" in even ones with fragment-order weights, "vmcnt <= 0" in odd steps
+and "<= 8" (no wait) in even ones with row-major weights.
 """
 import os
 import re
@@ -60,15 +61,22 @@ def _kernels(text):
     return out
 
 
-def test_both_kernels_are_present(asm):
+# template argument PACKED: fragment-order (b1) or row-major (b0) weights
+LAYOUTS = {"packed": ("ILb1E", 4), "row_major": ("ILb0E", 0)}
+
+
+def test_all_kernels_are_present(asm):
     names = list(_kernels(asm))
-    assert any("gate_up_dma_kernel" in n for n in names), names
-    assert any("down_dma_kernel" in n for n in names), names
+    for kernel in ("gate_up_dma_kernel", "down_dma_kernel"):
+        for tag, _ in LAYOUTS.values():
+            assert any(kernel + tag in n for n in names), (kernel, tag, names)
 
 
+@pytest.mark.parametrize("layout", list(LAYOUTS))
 @pytest.mark.parametrize("kernel", ["gate_up_dma_kernel", "down_dma_kernel"])
-def test_loops_keep_accumulators_in_place(asm, kernel):
-    code = [c for n, c in _kernels(asm).items() if kernel in n]
+def test_loops_keep_accumulators_in_place(asm, kernel, layout):
+    tag, odd_wait = LAYOUTS[layout]
+    code = [c for n, c in _kernels(asm).items() if kernel + tag in n]
     assert len(code) == 1
     loops = _loops(code[0])
     # one loop per token-fragment count the kernel is instantiated for (8, 6, 4, 2)
@@ -80,9 +88,11 @@ def test_loops_keep_accumulators_in_place(asm, kernel):
         assert not untied, untied[:3]
         assert not [b for b in body if "accvgpr" in b]
         waits = {re.sub(r"\s+", " ", b.strip()) for b in body if "s_waitcnt" in b}
-        assert waits == {"s_waitcnt vmcnt(4) lgkmcnt(0)", "s_waitcnt vmcnt(8) lgkmcnt(0)"}, waits
-        assert sum("vmcnt(4)" in b for b in body) == 2 and sum("vmcnt(8)" in b for b in body) == 2
-        # four K steps per loop trip: 2 weight loads each, 4 token loads in the two odd ones
+        odd = f"vmcnt({odd_wait})"
+        assert waits == {f"s_waitcnt {odd} lgkmcnt(0)", "s_waitcnt vmcnt(8) lgkmcnt(0)"}, waits
+        assert sum(odd in b for b in body) == 2 and sum("vmcnt(8)" in b for b in body) == 2
+        # four K steps per loop trip: fragment order, 2 weight loads each and 4 token loads in
+        # the two odd ones; row-major, 4 token and 4 weight loads in the two odd ones
         assert sum("buffer_load_dwordx4" in b and " lds" in b for b in body) == 16
 
 

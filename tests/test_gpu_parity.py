@@ -337,16 +337,16 @@ def test_exact_logit_ties_pick_lower_index(m):
 
 @pytest.mark.parametrize("d,ffn", [(128, 256), (256, 128), (256, 256), (256, 512)])
 def test_prefill_tail_tiles(m, d, ffn):
-    """The 256x256-tile kernels (fragment-order weights, tiled family, used
-    once A >= 512 E: gate/up always, down when d % 256 == 0) on hand-made
+    """The 256x256-tile kernels (tiled family, used once A >= 512 E: gate/up
+    always, down when d % 256 == 0; fragment-order and row-major weights) on hand-made
     routing whose per-expert row counts leave last tiles holding 16, 48, 80,
     128, 130 and 250 rows (every token-fragment count the kernels specialise:
     2, 4, 6, 8 and 0 for the idle half), an empty expert and an exact multiple
     of 256; one or two unrolled trips of the K loops. With ffn % 256 == 0 and
     these few tiles the down projection splits K in two (the workspace holds
     the two partial arrays), otherwise it does not. Oracle within the bf16
-    bar, and bit-identical to the standard-layout kernels (same MFMA
-    sequence, same split)."""
+    bar, and the two weight layouts bit-identical (same MFMA sequence, same
+    split)."""
     counts = [784, 816, 848, 896, 898, 0, 1024, 1018]
     E, k = len(counts), 2
     A = sum(counts)
