@@ -49,13 +49,17 @@
 // barriers with the other waves.
 //
 // Row-major weights (template parameter PACKED false): the weight rows are
-// staged exactly as the token rows are (8 rows x 128 bytes per load, two
-// swizzled 32 KiB K64 stages, loads of stage (t+3)/2 in odd steps t, after
-// the token loads), and the weight fragments are read like the token
-// fragments; the only waits are "vmcnt <= 0" in odd steps and none in even
-// steps (the whole stage is in hand), plus the barrier. The MFMAs, their
-// operands and their order are those of the fragment-order kernel, so the
-// results of the two layouts are identical.
+// staged as the token rows are (8 rows x 128 bytes per load, swizzled 32 KiB
+// K64 stages) and the weight fragments are read like the token fragments.
+// Three weight stages (160 KiB of LDS in all): the loads of weight stage
+// (t+5)/2 go out in odd steps t after the token loads of stage (t+3)/2, four
+// steps of lead (with two stages, two steps of lead and a full drain per
+// stage measured 1-4% slower); the only waits are "vmcnt <= 4" in odd steps
+// and none in even ones, plus the barrier. The loop is unrolled over the 12
+// steps of a buffer cycle so that every buffer index is a constant; the 4 or
+// 8 steps left after the last whole cycle run with the first cycle's
+// indices. The MFMAs, their operands and their order are those of the
+// fragment-order kernel, so the results of the two layouts are identical.
 //
 // Every output element is one float32 MFMA accumulation over its K range in
 // increasing K, 32 at a time: the order of the 128-row tiled kernels, whose
@@ -139,13 +143,13 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
 
   // one array per buffer: distinct objects let the compiler see that a
   // fragment read does not depend on the loads in flight to other buffers
-  // (fragment order: four K32 weight buffers; row-major: two K64 weight stages)
-  constexpr int kWB01 = PACKED ? kWBufE : kTBufE;
-  constexpr int kWB23 = PACKED ? kWBufE : 8;
-  __shared__ __attribute__((aligned(1024))) uint16_t wb0[kWB01];
-  __shared__ __attribute__((aligned(1024))) uint16_t wb1[kWB01];
-  __shared__ __attribute__((aligned(1024))) uint16_t wb2[kWB23];
-  __shared__ __attribute__((aligned(1024))) uint16_t wb3[kWB23];
+  // (fragment order: four K32 weight buffers; row-major: three K64 weight stages)
+  constexpr int kWB012 = PACKED ? kWBufE : kTBufE;
+  constexpr int kWB3 = PACKED ? kWBufE : 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t wb0[kWB012];
+  __shared__ __attribute__((aligned(1024))) uint16_t wb1[kWB012];
+  __shared__ __attribute__((aligned(1024))) uint16_t wb2[kWB012];
+  __shared__ __attribute__((aligned(1024))) uint16_t wb3[kWB3];
   __shared__ __attribute__((aligned(1024))) uint16_t tb0[kTBufE];
   __shared__ __attribute__((aligned(1024))) uint16_t tb1[kTBufE];
   auto wbufp = [&](auto bi) -> uint16_t* {
@@ -178,7 +182,10 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(act), 0, static_cast<int>(act_rows * K * 2), kRsrcWord3);
   int aoff[2];  // fragment order: byte offsets of step 0 (wave-uniform)
-  int woff[4];  // row-major: per-lane byte offsets of stage 0, placed as the token rows below
+  // row-major: per-lane byte offsets of stage 0 for the loads q = 0, 2 and
+  // q = 1, 3 (rows placed as the token rows below; load q reads 8q rows
+  // further, a wave-uniform offset, and the swizzle slot depends on q % 2)
+  int woff[2];
   if constexpr (PACKED) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -187,7 +194,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       const int r = 32 * w + 8 * q + (lane >> 3);  // LDS row = 16 * fragment + fragment row
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       const int row = GATE_UP ? nt * 128 + (w >> 1) * 32 + 8 * q + (lane >> 3) : nt * 256 + r;
@@ -218,8 +225,8 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
                                              s * 128, 0, 0);
   };
   auto load_ws = [&](uint16_t* L, int q, int s) {  // row-major weights, K64 stage s
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr)(L + (32 * w + 8 * q) * 64), 16, woff[q],
-                                             s * 128, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr)(L + (32 * w + 8 * q) * 64), 16,
+                                             woff[q & 1], s * 128 + (q >> 1) * 16 * K * 2, 0, 0);
   };
   // prologue: the loads steps -4 .. -1 would have issued in the steady state
   // (weights of steps 0-3, token stages 0-1; odd steps tokens first), so the
@@ -228,7 +235,8 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  // (row-major weights: both stages of both operands, stage by stage)
+  // (row-major weights: weight stages 0-2 and token stages 0-1, in the order
+  // odd steps issue them, tokens of stage s with weights of stage s+1)
   if constexpr (PACKED) {
     load_w(wbufp(I0{}), 0, 0); load_w(wbufp(I0{}), 1, 0);
     load_x(tbufp(I0{}), 0, 0); load_x(tbufp(I0{}), 1, 0); load_x(tbufp(I0{}), 2, 0); load_x(tbufp(I0{}), 3, 0);
@@ -238,11 +246,12 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
     load_x(tbufp(I1{}), 2, min(1, last_stage)); load_x(tbufp(I1{}), 3, min(1, last_stage));
     load_w(wbufp(I3{}), 0, min(3, last)); load_w(wbufp(I3{}), 1, min(3, last));
   } else {
-    const int s1 = min(1, last_stage);
-    load_x(tbufp(I0{}), 0, 0); load_x(tbufp(I0{}), 1, 0); load_x(tbufp(I0{}), 2, 0); load_x(tbufp(I0{}), 3, 0);
+    const int s1 = min(1, last_stage), s2 = min(2, last_stage);
     load_ws(wbufp(I0{}), 0, 0); load_ws(wbufp(I0{}), 1, 0); load_ws(wbufp(I0{}), 2, 0); load_ws(wbufp(I0{}), 3, 0);
-    load_x(tbufp(I1{}), 0, s1); load_x(tbufp(I1{}), 1, s1); load_x(tbufp(I1{}), 2, s1); load_x(tbufp(I1{}), 3, s1);
+    load_x(tbufp(I0{}), 0, 0); load_x(tbufp(I0{}), 1, 0); load_x(tbufp(I0{}), 2, 0); load_x(tbufp(I0{}), 3, 0);
     load_ws(wbufp(I1{}), 0, s1); load_ws(wbufp(I1{}), 1, s1); load_ws(wbufp(I1{}), 2, s1); load_ws(wbufp(I1{}), 3, s1);
+    load_x(tbufp(I1{}), 0, s1); load_x(tbufp(I1{}), 1, s1); load_x(tbufp(I1{}), 2, s1); load_x(tbufp(I1{}), 3, s1);
+    load_ws(wbufp(I2{}), 0, s2); load_ws(wbufp(I2{}), 1, s2); load_ws(wbufp(I2{}), 2, s2); load_ws(wbufp(I2{}), 3, s2);
   }
 
   // fragments of this wave's token tiles that hold a row, rounded up to even
@@ -272,24 +281,25 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
         if constexpr (PACKED)
           fa[S][k] = *reinterpret_cast<const u32x4*>(wbufp(wi) + (wn * 4 + k) * kFragE + lane * 8);
         else
-          fa[S][k] = *reinterpret_cast<const u32x4*>(wbufp(ti) + wrow + k * 16 * 64 + (HH ? tcol1 : tcol0));
+          fa[S][k] = *reinterpret_cast<const u32x4*>(wbufp(wi) + wrow + k * 16 * 64 + (HH ? tcol1 : tcol0));
       } else if (k - 4 < JV) {
         const uint16_t* TL = tbufp(ti);
         fb[S][k - 4] = *reinterpret_cast<const u32x4*>(TL + trow + (k - 4) * 16 * 64 + (HH ? tcol1 : tcol0));
       }
     };
     // weights of step 0 and token stage 0 (row-major: stage 0 of both)
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(PACKED ? 10 : 8));
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(PACKED ? 10 : 12));
     lds_barrier();
 #pragma unroll
     for (int k = 0; k < 12; ++k) rd(I0{}, I0{}, I0{}, I0{}, k);
 
     int t0 = 0;
     auto step = [&](auto tm) {
-      // step t = t0 + T: weights in wbuf T, tokens in tbuf T/2 half T%2 (t0 % 4 == 0)
+      // step t = t0 + T: weights in wbuf T (row-major: wbuf (T/2) % 3), tokens
+      // in tbuf T/2 half T%2 (t0 % 4 == 0; row-major: t0 % 12 == 0)
       constexpr int T = decltype(tm)::value;
       constexpr int CUR = T & 1, NXT = CUR ^ 1;
-      using WN = std::integral_constant<int, (T + 1) & 3>;
+      using WN = std::integral_constant<int, PACKED ? (T + 1) & 3 : ((T + 1) >> 1) % 3>;
       using TN = std::integral_constant<int, ((T + 1) >> 1) & 1>;
       using HN = std::integral_constant<int, (T + 1) & 1>;
       const int t = t0 + T;
@@ -297,12 +307,14 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
       // stage (issued in step t-2 for odd t, t-3 for even t; counted from the
       // issue order above); the barrier publishes step t+1 and frees the
       // buffers step t was read from (it is in registers)
-      // (row-major weights: step t+1 of an odd step t is stage (t+1)/2 of
-      // both operands, whose loads went out in step t-2 with none since)
-      __builtin_amdgcn_s_waitcnt(vmcnt_le((T & 1) ? (PACKED ? 4 : 0) : 8));
+      // (row-major weights: step t+1 of an odd step t is stage (t+1)/2, whose
+      // tokens went out in step t-2 before the weights of stage (t+3)/2 and
+      // whose weights in step t-4; even steps need nothing new)
+      __builtin_amdgcn_s_waitcnt(vmcnt_le((T & 1) ? 4 : (PACKED ? 8 : 12)));
       lds_barrier();
       const int tw = min(t + 4, last);
       const int ts = min((t + 3) >> 1, last_stage);
+      const int ts5 = min((t + 5) >> 1, last_stage);
       unrolled([&](auto gm) {
         constexpr int g = decltype(gm)::value;
         constexpr int i = g >> 1, j0 = (g & 1) * 4;
@@ -319,11 +331,13 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
           }, std::make_integer_sequence<int, 3>{});
           if constexpr (T & 1) {
             // tokens of stage (t+3)/2 into the buffer stage (t-1)/2 has left,
-            // then the weights of step t+4 (row-major: of stage (t+3)/2)
+            // then the weights of step t+4 (row-major: of stage (t+5)/2, into
+            // the buffer stage (t-1)/2 has left)
             using TB = std::integral_constant<int, ((T + 3) >> 1) & 1>;
+            using WB = std::integral_constant<int, ((T + 5) >> 1) % 3>;
             if constexpr (g < 2) { load_x(tbufp(TB{}), 2 * g, ts); load_x(tbufp(TB{}), 2 * g + 1, ts); }
             else if constexpr (PACKED) load_w(wbufp(tm), g - 2, tw);
-            else { load_ws(wbufp(TB{}), 2 * g - 4, ts); load_ws(wbufp(TB{}), 2 * g - 3, ts); }
+            else { load_ws(wbufp(WB{}), 2 * g - 4, ts5); load_ws(wbufp(WB{}), 2 * g - 3, ts5); }
           } else if constexpr (PACKED) {
             if constexpr (g < 2) load_w(wbufp(tm), g, tw);
           }
@@ -331,7 +345,20 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
         __builtin_amdgcn_sched_barrier(0);
       }, std::make_integer_sequence<int, 8>{});
     };
-    for (; t0 < nsteps; t0 += 4) unrolled(step, std::make_integer_sequence<int, 4>{});
+    // unrolled over a whole buffer cycle so that every buffer index is a
+    // constant: 4 steps, or 12 with row-major weights (3 weight stages x 2
+    // token stages), then the remaining 4 or 8 steps with the first cycle's
+    // indices (the remainder starts at a multiple of 12)
+    constexpr int UNR = PACKED ? 4 : 12;
+    for (; t0 + UNR <= nsteps; t0 += UNR) unrolled(step, std::make_integer_sequence<int, UNR>{});
+    if constexpr (!PACKED) {
+      if (t0 < nsteps) {
+        unrolled(step, std::make_integer_sequence<int, 4>{});
+        if (t0 + 4 < nsteps)
+          unrolled([&](auto i) { step(std::integral_constant<int, decltype(i)::value + 4>{}); },
+                   std::make_integer_sequence<int, 4>{});
+      }
+    }
     // epilogue: lane holds token column fr of each 16x16 tile and weight rows
     // 4*fg .. 4*fg+3 of it; gate/up: gate in tiles 0-1, up in tiles 2-3. An
     // empty asm with VGPR constraints (no instruction) fixes the accumulators'

@@ -335,14 +335,17 @@ def test_exact_logit_ties_pick_lower_index(m):
     assert (w == 0.5).all()
 
 
-@pytest.mark.parametrize("d,ffn", [(128, 256), (256, 128), (256, 256), (256, 512)])
+@pytest.mark.parametrize("d,ffn", [(128, 256), (256, 128), (256, 256), (256, 512), (512, 640),
+                                   (768, 384)])
 def test_prefill_tail_tiles(m, d, ffn):
     """The 256x256-tile kernels (tiled family, used once A >= 512 E: gate/up
     always, down when d % 256 == 0; fragment-order and row-major weights) on hand-made
     routing whose per-expert row counts leave last tiles holding 16, 48, 80,
     128, 130 and 250 rows (every token-fragment count the kernels specialise:
     2, 4, 6, 8 and 0 for the idle half), an empty expert and an exact multiple
-    of 256; one or two unrolled trips of the K loops. With ffn % 256 == 0 and
+    of 256; K loops of 4 to 24 steps of 32, so that the row-major kernels'
+    12-step cycle runs not at all, once with 4 or 8 steps left, exactly once
+    and twice, and the fragment-order kernels' 4-step trip once to six times. With ffn % 256 == 0 and
     these few tiles the down projection splits K in two (the workspace holds
     the two partial arrays), otherwise it does not. Oracle within the bf16
     bar, and the two weight layouts bit-identical (same MFMA sequence, same
