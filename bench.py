@@ -310,7 +310,8 @@ def main():
     torch.cuda.synchronize()
     moe.moe_set_ffn_variant(args.variant)
     wdt = dev["x"].dtype
-    ws = moe.workspace(T, d, F, E, k, wdt, "cuda")
+    # (int8 weights at prefill sizes also need room for widened codes)
+    ws = moe.workspace(T, d, F, E, k, moe.MOE_INT8_PACKED if int8 else wdt, "cuda")
     out = torch.empty(T, d, dtype=wdt, device="cuda")
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     hip = Hip()

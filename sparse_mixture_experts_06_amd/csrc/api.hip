@@ -17,7 +17,7 @@ int g_nevents = 0;
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t idx, w, counts, offsets, sorted, pos, h, y, total;
+  size_t idx, w, counts, offsets, sorted, pos, h, y, wide, total;
 };
 
 // bfloat16 activations (x, h): bf16 weights in either layout, or int8 weights
@@ -48,6 +48,9 @@ Layout layout(int64_t T, int d, int ffn, int E, int k, int dtype) {
   L.pos = o;     o = align256(o + A * 4);
   L.h = o;       o = align256(o + A * static_cast<size_t>(ffn) * hb);
   L.y = o;       o = align256(o + ns * A * static_cast<size_t>(d) * 4);
+  L.wide = o;
+  if (dtype == MOE_INT8_PACKED)
+    o = align256(o + moe::int8_wide_bytes(static_cast<int64_t>(A), k, d, ffn, E));
   L.total = o;
   return L;
 }
@@ -90,21 +93,45 @@ inline void stage(int i, hipStream_t s) {
 }
 
 // gate/up then down; the down result is left as `nsplit_out` partial arrays
-// at `part` (the caller sums them: the combine, or moe_expert_ffn)
+// at `part` (the caller sums them: the combine, or moe_expert_ffn). `wide`:
+// the workspace region for int8 weights widened to bf16 (prefill sizes)
 int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
             const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d, int ffn, int E,
-            int k, float* part, void* h, hipStream_t s, bool with_events, int* nsplit_out) {
+            int k, float* part, void* h, void* wide, hipStream_t s, bool with_events,
+            int* nsplit_out) {
   const int64_t A = T * k;
   hipError_t err;
   if (dtype == MOE_INT8_PACKED) {
-    // int8 weights: the streaming kernels at every batch size
-    *nsplit_out = moe::down_splits(1, A, d, ffn, E);
-    err = moe::launch_gate_up_int8(static_cast<const uint16_t*>(x), w1, w3, offsets, sorted_asg,
-                                   d, ffn, E, k, static_cast<uint16_t*>(h), s);
+    // int8 weights: the streaming kernels on the codes (few rows per expert),
+    // or the codes widened to bf16 and the direct-to-LDS kernels with row
+    // scales (many rows per expert)
+    *nsplit_out = moe::int8_down_splits(A, d, ffn, E);
+    uint16_t* wb = static_cast<uint16_t*>(wide);
+    if (moe::int8_gate_up_dma(A, k, d, ffn, E)) {
+      uint16_t* w3b = wb + static_cast<size_t>(E) * ffn * d;
+      err = moe::launch_widen_int8(w1, E, ffn, d, wb, s);
+      if (err == hipSuccess) err = moe::launch_widen_int8(w3, E, ffn, d, w3b, s);
+      if (err == hipSuccess)
+        err = moe::launch_gate_up_dma(true, static_cast<const uint16_t*>(x), wb, w3b, offsets,
+                                      sorted_asg, A, d, ffn, E, k, static_cast<uint16_t*>(h), s,
+                                      moe::int8_scales(w1, E, ffn, d),
+                                      moe::int8_scales(w3, E, ffn, d));
+    } else {
+      err = moe::launch_gate_up_int8(static_cast<const uint16_t*>(x), w1, w3, offsets, sorted_asg,
+                                     d, ffn, E, k, static_cast<uint16_t*>(h), s);
+    }
     if (err != hipSuccess) return MOE_EHIP;
     if (with_events) stage(3, s);
-    err = moe::launch_down_int8(static_cast<const uint16_t*>(h), w2, offsets, A, d, ffn, E,
-                                *nsplit_out, part, s);
+    if (moe::int8_down_dma(A, d, ffn, E)) {
+      // (stream order: gate/up has finished with the widened w1 and w3)
+      err = moe::launch_widen_int8(w2, E, d, ffn, wb, s);
+      if (err == hipSuccess)
+        err = moe::launch_down_dma(true, static_cast<const uint16_t*>(h), wb, offsets, A, d, ffn,
+                                   E, *nsplit_out, part, s, moe::int8_scales(w2, E, d, ffn));
+    } else {
+      err = moe::launch_down_int8(static_cast<const uint16_t*>(h), w2, offsets, A, d, ffn, E,
+                                  *nsplit_out, part, s);
+    }
   } else if (is_bf16(dtype)) {
     const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
     const bool packed = dtype == MOE_BF16_PACKED;
@@ -196,12 +223,13 @@ int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, con
   char* base = static_cast<char*>(ws);
   const int64_t A = T * k;
   const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
-  const int nsplit = dtype == MOE_INT8_PACKED ? moe::down_splits(1, A, d, ffn, E)
+  const int nsplit = dtype == MOE_INT8_PACKED ? moe::int8_down_splits(A, d, ffn, E)
                      : is_bf16(dtype)          ? moe::down_splits(variant, A, d, ffn, E)
                                                : 1;
   float* part = nsplit > 1 ? reinterpret_cast<float*>(base + L.y) : y;
   int used = 1;
-  st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, part, base + L.h, s,
+  st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, part, base + L.h,
+               base + L.wide, s,
                false, &used);
   if (st != MOE_OK) return st;
   if (used > 1)
@@ -268,8 +296,8 @@ int forward_impl(const void* x, int dtype, const float* gamma, float eps, void* 
     return MOE_OK;
   }
   int nsplit = 1;
-  st = run_ffn(xin, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, h, s, true,
-               &nsplit);
+  st = run_ffn(xin, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, h, base + L.wide,
+               s, true, &nsplit);
   if (st != MOE_OK) return st;
   stage(4, s);
   if (moe::launch_combine(y, nsplit, asg_pos, w, T, d, k, out, out_dtype == MOE_BF16, s,

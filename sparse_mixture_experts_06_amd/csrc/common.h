@@ -114,21 +114,33 @@ int down_splits(int variant, int64_t A, int d, int ffn, int E);
 // gate/up and down for many rows per expert with direct-to-LDS loads
 // (ffn_dma.hip), for fragment-order (packed) or row-major weights: the sizes
 // they are used for, the K split of the down projection (1 or 2) and the
-// launchers
+// launchers; optional float32 row scales [E, rows] multiply the finished sums
+// (int8 codes widened to bfloat16)
 bool dma_gate_up_ok(int64_t A, int k, int d, int ffn, int E);
 hipError_t launch_gate_up_dma(bool packed, const uint16_t* x, const uint16_t* w1,
                               const uint16_t* w3, const int32_t* offsets,
                               const int32_t* sorted_asg, int64_t A, int d, int ffn, int E, int k,
-                              uint16_t* h, hipStream_t s);
+                              uint16_t* h, hipStream_t s, const float* s1 = nullptr,
+                              const float* s3 = nullptr);
 bool dma_down_ok(int64_t A, int d, int ffn, int E);
 int dma_down_splits(int64_t A, int d, int ffn, int E);
 hipError_t launch_down_dma(bool packed, const uint16_t* h, const uint16_t* w2,
                            const int32_t* offsets, int64_t A, int d, int ffn, int E, int nsplit,
-                           float* part, hipStream_t s);
+                           float* part, hipStream_t s, const float* s2 = nullptr);
 // weight-only int8 experts (ffn_int8.hip): bytes of one quantized matrix
 // (codes, then float32 row scales at the next 256-byte boundary), the
 // quantizer, and the streaming gate/up and down kernels that read it
 size_t int8_weight_bytes(int E, int rows, int cols);
+// the row scales inside a quantized matrix; prefill: whether gate/up and down
+// widen the codes and run the direct-to-LDS kernels, the down K split, and
+// the workspace bytes the widened matrices take (0 when neither does)
+const float* int8_scales(const void* w, int E, int rows, int cols);
+hipError_t launch_widen_int8(const void* w, int E, int rows, int cols, uint16_t* out,
+                             hipStream_t s);
+bool int8_gate_up_dma(int64_t A, int k, int d, int ffn, int E);
+bool int8_down_dma(int64_t A, int d, int ffn, int E);
+int int8_down_splits(int64_t A, int d, int ffn, int E);
+size_t int8_wide_bytes(int64_t A, int k, int d, int ffn, int E);
 hipError_t launch_quantize_int8(const uint16_t* w, int E, int rows, int cols, void* out,
                                 hipStream_t s);
 hipError_t launch_gate_up_int8(const uint16_t* x, const void* w1, const void* w3,

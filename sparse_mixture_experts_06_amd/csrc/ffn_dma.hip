@@ -61,6 +61,13 @@
 // indices. The MFMAs, their operands and their order are those of the
 // fragment-order kernel, so the results of the two layouts are identical.
 //
+// Row scales (weight-only int8, whose codes the caller has widened to exact
+// bfloat16 in fragment order; template parameter SCALED, fragment order
+// only): with scale arrays [E, N] the finished
+// float32 sums are multiplied by their weight row's scale before the SiLU*mul
+// (gate/up: gate by the w1 row's scale, up by the w3 row's) or the store
+// (down, each K-split partial), as the int8 decode kernels do.
+//
 // Every output element is one float32 MFMA accumulation over its K range in
 // increasing K, 32 at a time: the order of the 128-row tiled kernels, whose
 // results this kernel reproduces bit for bit.
@@ -125,19 +132,20 @@ __device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offse
   return false;
 }
 
-// GATE_UP: act = x [act_rows = T, K = d] bf16, wa/wb = w1/w3 in fragment
-// order [E, N = ffn, d], out = h [A, ffn] bf16, nsplit = 1.
-// !GATE_UP: act = h [act_rows = A, K = ffn] bf16 in grouped order, wa = w2 in
-// fragment order [E, N = d, ffn], out = part [nsplit][A][d] float32, the
-// partial arrays pstride floats apart.
-template <bool GATE_UP, bool PACKED>
+// GATE_UP: act = x [act_rows = T, K = d] bf16, wa/wb = w1/w3 [E, N = ffn, d],
+// out = h [A, ffn] bf16, nsplit = 1.
+// !GATE_UP: act = h [act_rows = A, K = ffn] bf16 in grouped order, wa = w2
+// [E, N = d, ffn], out = part [nsplit][A][d] float32, the partial arrays
+// pstride floats apart. SCALED: sa/sb = row scales [E, N] of wa/wb.
+template <bool GATE_UP, bool PACKED, bool SCALED>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64_t act_rows,
                                          const uint16_t* __restrict__ wa,
                                          const uint16_t* __restrict__ wb,
                                          const int32_t* __restrict__ offsets,
                                          const int32_t* __restrict__ sorted_asg, int K, int N,
                                          int E, int ktop, void* __restrict__ out, int ntn,
-                                         int nsplit, int64_t pstride) {
+                                         int nsplit, int64_t pstride, const float* __restrict__ sa,
+                                         const float* __restrict__ sb) {
   int e, beg, M, m0, nt, sp;
   if (!decode_tile256(offsets, E, ntn, nsplit, e, beg, M, m0, nt, sp)) return;
 
@@ -363,6 +371,10 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
     // 4*fg .. 4*fg+3 of it; gate/up: gate in tiles 0-1, up in tiles 2-3. An
     // empty asm with VGPR constraints (no instruction) fixes the accumulators'
     // register class for the allocator.
+    // (SCALED: the row scales of the lane's 4 rows of a weight tile, read
+    // where they are used; cache hits after the first token tile)
+    const float* rsa = SCALED ? sa + static_cast<size_t>(e) * N : nullptr;
+    const float* rsb = SCALED ? sb + static_cast<size_t>(e) * N : nullptr;
 #pragma unroll
     for (int j = 0; j < JV; ++j) {
       const int m = m0 + wm * 128 + j * 16 + fr;
@@ -374,6 +386,10 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
           f32x4 gt = acc[i][j];
           f32x4 up = acc[i + 2][j];
           asm volatile("" : "+v"(gt), "+v"(up));
+          if constexpr (SCALED) {
+            gt *= *reinterpret_cast<const f32x4*>(rsa + n);
+            up *= *reinterpret_cast<const f32x4*>(rsb + n);
+          }
           uint2 v;
           v.x = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
           v.y = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
@@ -386,6 +402,8 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
         for (int i = 0; i < 4; ++i) {
           f32x4 v = acc[i][j];
           asm volatile("" : "+v"(v));
+          if constexpr (SCALED)
+            v *= *reinterpret_cast<const f32x4*>(rsa + nt * 256 + wn * 64 + i * 16 + 4 * fg);
           *reinterpret_cast<f32x4*>(y + nt * 256 + wn * 64 + i * 16 + 4 * fg) = v;
         }
       }
@@ -401,22 +419,23 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
 }
 
 // x [T, d] bf16, w1/w3 [E, ffn, d] (fragment order or row-major), h [A, ffn] bf16
-template <bool PACKED>
+template <bool PACKED, bool SCALED>
 __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
     const uint16_t* __restrict__ x, int64_t T, const uint16_t* __restrict__ w1,
     const uint16_t* __restrict__ w3, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_asg, int d, int ffn, int E, int ktop,
-    uint16_t* __restrict__ h, int ntn) {
-  dma_tile<true, PACKED>(x, T, w1, w3, offsets, sorted_asg, d, ffn, E, ktop, h, ntn, 1, 0);
+    uint16_t* __restrict__ h, int ntn, const float* __restrict__ s1, const float* __restrict__ s3) {
+  dma_tile<true, PACKED, SCALED>(x, T, w1, w3, offsets, sorted_asg, d, ffn, E, ktop, h, ntn, 1, 0, s1, s3);
 }
 
 // h [A, ffn] bf16 grouped, w2 [E, d, ffn] (fragment order or row-major), part [nsplit, A, d] f32
-template <bool PACKED>
+template <bool PACKED, bool SCALED>
 __global__ __launch_bounds__(kDmaThreads, 1) void down_dma_kernel(
     const uint16_t* __restrict__ h, int64_t A, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ offsets, int d, int ffn, int E, float* __restrict__ part, int ntn,
-    int nsplit) {
-  dma_tile<false, PACKED>(h, A, w2, w2, offsets, nullptr, ffn, d, E, 1, part, ntn, nsplit, A * d);
+    int nsplit, const float* __restrict__ s2) {
+  dma_tile<false, PACKED, SCALED>(h, A, w2, w2, offsets, nullptr, ffn, d, E, 1, part, ntn, nsplit, A * d,
+                          s2, s2);
 }
 
 constexpr int64_t kMax31 = (int64_t(1) << 31) - 1;
@@ -437,16 +456,20 @@ bool dma_gate_up_ok(int64_t A, int k, int d, int ffn, int E) {
 hipError_t launch_gate_up_dma(bool packed, const uint16_t* x, const uint16_t* w1,
                               const uint16_t* w3, const int32_t* offsets,
                               const int32_t* sorted_asg, int64_t A, int d, int ffn, int E, int k,
-                              uint16_t* h, hipStream_t s) {
+                              uint16_t* h, hipStream_t s, const float* s1, const float* s3) {
   const int ntn = ffn / 128;
   const int64_t tiles = ((A + DT - 1) / DT + E) * ntn;  // upper bound
   const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8));
-  if (packed)
-    hipLaunchKernelGGL(gate_up_dma_kernel<true>, grid, dim3(kDmaThreads), 0, s, x, A / k, w1, w3,
-                       offsets, sorted_asg, d, ffn, E, k, h, ntn);
+  if (s1 && !packed) return hipErrorInvalidValue;  // row scales come with fragment order only
+  if (s1)
+    hipLaunchKernelGGL((gate_up_dma_kernel<true, true>), grid, dim3(kDmaThreads), 0, s, x, A / k,
+                       w1, w3, offsets, sorted_asg, d, ffn, E, k, h, ntn, s1, s3);
+  else if (packed)
+    hipLaunchKernelGGL((gate_up_dma_kernel<true, false>), grid, dim3(kDmaThreads), 0, s, x, A / k,
+                       w1, w3, offsets, sorted_asg, d, ffn, E, k, h, ntn, s1, s3);
   else
-    hipLaunchKernelGGL(gate_up_dma_kernel<false>, grid, dim3(kDmaThreads), 0, s, x, A / k, w1, w3,
-                       offsets, sorted_asg, d, ffn, E, k, h, ntn);
+    hipLaunchKernelGGL((gate_up_dma_kernel<false, false>), grid, dim3(kDmaThreads), 0, s, x, A / k,
+                       w1, w3, offsets, sorted_asg, d, ffn, E, k, h, ntn, s1, s3);
   return hipGetLastError();
 }
 
@@ -472,16 +495,20 @@ int dma_down_splits(int64_t A, int d, int ffn, int E) {
 
 hipError_t launch_down_dma(bool packed, const uint16_t* h, const uint16_t* w2,
                            const int32_t* offsets, int64_t A, int d, int ffn, int E, int nsplit,
-                           float* part, hipStream_t s) {
+                           float* part, hipStream_t s, const float* s2) {
   const int ntn = d / 256;
   const int64_t tiles = ((A + DT - 1) / DT + E) * ntn * nsplit;  // upper bound
   const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8));
-  if (packed)
-    hipLaunchKernelGGL(down_dma_kernel<true>, grid, dim3(kDmaThreads), 0, s, h, A, w2, offsets, d,
-                       ffn, E, part, ntn, nsplit);
+  if (s2 && !packed) return hipErrorInvalidValue;  // row scales come with fragment order only
+  if (s2)
+    hipLaunchKernelGGL((down_dma_kernel<true, true>), grid, dim3(kDmaThreads), 0, s, h, A, w2,
+                       offsets, d, ffn, E, part, ntn, nsplit, s2);
+  else if (packed)
+    hipLaunchKernelGGL((down_dma_kernel<true, false>), grid, dim3(kDmaThreads), 0, s, h, A, w2,
+                       offsets, d, ffn, E, part, ntn, nsplit, s2);
   else
-    hipLaunchKernelGGL(down_dma_kernel<false>, grid, dim3(kDmaThreads), 0, s, h, A, w2, offsets, d,
-                       ffn, E, part, ntn, nsplit);
+    hipLaunchKernelGGL((down_dma_kernel<false, false>), grid, dim3(kDmaThreads), 0, s, h, A, w2,
+                       offsets, d, ffn, E, part, ntn, nsplit, s2);
   return hipGetLastError();
 }
 

@@ -21,6 +21,13 @@
 // 256-byte boundary, the float32 scales [E, rows]. A wave's 16-byte load of one
 // block is one contiguous KiB and feeds two 32-deep MFMA steps.
 //
+// Many rows per expert (prefill): the codes are widened to bfloat16 (exact)
+// in the fragment order of the bf16 path, into the caller's workspace, and
+// the direct-to-LDS tile kernels run on them with the row scales applied to
+// their finished sums. Block b of the codes holds exactly the bf16 fragments
+// 2b (its bytes 0-7 in each lane) and 2b+1 (bytes 8-15), since both layouts
+// order (expert, 16-row tile, K step) and put lane l's values in lane order.
+//
 // Kernels: the streaming decode kernels of ffn_bf16.hip with int8 weights.
 // gate/up: a workgroup owns two 16-row tiles of w1 and w3, its 4 waves split
 // K, partial sums meet in LDS, wave 0 scales, applies SiLU*mul and stores bf16
@@ -95,6 +102,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     int8_t* dst = codes + w8_block(e, n >> 4, s, rows, cols) + (16 * g + r) * 16 + half * 8;
     *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
   }
+}
+
+// codes of nblocks blocks -> bf16 fragment order: one thread per (block, lane)
+__global__ __launch_bounds__(256) void widen_kernel(const int8_t* __restrict__ codes,
+                                                    int64_t nblocks, uint16_t* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= nblocks * kWave) return;
+  const int64_t b = i / kWave;
+  const int lane = static_cast<int>(i % kWave);
+  u32x4 lo, hi;
+  cvt16(ldw8(codes + b * 1024 + lane * 16), lo, hi);
+  *reinterpret_cast<u32x4*>(out + (2 * b) * 512 + lane * 8) = lo;
+  *reinterpret_cast<u32x4*>(out + (2 * b + 1) * 512 + lane * 8) = hi;
 }
 
 // x [T, K=d] bf16 rows gathered through sorted_asg / ktop; w1, w3 codes and
@@ -339,6 +359,37 @@ constexpr int kW8DownRT = MOE_W8_DN_RT, kW8DownU = MOE_W8_DN_U;
 
 size_t int8_weight_bytes(int E, int rows, int cols) {
   return align256(static_cast<size_t>(E) * rows * cols) + static_cast<size_t>(E) * rows * 4;
+}
+
+const float* int8_scales(const void* w, int E, int rows, int cols) {
+  return reinterpret_cast<const float*>(static_cast<const char*>(w) +
+                                        align256(static_cast<size_t>(E) * rows * cols));
+}
+
+hipError_t launch_widen_int8(const void* w, int E, int rows, int cols, uint16_t* out,
+                             hipStream_t s) {
+  const int64_t nblocks = static_cast<int64_t>(E) * (rows / 16) * (cols / 64);
+  const int64_t threads = nblocks * kWave;
+  hipLaunchKernelGGL(widen_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
+                     0, s, static_cast<const int8_t*>(w), nblocks, out);
+  return hipGetLastError();
+}
+
+bool int8_gate_up_dma(int64_t A, int k, int d, int ffn, int E) {
+  return dma_gate_up_ok(A, k, d, ffn, E);
+}
+bool int8_down_dma(int64_t A, int d, int ffn, int E) { return dma_down_ok(A, d, ffn, E); }
+
+int int8_down_splits(int64_t A, int d, int ffn, int E) {
+  return int8_down_dma(A, d, ffn, E) ? dma_down_splits(A, d, ffn, E) : down_splits(1, A, d, ffn, E);
+}
+
+size_t int8_wide_bytes(int64_t A, int k, int d, int ffn, int E) {
+  const size_t m = static_cast<size_t>(E) * ffn * d * 2;  // one widened matrix
+  size_t b = 0;
+  if (int8_gate_up_dma(A, k, d, ffn, E)) b = 2 * m;        // w1 and w3
+  if (int8_down_dma(A, d, ffn, E) && m > b) b = m;          // w2, after gate/up is done
+  return b;
 }
 
 hipError_t launch_quantize_int8(const uint16_t* w, int E, int rows, int cols, void* out,

@@ -61,9 +61,11 @@ def _kernels(text):
     return out
 
 
-# template argument PACKED: fragment-order (b1) or row-major (b0) weights;
-# K steps per loop trip and the even steps' wait
-LAYOUTS = {"packed": ("ILb1E", 4, 8), "row_major": ("ILb0E", 12, 12)}
+# template arguments PACKED (fragment-order b1 or row-major b0 weights) and
+# SCALED (row scales of int8 codes widened to bf16); K steps per loop trip and
+# the even steps' wait
+LAYOUTS = {"packed": ("ILb1ELb0E", 4, 8), "packed_scaled": ("ILb1ELb1E", 4, 8),
+           "row_major": ("ILb0ELb0E", 12, 12)}
 
 
 def test_all_kernels_are_present(asm):

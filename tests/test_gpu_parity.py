@@ -239,6 +239,47 @@ def test_int8_forward_matches_oracle(m, name):
     assert torch.equal(out_b, out_f + dev["x"].float())
 
 
+@pytest.mark.parametrize("d,ffn", [(256, 512), (384, 640)])
+def test_int8_prefill_matches_oracle(m, d, ffn):
+    """int8 weights at prefill sizes (A >= 512 E): the codes are widened to
+    bf16 in fragment order in the workspace and the 256x256-tile kernels apply
+    the row scales to their sums. Hand-made routing with the tail-tile row
+    counts (expert step alone), then the fused layer on the same weights with
+    its own routing; both against the oracle on its dequantized weights. At
+    d = 384 the down projection stays on the streaming int8 kernel (the tile
+    kernel needs d % 256 == 0); at d = 256, ffn = 512 it splits K in two."""
+    counts = [784, 816, 848, 896, 898, 0, 1024, 1018]
+    E, k = len(counts), 2
+    A = sum(counts)
+    inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=60 + d)
+    sasg = np.random.default_rng(61).permutation(A).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ws_i8 = m.moe_workspace_bytes(A // k, d, ffn, E, k, m.MOE_INT8_PACKED)
+    ws_b = m.moe_workspace_bytes(A // k, d, ffn, E, k, torch.bfloat16)
+    assert ws_i8 - ws_b == 2 * E * ffn * d * 2  # widened w1 and w3 (w2 reuses them)
+    print(f"[parity] int8 prefill d={d} ffn={ffn} A={A}", flush=True)
+    dev = to_device(inp)
+    qw = m.QuantizedWeights(dev["w1"], dev["w3"], dev["w2"])
+    deq = _quantized(inp)
+    y = m.moe_expert_ffn(dev["x"], qw.w1, qw.w3, qw.w2, torch.from_numpy(offs).cuda(),
+                         torch.from_numpy(sasg).cuda(), k)
+    T = inp["T"]
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    out = m.moe_forward(dev["x"], dev["router"], qw.w1, qw.w3, qw.w2, k, out_dtype=torch.float32,
+                        topk_idx_out=idx, topk_w_out=w)
+    torch.cuda.synchronize()
+    y_ref = oracle.expert_ffn(inp["x"], deq["w1"][2], deq["w3"][2], deq["w2"][2], offs, sasg, k)
+    assert rel_err(host(y), y_ref) <= OUT_TOL[gen.BF16]
+    ref_inp = dict(inp, w1=deq["w1"][2], w3=deq["w3"][2], w2=deq["w2"][2])
+    logits64 = oracle.router_logits(inp["x"], inp["router"], inp["bias"])
+    idx_g = host(idx)
+    check_routing(logits64, k, idx_g, host(w))
+    assert np.bincount(idx_g.ravel(), minlength=E).min() > 0
+    ref = expected_output(ref_inp, idx_g, None, np.arange(T), logits64)
+    assert rel_err(host(out), ref) <= OUT_TOL[gen.BF16]
+
+
 def _pack_reference(w):
     """Fragment order as include/moe.h defines it, by plain index arithmetic."""
     E, R, C = w.shape
@@ -493,6 +534,39 @@ def test_full_size_decode_int8_and_block(m):
     err_b = rel_err(mlp_gpu, mlp_ref)
     print(f"[parity] block decode: max|err|/rms={err_b:.3e}", flush=True)
     assert err_b <= OUT_TOL[gen.BF16]
+
+
+@pytest.mark.slow
+def test_full_size_prefill_int8(m):
+    """Prefill 8x7B shape on int8 weights (the configuration the benchmark
+    times with --weights int8): widened codes on the 256x256-tile kernels,
+    routing on every token, sampled outputs against the oracle's dequantized
+    weights."""
+    print("[parity] full-size prefill_8x7b int8", flush=True)
+    m.moe_set_ffn_variant(0)
+    inp = gen.make_config("prefill_8x7b")
+    dev = to_device(inp)
+    T, E, k = inp["T"], inp["E"], inp["k"]
+    qw = m.QuantizedWeights(dev["w1"], dev["w3"], dev["w2"])
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    out = m.moe_forward(dev["x"], dev["router"], qw.w1, qw.w3, qw.w2, k, out_dtype=torch.float32,
+                        topk_idx_out=idx, topk_w_out=w)
+    torch.cuda.synchronize()
+    del qw
+    qs = {n: oracle.quantize_int8(inp[n]) for n in ("w1", "w3", "w2")}
+    logits64 = oracle.router_logits(inp["x"], inp["router"], inp["bias"])
+    idx_g = host(idx)
+    near, _ = check_routing(logits64, k, idx_g, host(w))
+    idx_use = oracle.select_topk(logits64, k)
+    idx_use[near] = idx_g[near]
+    w_use = oracle.renormalised_weights_for(logits64, idx_use)
+    rng = np.random.default_rng(2468)
+    tokens = np.unique(np.concatenate([rng.choice(T, size=40, replace=False), [0, T - 1]]))
+    ref = _tokens_output_int8(inp["x"], qs, idx_use, w_use, tokens)
+    err = rel_err(host(out)[tokens], ref)
+    print(f"[parity] int8 prefill: max|err|/rms={err:.3e}", flush=True)
+    assert err <= OUT_TOL[gen.BF16]
 
 
 @pytest.mark.slow
