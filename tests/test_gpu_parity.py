@@ -239,6 +239,42 @@ def test_int8_forward_matches_oracle(m, name):
     assert torch.equal(out_b, out_f + dev["x"].float())
 
 
+@pytest.mark.parametrize("E,k", [(16, 4), (32, 1)])
+def test_prefill_tiles_many_experts(m, E, k):
+    """The 256x256-tile kernels with 16 and 32 experts (tile lists of 28-60
+    m-tiles over 8 XCD groups): per-expert counts from empty through tails of
+    every token-fragment count to several full tiles, both weight layouts
+    (bit-identical) and int8 weights, against the oracle."""
+    rng = np.random.default_rng(70 + E)
+    base = [0, 16, 300, 512, 700, 1100, 520, 257]
+    counts = [base[i % len(base)] + (i // len(base)) * 48 for i in range(E)]
+    counts[5] += max(0, 512 * E - sum(counts))  # one expert of many full tiles
+    A = sum(counts)
+    A += (-A) % k
+    counts[1] += A - sum(counts)
+    assert A >= 512 * E
+    d, ffn = 256, 384
+    inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=71 + E)
+    sasg = rng.permutation(A).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    print(f"[parity] prefill tiles E={E} k={k} A={A}", flush=True)
+    dev = to_device(inp)
+    o_t = torch.from_numpy(offs).cuda()
+    s_t = torch.from_numpy(sasg).cuda()
+    pw = m.PackedWeights(dev["w1"], dev["w3"], dev["w2"])
+    qw = m.QuantizedWeights(dev["w1"], dev["w3"], dev["w2"])
+    y_p = m.moe_expert_ffn(dev["x"], pw.w1, pw.w3, pw.w2, o_t, s_t, k, packed=True)
+    y_s = m.moe_expert_ffn(dev["x"], dev["w1"], dev["w3"], dev["w2"], o_t, s_t, k)
+    y_q = m.moe_expert_ffn(dev["x"], qw.w1, qw.w3, qw.w2, o_t, s_t, k)
+    torch.cuda.synchronize()
+    assert torch.equal(y_p, y_s)
+    ref = oracle.expert_ffn(inp["x"], inp["w1"], inp["w3"], inp["w2"], offs, sasg, k)
+    assert rel_err(host(y_p), ref) <= OUT_TOL[gen.BF16]
+    deq = _quantized(inp)
+    ref_q = oracle.expert_ffn(inp["x"], deq["w1"][2], deq["w3"][2], deq["w2"][2], offs, sasg, k)
+    assert rel_err(host(y_q), ref_q) <= OUT_TOL[gen.BF16]
+
+
 @pytest.mark.parametrize("d,ffn", [(256, 512), (384, 640)])
 def test_int8_prefill_matches_oracle(m, d, ffn):
     """int8 weights at prefill sizes (A >= 512 E): the codes are widened to
