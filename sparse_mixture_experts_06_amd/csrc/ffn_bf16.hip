@@ -31,13 +31,17 @@
 //    K, written as a float32 partial; the partials are summed later in a
 //    fixed order (by the combine, or by moe_expert_ffn before it returns).
 //    With fragment-order weights the weight loads are non-temporal.
-//  * tiled (many rows per expert, prefill): 128 weight rows x 128 token rows
-//    x 64 K per step, double-buffered in LDS with an XOR swizzle of the
-//    16-byte chunks (conflict-free ds_read_b128 for the MFMA fragments); 4
-//    waves each own a 64x64 block of 4x4 MFMA tiles. Tiles are listed expert
-//    by expert, n-tile by n-tile, m-tile by m-tile, and consecutive tiles go
-//    to the same XCD so the m-tiles sharing a weight tile meet in that XCD's
-//    L2.
+//  * tiled (many rows per expert, prefill). When experts average two or more
+//    full 256-row tiles (A >= 512 E; d and ffn multiples of 128, and for down
+//    d % 256 == 0) the 256x256-tile direct-to-LDS kernels of ffn_dma.hip run,
+//    for either layout. Below that: with fragment-order weights wtiled_kernel
+//    (256 weight rows x 128 tokens, weights straight into registers), with
+//    the standard layout tiled_kernel: 128 weight rows x 128 token rows x 64
+//    K per step, double-buffered in LDS with an XOR swizzle of the 16-byte
+//    chunks (conflict-free ds_read_b128 for the MFMA fragments); 4 waves each
+//    own a 64x64 block of 4x4 MFMA tiles. Tiles are listed expert by expert,
+//    n-tile by n-tile, m-tile by m-tile, and consecutive tiles go to the same
+//    XCD so the m-tiles sharing a weight tile meet in that XCD's L2.
 #include <type_traits>
 #include <utility>
 
@@ -811,8 +815,8 @@ int choose_ffn_variant(int requested, int64_t A, int E) {
 int down_splits(int variant, int64_t A, int d, int ffn, int E) {
   // the streaming down kernel splits K two ways while its float32 partials
   // stay small; the tiled kernels split K where the 256-row tiles of the
-  // direct-to-LDS kernel would leave the last round over the CUs part-empty
-  // (the 128-row kernels follow the same split, so y does not depend on the
+  // direct-to-LDS kernels would leave the last round over the CUs part-empty
+  // (all tiled kernels follow the same split, so y does not depend on the
   // weight layout)
   if (variant == 1) return A <= 4096 ? 2 : 1;
   return dma_down_splits(A, d, ffn, E);

@@ -1,8 +1,8 @@
 // Expert projections for many rows per expert (prefill), with fragment-order
-// or row-major weights: both grouped GEMMs of the Mixtral sparse-MoE block (nnterp Mixtral
-// page, support(): the down projection receives act(gate) * up with act =
-// SiLU; the experts are one stacked module), the first fused with that
-// activation, as in ffn_bf16.hip:
+// or row-major weights: both grouped GEMMs of the Mixtral sparse-MoE block
+// (nnterp Mixtral page, support(): the down projection receives act(gate) *
+// up with act = SiLU; the experts are one stacked module), the first fused
+// with that activation, as in ffn_bf16.hip:
 //
 //   gate/up: h[p, n] = silu(sum_i x[r,i] w1[e,n,i]) * (sum_i x[r,i] w3[e,n,i]),
 //            r = sorted_asg[p] / k for p in expert e's grouped rows; h is bf16;
@@ -20,7 +20,8 @@
 // .. + 63. K advances in 32-wide steps.
 //
 // Both operands go global -> LDS with the 16-byte direct-to-LDS buffer loads,
-// no register staging. Weights: one load instruction moves one 1 KiB MFMA
+// no register staging. Fragment-order weights (template parameter PACKED;
+// row-major weights below): one load instruction moves one 1 KiB MFMA
 // fragment (one contiguous KiB of the fragment-order matrix) into LDS in lane
 // order; four 16 KiB buffers hold the weight fragments of steps t .. t+3.
 // Tokens: one load instruction moves 8 token rows x 128 bytes (gathered rows
@@ -61,11 +62,10 @@
 // indices. The MFMAs, their operands and their order are those of the
 // fragment-order kernel, so the results of the two layouts are identical.
 //
-// Row scales (weight-only int8, whose codes the caller has widened to exact
-// bfloat16 in fragment order; template parameter SCALED, fragment order
-// only): with scale arrays [E, N] the finished
-// float32 sums are multiplied by their weight row's scale before the SiLU*mul
-// (gate/up: gate by the w1 row's scale, up by the w3 row's) or the store
+// Row scales (template parameter SCALED, fragment order only: weight-only
+// int8 codes the caller has widened to exact bfloat16): the finished float32
+// sums are multiplied by their weight row's scale from arrays [E, N] before
+// the SiLU*mul (gate by the w1 row's scale, up by the w3 row's) or the store
 // (down, each K-split partial), as the int8 decode kernels do.
 //
 // Every output element is one float32 MFMA accumulation over its K range in
