@@ -28,6 +28,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import os
 import sys
@@ -143,10 +144,15 @@ def algorithmic_work(cfg, counts, block=False, int8=False):
 
 
 def ffn_sources_sha():
+    """Hash of the expert-kernel sources with comments and layout removed, so
+    that the traffic records follow the code, not its comments."""
     h = hashlib.sha256()
     for path in FFN_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
