@@ -11,6 +11,8 @@
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -21,19 +23,24 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float32 -> bfloat16, round to nearest, ties to even (inputs are finite).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-
+// Two float32 -> bfloat16, round to nearest, ties to even, in one
+// v_cvt_pk_bf16_f32 (lo in bits 0-15); for every non-NaN input the same bits
+// as rounding the float32 bit pattern by hand (u + 0x7FFF + lsb, >> 16).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// SiLU(z) = z / (1 + exp(-z)) in float32.
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.0f));
+}
+
+// SiLU(z) = z / (1 + exp(-z)) in float32, the division as a multiply by the
+// hardware reciprocal (v_rcp_f32, 1 ulp): the gate/up epilogues evaluate one
+// per output, and h is rounded to bfloat16 right after. Limits: 1 + exp(-z)
+// = inf for very negative z gives -0, as the division does.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // 16 bytes (8 bf16) as an MFMA operand.
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
