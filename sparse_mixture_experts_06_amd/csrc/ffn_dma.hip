@@ -7,8 +7,8 @@
 //   gate/up: h[p, n] = silu(sum_i x[r,i] w1[e,n,i]) * (sum_i x[r,i] w3[e,n,i]),
 //            r = sorted_asg[p] / k for p in expert e's grouped rows; h is bf16;
 //   down:    y[p, n] = sum_i h[p,i] w2[e,n,i], float32, optionally split in K
-//            into nsplit partial sums (written to part[sp]; their sum in split
-//            order is y).
+//            into two partial sums over [0, ksplit) and [ksplit, K) (written
+//            to part[0] and part[1]; y is their sum in that order).
 //
 // Tile: 256 weight rows x 256 token rows per workgroup of 8 waves, two per
 // SIMD (so one wave's MFMAs run while the other waits on a load issue or the
@@ -95,36 +95,67 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // workgroup -> (expert e, its first grouped row beg and row count M, token
-// tile m0, weight tile nt, K split sp). Workgroup b runs on XCD x = b % 8,
-// which takes the weight tiles nt = x, x + 8, ... of every expert and split,
-// each with all its m-tiles: every XCD then gets the same share of every
-// expert's rows, part-filled last m-tiles included (contiguous slices of an
+// tile m0, weight tile nt, K part sp); workgroup b runs on XCD x = b % 8.
+// When the weight tiles come in multiples of 8 (every real shape), XCD x
+// takes the weight tiles nt = x, x + 8, ... of every expert and K part, each
+// with all its m-tiles: every XCD then gets the same share of every expert's
+// rows, part-filled last m-tiles included (contiguous slices of an
 // expert-major list gave XCDs with several nearly empty last tiles 12% less
 // work than others), and the m-tiles sharing a weight tile run together in
-// one XCD's L2. An XCD's tiles are listed expert by expert, split by split,
-// n-tile by n-tile, m-tile by m-tile and taken in that order, tile q by
-// workgroup 8q + x. Surplus workgroups of the worst-case grid return.
+// one XCD's L2. Its tiles are listed K part by K part (the longer first part
+// of every tile before any second part, so that the short ones fill the last
+// round), expert by expert, n-tile by n-tile, m-tile by m-tile, and taken in
+// that order, tile q by workgroup 8q + x. Otherwise (fewer or ragged weight
+// tiles) XCD x takes the x-th of 8 equal slices of the list of all tiles,
+// expert by expert, K part, n-tile, m-tile. Surplus workgroups of the
+// worst-case grid return.
 __device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offsets, int E, int ntn,
                                                int nsplit, int& e, int& beg, int& M, int& m0,
                                                int& nt, int& sp) {
   const int x = blockIdx.x & 7;
-  const int nnx = (ntn - x + 7) >> 3;  // weight tiles of this XCD
   int q = blockIdx.x >> 3;
+  if ((ntn & 7) == 0) {
+    const int nnx = ntn >> 3;  // weight tiles of each XCD
+    for (int s = 0; s < nsplit; ++s) {
+      for (int i = 0; i < E; ++i) {
+        const int Mi = offsets[i + 1] - offsets[i];
+        const int mt = (Mi + DT - 1) / DT;
+        const int cnt = mt * nnx;
+        if (q < cnt) {
+          e = i;
+          beg = offsets[i];
+          M = Mi;
+          m0 = (q % mt) * DT;
+          nt = (q / mt) * 8 + x;
+          sp = s;
+          return true;
+        }
+        q -= cnt;
+      }
+    }
+    return false;
+  }
+  int total = 0;
+  for (int i = 0; i < E; ++i) total += ((offsets[i + 1] - offsets[i] + DT - 1) / DT) * ntn * nsplit;
+  const int per = (total + 7) / 8;
+  if (q >= per) return false;
+  int L = x * per + q;
+  if (L >= total) return false;
   for (int i = 0; i < E; ++i) {
     const int Mi = offsets[i + 1] - offsets[i];
     const int mt = (Mi + DT - 1) / DT;
-    const int cnt = mt * nnx * nsplit;
-    if (q < cnt) {
+    const int cnt = mt * ntn * nsplit;
+    if (L < cnt) {
       e = i;
       beg = offsets[i];
       M = Mi;
-      m0 = (q % mt) * DT;
-      const int r = q / mt;
-      nt = (r % nnx) * 8 + x;
-      sp = r / nnx;
+      m0 = (L % mt) * DT;
+      const int r = L / mt;
+      nt = r % ntn;
+      sp = r / ntn;
       return true;
     }
-    q -= cnt;
+    L -= cnt;
   }
   return false;
 }
@@ -133,7 +164,8 @@ __device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offse
 // out = h [A, ffn] bf16, nsplit = 1.
 // !GATE_UP: act = h [act_rows = A, K = ffn] bf16 in grouped order, wa = w2
 // [E, N = d, ffn], out = part [nsplit][A][d] float32, the partial arrays
-// pstride floats apart. SCALED: sa/sb = row scales [E, N] of wa/wb.
+// pstride floats apart; with nsplit = 2 the K parts are [0, ksplit) and
+// [ksplit, K) (ksplit a multiple of 128). SCALED: sa/sb = row scales [E, N] of wa/wb.
 template <bool GATE_UP, bool PACKED, bool SCALED>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64_t act_rows,
                                          const uint16_t* __restrict__ wa,
@@ -141,7 +173,8 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
                                          const int32_t* __restrict__ offsets,
                                          const int32_t* __restrict__ sorted_asg, int K, int N,
                                          int E, int ktop, void* __restrict__ out, int ntn,
-                                         int nsplit, int64_t pstride, const float* __restrict__ sa,
+                                         int nsplit, int ksplit, int64_t pstride,
+                                         const float* __restrict__ sa,
                                          const float* __restrict__ sb) {
   int e, beg, M, m0, nt, sp;
   if (!decode_tile256(offsets, E, ntn, nsplit, e, beg, M, m0, nt, sp)) return;
@@ -174,8 +207,9 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wn = w & 3, wm = w >> 2;
   const int fr = lane & 15, fg = lane >> 4;
-  const int Kc = GATE_UP ? K : K / nsplit;  // this tile's K range: [k0, k0 + Kc)
-  const int k0 = GATE_UP ? 0 : sp * Kc;
+  // this tile's K range: [k0, k0 + Kc)
+  const int k0 = (GATE_UP || sp == 0) ? 0 : ksplit;
+  const int Kc = (GATE_UP || nsplit == 1) ? K : (sp == 0 ? ksplit : K - ksplit);
   // LDS weight fragment f (of 16) is wave wn = f >> 2's tile f & 3. Gate/up:
   // w1 rows for f & 3 < 2, else w3 rows, nt*128 + (f >> 2)*32 + (f & 1)*16;
   // wave w loads fragments 2w, 2w+1 (all w1 for even w, all w3 for odd w).
@@ -422,7 +456,8 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
     const uint16_t* __restrict__ w3, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_asg, int d, int ffn, int E, int ktop,
     uint16_t* __restrict__ h, int ntn, const float* __restrict__ s1, const float* __restrict__ s3) {
-  dma_tile<true, PACKED, SCALED>(x, T, w1, w3, offsets, sorted_asg, d, ffn, E, ktop, h, ntn, 1, 0, s1, s3);
+  dma_tile<true, PACKED, SCALED>(x, T, w1, w3, offsets, sorted_asg, d, ffn, E, ktop, h, ntn, 1, d, 0,
+                                 s1, s3);
 }
 
 // h [A, ffn] bf16 grouped, w2 [E, d, ffn] (fragment order or row-major), part [nsplit, A, d] f32
@@ -430,9 +465,9 @@ template <bool PACKED, bool SCALED>
 __global__ __launch_bounds__(kDmaThreads, 1) void down_dma_kernel(
     const uint16_t* __restrict__ h, int64_t A, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ offsets, int d, int ffn, int E, float* __restrict__ part, int ntn,
-    int nsplit, const float* __restrict__ s2) {
-  dma_tile<false, PACKED, SCALED>(h, A, w2, w2, offsets, nullptr, ffn, d, E, 1, part, ntn, nsplit, A * d,
-                          s2, s2);
+    int nsplit, int ksplit, const float* __restrict__ s2) {
+  dma_tile<false, PACKED, SCALED>(h, A, w2, w2, offsets, nullptr, ffn, d, E, 1, part, ntn, nsplit,
+                                  ksplit, A * d, s2, s2);
 }
 
 constexpr int64_t kMax31 = (int64_t(1) << 31) - 1;
@@ -455,9 +490,8 @@ hipError_t launch_gate_up_dma(bool packed, const uint16_t* x, const uint16_t* w1
                               const int32_t* sorted_asg, int64_t A, int d, int ffn, int E, int k,
                               uint16_t* h, hipStream_t s, const float* s1, const float* s3) {
   const int ntn = ffn / 128;
-  // the most tiles one XCD can get, times 8
-  const int64_t grid_n = 8 * ((A + DT - 1) / DT + E) * ((ntn + 7) / 8);
-  const dim3 grid(static_cast<unsigned>(grid_n));
+  const int64_t tiles = ((A + DT - 1) / DT + E) * ntn;  // upper bound
+  const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8));
   if (s1 && !packed) return hipErrorInvalidValue;  // row scales come with fragment order only
   if (s1)
     hipLaunchKernelGGL((gate_up_dma_kernel<true, true>), grid, dim3(kDmaThreads), 0, s, x, A / k,
@@ -477,37 +511,103 @@ bool dma_down_ok(int64_t A, int d, int ffn, int E) {
   return static_cast<int64_t>(ffn) * d * 2 <= kMax31 && A * ffn * 2 <= kMax31;
 }
 
-int dma_down_splits(int64_t A, int d, int ffn, int E) {
-  if (!dma_down_ok(A, d, ffn, E) || ffn % 256 != 0) return 1;
-  // One workgroup per CU (128 KiB of LDS). Splitting K in two halves each
-  // tile's time and doubles the tile count; it pays when that packs the tiles
-  // into noticeably fewer rounds over the CUs, e.g. 2.25 rounds of tiles
-  // taking 3 round times unsplit and 2.5 split. The tile count is estimated
-  // from A with half a part-filled tile per expert (the device holds the true
-  // counts), so the choice depends on the sizes only.
-  const int64_t tiles = ((A + DT - 1) / DT + E / 2) * (d / 256);
-  const int64_t r1 = (tiles + kCUs - 1) / kCUs;      // round times, unsplit
-  const int64_t r2 = (2 * tiles + kCUs - 1) / kCUs;  // half-round times, split
-  return 10 * r2 <= 9 * 2 * r1 ? 2 : 1;
+namespace {
+
+// Makespan (in K steps) of one XCD's 32 CUs taking the listed tiles in order,
+// each CU the next tile as soon as it is free (how workgroups are dispatched
+// here: one per CU, 128-160 KiB of LDS each).
+int64_t xcd_makespan(const int64_t* cost, int n) {
+  constexpr int kXcdCUs = kCUs / 8;
+  int64_t busy[kXcdCUs] = {};
+  for (int i = 0; i < n; ++i) {
+    int c = 0;
+    for (int j = 1; j < kXcdCUs; ++j)
+      if (busy[j] < busy[c]) c = j;
+    busy[c] += cost[i];
+  }
+  int64_t m = 0;
+  for (int j = 0; j < kXcdCUs; ++j) m = busy[j] > m ? busy[j] : m;
+  return m;
 }
+
+struct DownPlan {
+  int nsplit, ksplit;
+};
+
+// The K split of the down projection. Its tiles are few and long (8x7B
+// prefill: 72 per XCD of 448 K steps each, 2.25 per CU), so the last round
+// over the CUs decides much of the time. Splitting each tile's K range into a
+// longer first and a shorter second part, all first parts listed before any
+// second part, lets the short parts fill that last round; the price is one
+// more fixed cost per tile (start-up and epilogue, about 10 us) and a second
+// float32 partial of y for the combine to read (A*d*4 bytes). Measured on
+// MI355X (down kernel + combine): 8x7B 905 us unsplit, 900 split in halves,
+// 853 with 13/16 first parts; T = 8192 with skewed routing 1707 unsplit,
+// 1645 with 3/4; 8x22B (1.875 tiles per CU) 788 unsplit and 823-839 split.
+// So the split is taken when the last round over an XCD's 32 CUs is at most
+// half full, and its point by simulating one XCD's schedule for first parts
+// of 8/16 .. 13/16 of K: the tiles of an XCD estimated from A (every expert
+// one part-filled last m-tile, costed at 65%; the device holds the true
+// counts) and taken in list order, each CU the next one as soon as it is
+// free, 12 K steps of fixed cost per tile. The choice depends on the sizes
+// only.
+DownPlan dma_down_plan(int64_t A, int d, int ffn, int E) {
+  DownPlan p{1, ffn};
+  if (!dma_down_ok(A, d, ffn, E)) return p;
+  constexpr int kFixed = 12;
+  constexpr int64_t kXcdCUs = kCUs / 8;
+  const int nsteps = ffn / 32;
+  const int64_t ntn = d / 256;
+  const int64_t mfull = A / DT - E / 2;
+  const int64_t full = ((mfull > 0 ? mfull : 0) * ntn + 7) / 8;  // tiles per XCD
+  const int64_t part = (static_cast<int64_t>(E) * ntn + 7) / 8;   // part-filled ones
+  const int64_t n = full + part;
+  const int64_t last = n % kXcdCUs;  // tiles in the last round
+  if (n <= kXcdCUs || last == 0 || 2 * last > kXcdCUs || n > 4096) return p;
+  int64_t cost[2 * 4096];
+  auto fill = [&](int64_t* c, int steps) {
+    for (int64_t i = 0; i < full; ++i) c[i] = steps + kFixed;
+    for (int64_t i = 0; i < part; ++i) c[full + i] = steps * 13 / 20 + kFixed;
+  };
+  int64_t best = -1;
+  for (int j = 8; j <= 13; ++j) {
+    const int s0 = nsteps * j / 16 / 4 * 4;  // a multiple of 4 steps
+    if (s0 < 4 || nsteps - s0 < 4) continue;
+    fill(cost, s0);
+    fill(cost + n, nsteps - s0);
+    const int64_t t = xcd_makespan(cost, static_cast<int>(2 * n));
+    if (best < 0 || t < best) {
+      best = t;
+      p = DownPlan{2, s0 * 32};
+    }
+  }
+  return p;
+}
+
+}  // namespace
+
+int dma_down_splits(int64_t A, int d, int ffn, int E) { return dma_down_plan(A, d, ffn, E).nsplit; }
 
 hipError_t launch_down_dma(bool packed, const uint16_t* h, const uint16_t* w2,
                            const int32_t* offsets, int64_t A, int d, int ffn, int E, int nsplit,
                            float* part, hipStream_t s, const float* s2) {
   const int ntn = d / 256;
-  // the most tiles one XCD can get, times 8
-  const int64_t grid_n = 8 * ((A + DT - 1) / DT + E) * nsplit * ((ntn + 7) / 8);
-  const dim3 grid(static_cast<unsigned>(grid_n));
+  const int64_t tiles = ((A + DT - 1) / DT + E) * ntn * nsplit;  // upper bound
+  const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8));
+  if (nsplit != 1 && nsplit != 2) return hipErrorInvalidValue;
+  const DownPlan plan = dma_down_plan(A, d, ffn, E);
+  // (a caller's nsplit is the plan's; otherwise halves on a 128 boundary)
+  const int ksplit = nsplit == 1 ? ffn : plan.nsplit == 2 ? plan.ksplit : ffn / 256 * 128;
   if (s2 && !packed) return hipErrorInvalidValue;  // row scales come with fragment order only
   if (s2)
     hipLaunchKernelGGL((down_dma_kernel<true, true>), grid, dim3(kDmaThreads), 0, s, h, A, w2,
-                       offsets, d, ffn, E, part, ntn, nsplit, s2);
+                       offsets, d, ffn, E, part, ntn, nsplit, ksplit, s2);
   else if (packed)
     hipLaunchKernelGGL((down_dma_kernel<true, false>), grid, dim3(kDmaThreads), 0, s, h, A, w2,
-                       offsets, d, ffn, E, part, ntn, nsplit, s2);
+                       offsets, d, ffn, E, part, ntn, nsplit, ksplit, s2);
   else
     hipLaunchKernelGGL((down_dma_kernel<false, false>), grid, dim3(kDmaThreads), 0, s, h, A, w2,
-                       offsets, d, ffn, E, part, ntn, nsplit, s2);
+                       offsets, d, ffn, E, part, ntn, nsplit, ksplit, s2);
   return hipGetLastError();
 }
 

@@ -42,16 +42,17 @@ def test_workspace_bytes():
     n32 = f(32, 4096, 14336, 8, 2, moe.MOE_F32)                 # h f32, one y
     assert n32 >= A * 14336 * 4 + A * 4096 * 4
     assert f(64, 4096, 14336, 8, 2, moe.MOE_BF16) > n
-    # large batches use the tiled kernels: 4096 tokens of 8x7B fill 2.25
-    # rounds of 256x256 tiles over the GPU's 256 CUs, so the down projection
-    # splits K in two (2.5 rounds of half-length tiles) and leaves two partial
-    # arrays; 8192 tokens at d = 6144 fill 6.4 rounds and leave y as one array
+    # large batches use the 256x256-tile kernels: 4096 tokens of 8x7B give
+    # each XCD's 32 CUs about 72 down tiles, 2.25 rounds, so the down
+    # projection splits K in two and leaves two partial arrays; 3200 tokens at
+    # d = 6144 give about 87 tiles, a last round more than half full, and
+    # leave y as one array
     big = 4096 * 2
     assert f(4096, 4096, 14336, 8, 2, moe.MOE_BF16) >= big * 14336 * 2 + 2 * big * 4096 * 4
-    big = 8192 * 2
-    assert f(8192, 6144, 16384, 8, 2, moe.MOE_BF16) < big * 16384 * 2 + 2 * big * 6144 * 4
-    # the K split needs ffn % 256 == 0 and d % 256 == 0
-    assert f(4096, 4096, 14208, 8, 2, moe.MOE_BF16) < 8192 * 14208 * 2 + 2 * 8192 * 4096 * 4
+    big = 3200 * 2
+    assert f(3200, 6144, 16384, 8, 2, moe.MOE_BF16) < big * 16384 * 2 + 2 * big * 6144 * 4
+    # the K split needs the 256x256-tile down kernel (d % 256 == 0)
+    assert f(4096, 4224, 14336, 8, 2, moe.MOE_BF16) < 8192 * 14336 * 2 + 2 * 8192 * 4224 * 4
     # int8 weights: as bf16 at decode; at prefill sizes (A >= 512 E, the tile
     # kernels) the workspace also holds w1 and w3 widened to bf16 (w2 reuses it)
     assert f(32, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) == n

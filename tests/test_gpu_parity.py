@@ -412,29 +412,48 @@ def test_exact_logit_ties_pick_lower_index(m):
     assert (w == 0.5).all()
 
 
-@pytest.mark.parametrize("d,ffn", [(128, 256), (256, 128), (256, 256), (256, 512), (512, 640),
-                                   (768, 384)])
-def test_prefill_tail_tiles(m, d, ffn):
+def _down_splits(A, d, ffn, E):
+    """Whether the 256x256-tile down kernel splits K (the library's rule,
+    restated): d % 256 == 0, experts averaging two full tiles, and the last
+    round of an XCD's estimated tiles over its 32 CUs at most half full."""
+    if d % 256 or ffn % 128 or A < 512 * E:
+        return False
+    ntn = d // 256
+    n = (max(0, A // 256 - E // 2) * ntn + 7) // 8 + (E * ntn + 7) // 8
+    last = n % 32
+    return n > 32 and last != 0 and 2 * last <= 32
+
+
+TAIL_COUNTS = [784, 816, 848, 896, 898, 0, 1024, 1018]
+
+
+@pytest.mark.parametrize("d,ffn,extra", [(128, 256, 0), (256, 128, 0), (256, 256, 0), (256, 512, 0),
+                                         (512, 640, 0), (768, 384, 0), (2048, 512, 389)])
+def test_prefill_tail_tiles(m, d, ffn, extra):
     """The 256x256-tile kernels (tiled family, used once A >= 512 E: gate/up
     always, down when d % 256 == 0; fragment-order and row-major weights) on hand-made
     routing whose per-expert row counts leave last tiles holding 16, 48, 80,
     128, 130 and 250 rows (every token-fragment count the kernels specialise:
     2, 4, 6, 8 and 0 for the idle half), an empty expert and an exact multiple
-    of 256; K loops of 4 to 24 steps of 32, so that the row-major kernels'
-    12-step cycle runs not at all, once with 4 or 8 steps left, exactly once
-    and twice, and the fragment-order kernels' 4-step trip once to six times. With ffn % 256 == 0 and
-    these few tiles the down projection splits K in two (the workspace holds
-    the two partial arrays), otherwise it does not. Oracle within the bf16
-    bar, and the two weight layouts bit-identical (same MFMA sequence, same
-    split)."""
-    counts = [784, 816, 848, 896, 898, 0, 1024, 1018]
+    of 256 (with extra rows added to every non-empty expert in the last case);
+    K loops of 4 to 24 steps of 32, so that the row-major kernels' 12-step
+    cycle runs not at all, once with 4 or 8 steps left, exactly once and
+    twice, and the fragment-order kernels' 4-step trip once to six times. The
+    last case has enough tiles for the down projection to split K into two
+    parts of unequal length (the workspace then holds the two partial arrays).
+    Oracle within the bf16 bar, and the two weight layouts bit-identical (same
+    MFMA sequence, same split)."""
+    counts = [c + extra if c else 0 for c in TAIL_COUNTS]
     E, k = len(counts), 2
     A = sum(counts)
+    A += A % 2
+    counts[0] += A - sum(counts)
     assert A >= 512 * E
     inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=45 + d)
     sasg = np.random.default_rng(46).permutation(A).astype(np.int32)
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    split = ffn % 256 == 0 and d % 256 == 0
+    split = _down_splits(A, d, ffn, E)
+    assert split == (extra > 0)
     ws = m.moe_workspace_bytes(A // k, d, ffn, E, k, torch.bfloat16)
     assert (ws >= A * ffn * 2 + 2 * A * d * 4) == split
     print(f"[parity] prefill tails d={d} ffn={ffn} A={A} split={split}", flush=True)
