@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_8x7b",
                    help="decode_8x7b (default), prefill_8x7b, skew_8x7b, prefill_8x22b, tiny")
+    p.add_argument("--tokens", type=int, default=0,
+                   help="override the workload's batch size T (same shapes and seed otherwise)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle (e.g. under a profiler)")
     p.add_argument("--variant", type=int, default=0, help="expert-FFN kernel family (0 = auto)")
@@ -286,6 +288,8 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     cfg = dict(gen.CONFIGS[args.workload])
+    if args.tokens > 0:
+        cfg["T"] = args.tokens
     T, d, F, E, k = cfg["T"], cfg["d"], cfg["ffn"], cfg["E"], cfg["k"]
     print(f"[bench] workload {args.workload}: T={T} d={d} ffn={F} E={E} k={k} {cfg['dtype']}",
           file=sys.stderr, flush=True)
@@ -380,7 +384,8 @@ def main():
                  "ms_per_step": round(ms_std, 4)}
 
     cnt = counts.cpu().tolist()
-    workload_key = args.workload + ("+block" if args.block else "") + ("+int8" if int8 else "")
+    workload_key = (args.workload + (f"+T{T}" if args.tokens > 0 else "") +
+                    ("+block" if args.block else "") + ("+int8" if int8 else ""))
     layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt, args.block, int8)
     ms_step = wall * 1e3 / args.steps
     tok_s = T / (ms_step / 1e3)

@@ -134,15 +134,16 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
     }
   } else if (is_bf16(dtype)) {
     const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
+    const int dvariant = moe::choose_down_variant(g_ffn_variant, A, E);
     const bool packed = dtype == MOE_BF16_PACKED;
-    *nsplit_out = moe::down_splits(variant, A, d, ffn, E);
+    *nsplit_out = moe::down_splits(dvariant, A, d, ffn, E);
     err = moe::launch_gate_up_bf16(variant, packed, static_cast<const uint16_t*>(x),
                                    static_cast<const uint16_t*>(w1),
                                    static_cast<const uint16_t*>(w3), offsets, sorted_asg, A, d,
                                    ffn, E, k, static_cast<uint16_t*>(h), s);
     if (err != hipSuccess) return MOE_EHIP;
     if (with_events) stage(3, s);
-    err = moe::launch_down_bf16(variant, packed, static_cast<const uint16_t*>(h),
+    err = moe::launch_down_bf16(dvariant, packed, static_cast<const uint16_t*>(h),
                                 static_cast<const uint16_t*>(w2), offsets, A, d, ffn, E, part, s);
   } else {
     *nsplit_out = 1;
@@ -222,9 +223,9 @@ int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   const int64_t A = T * k;
-  const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
+  const int dvariant = moe::choose_down_variant(g_ffn_variant, A, E);
   const int nsplit = dtype == MOE_INT8_PACKED ? moe::int8_down_splits(A, d, ffn, E)
-                     : is_bf16(dtype)          ? moe::down_splits(variant, A, d, ffn, E)
+                     : is_bf16(dtype)          ? moe::down_splits(dvariant, A, d, ffn, E)
                                                : 1;
   float* part = nsplit > 1 ? reinterpret_cast<float*>(base + L.y) : y;
   int used = 1;

@@ -176,6 +176,7 @@ hipError_t launch_combine(const float* part, int nsplit, const int32_t* asg_pos,
 hipError_t launch_sum_partials(const float* part, int nsplit, int64_t n, float* y, hipStream_t s);
 
 // Resolved expert-FFN kernel family for these sizes (1 streaming, 2 tiled).
-int choose_ffn_variant(int requested, int64_t A, int E);
+int choose_ffn_variant(int requested, int64_t A, int E);   // gate/up
+int choose_down_variant(int requested, int64_t A, int E);  // down
 
 }  // namespace moe

@@ -414,9 +414,9 @@ def test_exact_logit_ties_pick_lower_index(m):
 
 def _down_splits(A, d, ffn, E):
     """Whether the 256x256-tile down kernel splits K (the library's rule,
-    restated): d % 256 == 0, experts averaging two full tiles, and the last
+    restated): d % 256 == 0, experts averaging a full tile, and the last
     round of an XCD's estimated tiles over its 32 CUs at most half full."""
-    if d % 256 or ffn % 128 or A < 512 * E:
+    if d % 256 or ffn % 128 or A < 256 * E:
         return False
     ntn = d // 256
     n = (max(0, A // 256 - E // 2) * ntn + 7) // 8 + (E * ntn + 7) // 8
@@ -430,8 +430,8 @@ TAIL_COUNTS = [784, 816, 848, 896, 898, 0, 1024, 1018]
 @pytest.mark.parametrize("d,ffn,extra", [(128, 256, 0), (256, 128, 0), (256, 256, 0), (256, 512, 0),
                                          (512, 640, 0), (768, 384, 0), (2048, 512, 389)])
 def test_prefill_tail_tiles(m, d, ffn, extra):
-    """The 256x256-tile kernels (tiled family, used once A >= 512 E: gate/up
-    always, down when d % 256 == 0; fragment-order and row-major weights) on hand-made
+    """The 256x256-tile kernels (tiled family; gate/up from A >= 128 E, down
+    from A >= 256 E when d % 256 == 0; fragment-order and row-major weights) on hand-made
     routing whose per-expert row counts leave last tiles holding 16, 48, 80,
     128, 130 and 250 rows (every token-fragment count the kernels specialise:
     2, 4, 6, 8 and 0 for the idle half), an empty expert and an exact multiple
