@@ -81,7 +81,7 @@ const char* moe_strerror(int status);
 /* Bytes of device workspace that moe_forward needs for these sizes; the same
  * amount is always enough for moe_permute and moe_expert_ffn. Pure host
  * function. Returns 0 for invalid arguments. With MOE_INT8_PACKED at prefill
- * sizes (T*k >= 512*E, d and ffn multiples of 128) it includes room for w1
+ * sizes (T*k >= 256*E, d and ffn multiples of 128) it includes room for w1
  * and w3 widened to bfloat16, 2*E*ffn*d*2 bytes (see moe_quantize_weight). */
 size_t moe_workspace_bytes(int64_t T, int d, int ffn, int E, int k, int dtype);
 
@@ -204,7 +204,7 @@ int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* o
  * aligned, non-overlapping buffers, else MOE_ENOTSUP / MOE_EINVAL. With int8
  * weights the streaming expert kernels read the codes directly when experts
  * get few rows (decode, where the weight bytes set the time); when they get
- * many (T*k >= 512*E, d and ffn multiples of 128), the codes of w1 and w3,
+ * many (T*k >= 256*E, d and ffn multiples of 128), the codes of w1 and w3,
  * then of w2, are first widened to bfloat16 (exact) in the workspace and the
  * MFMA tile kernels of the bf16 path run on them, applying the row scales to
  * their finished sums. */

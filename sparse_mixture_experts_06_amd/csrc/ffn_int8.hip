@@ -375,13 +375,14 @@ hipError_t launch_widen_int8(const void* w, int E, int rows, int cols, uint16_t*
   return hipGetLastError();
 }
 
-// widening pays for itself once experts average two full 256-row tiles (the
-// 8x7B prefill batch: 3.2 ms against 11.5 ms on the streaming kernels)
+// widening pays for itself once experts average a full 256-row tile
+// (measured at the 8x7B shape: T = 1024, 256 rows per expert, 1.73 ms against
+// 2.45 on the streaming kernels; T = 512, 128 rows, 1.40 against 1.32)
 bool int8_gate_up_dma(int64_t A, int k, int d, int ffn, int E) {
-  return A >= static_cast<int64_t>(512) * E && dma_gate_up_ok(A, k, d, ffn, E);
+  return A >= static_cast<int64_t>(256) * E && dma_gate_up_ok(A, k, d, ffn, E);
 }
 bool int8_down_dma(int64_t A, int d, int ffn, int E) {
-  return A >= static_cast<int64_t>(512) * E && dma_down_ok(A, d, ffn, E);
+  return A >= static_cast<int64_t>(256) * E && dma_down_ok(A, d, ffn, E);
 }
 
 int int8_down_splits(int64_t A, int d, int ffn, int E) {

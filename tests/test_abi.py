@@ -53,12 +53,14 @@ def test_workspace_bytes():
     assert f(3200, 6144, 16384, 8, 2, moe.MOE_BF16) < big * 16384 * 2 + 2 * big * 6144 * 4
     # the K split needs the 256x256-tile down kernel (d % 256 == 0)
     assert f(4096, 4224, 14336, 8, 2, moe.MOE_BF16) < 8192 * 14336 * 2 + 2 * 8192 * 4224 * 4
-    # int8 weights: as bf16 at decode; at prefill sizes (A >= 512 E, the tile
-    # kernels) the workspace also holds w1 and w3 widened to bf16 (w2 reuses it)
+    # int8 weights: as bf16 at decode; once experts average a full 256-row tile
+    # (A >= 256 E) the workspace also holds w1 and w3 widened to bf16 (w2
+    # reuses it)
     assert f(32, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) == n
-    assert (f(4096, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) -
-            f(4096, 4096, 14336, 8, 2, moe.MOE_BF16)) == 2 * 8 * 14336 * 4096 * 2
-    assert f(2047, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) == f(2047, 4096, 14336, 8, 2,
+    for T in (1024, 4096):
+        assert (f(T, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) -
+                f(T, 4096, 14336, 8, 2, moe.MOE_BF16)) == 2 * 8 * 14336 * 4096 * 2
+    assert f(1023, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) == f(1023, 4096, 14336, 8, 2,
                                                                  moe.MOE_BF16)
     assert f(0, 128, 256, 8, 2, moe.MOE_F32) > 0                # counts/offsets still live
     for bad in [(-1, 128, 256, 8, 2, 0), (4, 128, 256, 8, 9, 0), (4, 128, 256, 33, 2, 0),

@@ -275,16 +275,22 @@ def test_prefill_tiles_many_experts(m, E, k):
     assert rel_err(host(y_q), ref_q) <= OUT_TOL[gen.BF16]
 
 
-@pytest.mark.parametrize("d,ffn", [(256, 512), (384, 640)])
-def test_int8_prefill_matches_oracle(m, d, ffn):
-    """int8 weights at prefill sizes (A >= 512 E): the codes are widened to
+MANY = [784, 816, 848, 896, 898, 0, 1024, 1018]
+AT_THRESHOLD = [300, 120, 260, 400, 0, 256, 511, 201]   # A = 256 E exactly
+
+
+@pytest.mark.parametrize("d,ffn,counts", [(256, 512, MANY), (384, 640, MANY),
+                                          (256, 512, AT_THRESHOLD)])
+def test_int8_prefill_matches_oracle(m, d, ffn, counts):
+    """int8 weights at prefill sizes (A >= 256 E): the codes are widened to
     bf16 in fragment order in the workspace and the 256x256-tile kernels apply
     the row scales to their sums. Hand-made routing with the tail-tile row
     counts (expert step alone), then the fused layer on the same weights with
     its own routing; both against the oracle on its dequantized weights. At
     d = 384 the down projection stays on the streaming int8 kernel (the tile
-    kernel needs d % 256 == 0); at d = 256, ffn = 512 it splits K in two."""
-    counts = [784, 816, 848, 896, 898, 0, 1024, 1018]
+    kernel needs d % 256 == 0); at d = 256, ffn = 512 it splits K in two.
+    The last case sits exactly on the widening threshold, with experts on
+    both sides of one 256-row tile."""
     E, k = len(counts), 2
     A = sum(counts)
     inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=60 + d)
@@ -293,7 +299,7 @@ def test_int8_prefill_matches_oracle(m, d, ffn):
     ws_i8 = m.moe_workspace_bytes(A // k, d, ffn, E, k, m.MOE_INT8_PACKED)
     ws_b = m.moe_workspace_bytes(A // k, d, ffn, E, k, torch.bfloat16)
     assert ws_i8 - ws_b == 2 * E * ffn * d * 2  # widened w1 and w3 (w2 reuses them)
-    print(f"[parity] int8 prefill d={d} ffn={ffn} A={A}", flush=True)
+    print(f"[parity] int8 prefill d={d} ffn={ffn} counts={counts}", flush=True)
     dev = to_device(inp)
     qw = m.QuantizedWeights(dev["w1"], dev["w3"], dev["w2"])
     deq = _quantized(inp)
