@@ -80,9 +80,10 @@ const char* moe_strerror(int status);
 
 /* Bytes of device workspace that moe_forward needs for these sizes; the same
  * amount is always enough for moe_permute and moe_expert_ffn. Pure host
- * function. Returns 0 for invalid arguments. With MOE_INT8_PACKED at prefill
- * sizes (T*k >= 256*E, d and ffn multiples of 128) it includes room for w1
- * and w3 widened to bfloat16, 2*E*ffn*d*2 bytes (see moe_quantize_weight). */
+ * function. Returns 0 for invalid arguments. With MOE_INT8_PACKED at large
+ * prefill sizes (d and ffn multiples of 128) it includes room for weights
+ * widened to bfloat16 (see moe_quantize_weight): E*ffn*d*2 bytes for w2 from
+ * T*k >= 1024*E (d % 256 == 0), 2*E*ffn*d*2 for w1 and w3 from T*k >= 1536*E. */
 size_t moe_workspace_bytes(int64_t T, int d, int ffn, int E, int k, int dtype);
 
 /* Router + scoring (nnterp page, Notes: softmax over the experts in float32,
@@ -203,11 +204,13 @@ int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* o
  * dtype must be MOE_BF16; rows % 16 == 0 and cols % 64 == 0 and 16-byte
  * aligned, non-overlapping buffers, else MOE_ENOTSUP / MOE_EINVAL. With int8
  * weights the streaming expert kernels read the codes directly when experts
- * get few rows (decode, where the weight bytes set the time); when they get
- * many (T*k >= 256*E, d and ffn multiples of 128), the codes of w1 and w3,
- * then of w2, are first widened to bfloat16 (exact) in the workspace and the
- * MFMA tile kernels of the bf16 path run on them, applying the row scales to
- * their finished sums. */
+ * get few rows (decode, where the weight bytes set the time); beyond that a
+ * tiled MFMA kernel converts them to bfloat16 operands in registers (gate/up
+ * when ffn % 128 == 0, down when d % 256 == 0); for large prefill batches
+ * (T*k >= 1536*E for w1 and w3, >= 1024*E for w2) the codes are first widened
+ * to bfloat16 (exact) in the workspace and the direct-to-LDS tile kernels of
+ * the bf16 path run on them. Every kernel applies the row scales to its
+ * finished sums. */
 size_t moe_quantized_weight_bytes(int E, int rows, int cols);
 int moe_quantize_weight(const void* w, int dtype, int E, int rows, int cols, void* out,
                         void* stream);

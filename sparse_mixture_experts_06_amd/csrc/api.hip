@@ -103,11 +103,14 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
   hipError_t err;
   if (dtype == MOE_INT8_PACKED) {
     // int8 weights: the streaming kernels on the codes (few rows per expert),
-    // or the codes widened to bf16 and the direct-to-LDS kernels with row
-    // scales (many rows per expert)
-    *nsplit_out = moe::int8_down_splits(A, d, ffn, E);
+    // the tiled kernel widening its operands in registers (more), or the
+    // codes widened to bf16 in the workspace and the direct-to-LDS kernels
+    // with row scales (many rows per expert)
+    const int variant = moe::choose_int8_ffn_variant(g_ffn_variant, A, E);
+    const int dvariant = moe::choose_int8_down_variant(g_ffn_variant, A, E);
+    *nsplit_out = moe::int8_down_splits(dvariant, A, d, ffn, E);
     uint16_t* wb = static_cast<uint16_t*>(wide);
-    if (moe::int8_gate_up_dma(A, k, d, ffn, E)) {
+    if (variant != 1 && moe::int8_gate_up_dma(A, k, d, ffn, E)) {
       uint16_t* w3b = wb + static_cast<size_t>(E) * ffn * d;
       err = moe::launch_widen_int8(w1, E, ffn, d, wb, s);
       if (err == hipSuccess) err = moe::launch_widen_int8(w3, E, ffn, d, w3b, s);
@@ -117,20 +120,20 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
                                       moe::int8_scales(w1, E, ffn, d),
                                       moe::int8_scales(w3, E, ffn, d));
     } else {
-      err = moe::launch_gate_up_int8(static_cast<const uint16_t*>(x), w1, w3, offsets, sorted_asg,
-                                     d, ffn, E, k, static_cast<uint16_t*>(h), s);
+      err = moe::launch_gate_up_int8(variant, static_cast<const uint16_t*>(x), w1, w3, offsets,
+                                     sorted_asg, A, d, ffn, E, k, static_cast<uint16_t*>(h), s);
     }
     if (err != hipSuccess) return MOE_EHIP;
     if (with_events) stage(3, s);
-    if (moe::int8_down_dma(A, d, ffn, E)) {
+    if (dvariant != 1 && moe::int8_down_dma(A, d, ffn, E)) {
       // (stream order: gate/up has finished with the widened w1 and w3)
       err = moe::launch_widen_int8(w2, E, d, ffn, wb, s);
       if (err == hipSuccess)
         err = moe::launch_down_dma(true, static_cast<const uint16_t*>(h), wb, offsets, A, d, ffn,
                                    E, *nsplit_out, part, s, moe::int8_scales(w2, E, d, ffn));
     } else {
-      err = moe::launch_down_int8(static_cast<const uint16_t*>(h), w2, offsets, A, d, ffn, E,
-                                  *nsplit_out, part, s);
+      err = moe::launch_down_int8(dvariant, static_cast<const uint16_t*>(h), w2, offsets, A, d,
+                                  ffn, E, *nsplit_out, part, s);
     }
   } else if (is_bf16(dtype)) {
     const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
@@ -223,10 +226,12 @@ int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   const int64_t A = T * k;
-  const int dvariant = moe::choose_down_variant(g_ffn_variant, A, E);
-  const int nsplit = dtype == MOE_INT8_PACKED ? moe::int8_down_splits(A, d, ffn, E)
-                     : is_bf16(dtype)          ? moe::down_splits(dvariant, A, d, ffn, E)
-                                               : 1;
+  const int nsplit =
+      dtype == MOE_INT8_PACKED
+          ? moe::int8_down_splits(moe::choose_int8_down_variant(g_ffn_variant, A, E), A, d, ffn, E)
+      : is_bf16(dtype)
+          ? moe::down_splits(moe::choose_down_variant(g_ffn_variant, A, E), A, d, ffn, E)
+          : 1;
   float* part = nsplit > 1 ? reinterpret_cast<float*>(base + L.y) : y;
   int used = 1;
   st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, part, base + L.h,

@@ -51,6 +51,22 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// One 32-deep MFMA operand from a lane's 16 bytes of int8 weight codes: half
+// 0 takes bytes 0-7, half 1 bytes 8-15. Each code is sign-extended to float32
+// (v_cvt_f32_i32 with a byte select); a code is a small integer, so the top
+// half of its float32 is its exact bfloat16 encoding, and v_perm_b32 joins
+// two of those halves into one dword.
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t q, int b) {
+  const float lo = static_cast<float>(static_cast<int32_t>(q << (24 - 8 * b)) >> 24);
+  const float hi = static_cast<float>(static_cast<int32_t>(q << (16 - 8 * b)) >> 24);
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+__device__ __forceinline__ u32x4 i8_operand(u32x4 q, int half) {
+  const uint32_t a = q[2 * half], b = q[2 * half + 1];
+  return u32x4{i8x2_to_bf16x2(a, 0), i8x2_to_bf16x2(a, 2), i8x2_to_bf16x2(b, 0),
+               i8x2_to_bf16x2(b, 2)};
+}
+
 // element offset of w[e][n][k] (k a multiple of 8) of an [E, N, K] weight in
 // the standard layout (PACKED false) or in fragment order (PACKED true: 16-row
 // x 32-k fragments of 1 KiB in MFMA lane order, ordered expert, row tile, k step)
@@ -117,6 +133,16 @@ hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const u
                             const int32_t* offsets, int64_t A, int d, int ffn, int E, float* part,
                             hipStream_t s);
 int down_splits(int variant, int64_t A, int d, int ffn, int E);
+// int8 codes (16-row x 64-k blocks) with float32 row scales on the tiled
+// weights-in-registers kernel, operands widened in registers: gate/up needs
+// ffn % 128 == 0, down d % 256 == 0 (one partial, no K split)
+hipError_t launch_gate_up_w8_tiled(const uint16_t* x, const void* q1, const void* q3,
+                                  const float* s1, const float* s3, const int32_t* offsets,
+                                  const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
+                                  int k, uint16_t* h, hipStream_t s);
+hipError_t launch_down_w8_tiled(const uint16_t* h, const void* q2, const float* s2,
+                               const int32_t* offsets, int64_t A, int d, int ffn, int E,
+                               float* part, hipStream_t s);
 
 // gate/up and down for many rows per expert with direct-to-LDS loads
 // (ffn_dma.hip), for fragment-order (packed) or row-major weights: the sizes
@@ -136,7 +162,8 @@ hipError_t launch_down_dma(bool packed, const uint16_t* h, const uint16_t* w2,
                            float* part, hipStream_t s, const float* s2 = nullptr);
 // weight-only int8 experts (ffn_int8.hip): bytes of one quantized matrix
 // (codes, then float32 row scales at the next 256-byte boundary), the
-// quantizer, and the streaming gate/up and down kernels that read it
+// quantizer, and the gate/up and down launchers that read it (`variant`
+// resolved as for bf16: 1 streaming, 2 tiled)
 size_t int8_weight_bytes(int E, int rows, int cols);
 // the row scales inside a quantized matrix; prefill: whether gate/up and down
 // widen the codes and run the direct-to-LDS kernels, the down K split, and
@@ -144,17 +171,20 @@ size_t int8_weight_bytes(int E, int rows, int cols);
 const float* int8_scales(const void* w, int E, int rows, int cols);
 hipError_t launch_widen_int8(const void* w, int E, int rows, int cols, uint16_t* out,
                              hipStream_t s);
+int choose_int8_ffn_variant(int requested, int64_t A, int E);   // gate/up
+int choose_int8_down_variant(int requested, int64_t A, int E);  // down
 bool int8_gate_up_dma(int64_t A, int k, int d, int ffn, int E);
 bool int8_down_dma(int64_t A, int d, int ffn, int E);
-int int8_down_splits(int64_t A, int d, int ffn, int E);
+int int8_down_splits(int variant, int64_t A, int d, int ffn, int E);
 size_t int8_wide_bytes(int64_t A, int k, int d, int ffn, int E);
 hipError_t launch_quantize_int8(const uint16_t* w, int E, int rows, int cols, void* out,
                                 hipStream_t s);
-hipError_t launch_gate_up_int8(const uint16_t* x, const void* w1, const void* w3,
-                               const int32_t* offsets, const int32_t* sorted_asg, int d, int ffn,
-                               int E, int k, uint16_t* h, hipStream_t s);
-hipError_t launch_down_int8(const uint16_t* h, const void* w2, const int32_t* offsets, int64_t A,
-                            int d, int ffn, int E, int nsplit, float* part, hipStream_t s);
+hipError_t launch_gate_up_int8(int variant, const uint16_t* x, const void* w1, const void* w3,
+                               const int32_t* offsets, const int32_t* sorted_asg, int64_t A,
+                               int d, int ffn, int E, int k, uint16_t* h, hipStream_t s);
+hipError_t launch_down_int8(int variant, const uint16_t* h, const void* w2,
+                            const int32_t* offsets, int64_t A, int d, int ffn, int E, int nsplit,
+                            float* part, hipStream_t s);
 // standard [E, R, C] bf16 -> fragment order (16-row x 32-column fragments)
 hipError_t launch_pack_bf16(const uint16_t* w, int E, int R, int C, uint16_t* out, hipStream_t s);
 

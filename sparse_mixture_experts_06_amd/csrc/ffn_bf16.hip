@@ -563,16 +563,20 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
 // Needs N % 256 == 0 (down) or ffn % 128 == 0 (gate/up). Used with
 // fragment-order weights; with the standard layout each weight load would be
 // 16 rows x 64 bytes, and staging both operands through LDS is faster there.
+// W8: int8 weight codes in their 16-row x 64-k blocks (one 16-byte lane load
+// per block holds the lane's operands of two 32-wide K steps), converted to
+// bf16 operands in registers; the ring then holds RING/2 64-wide stages and
+// the epilogue multiplies each row's sum by its scale (sa: w1 or w2, sb: w3).
 
 constexpr int gcd_i(int a, int b) { return b == 0 ? a : gcd_i(b, a % b); }
 constexpr int lcm_i(int a, int b) { return a / gcd_i(a, b) * b; }
 
-template <bool GATE_UP, bool PACKED, int RING, int OCC, int XSETS>
+template <bool GATE_UP, bool PACKED, bool W8, int RING, int OCC, int XSETS>
 __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
-    const uint16_t* __restrict__ act, const uint16_t* __restrict__ wa,
-    const uint16_t* __restrict__ wb, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_asg, int K, int N, int E, int ktop,
-    void* __restrict__ out, int ntn) {
+    const uint16_t* __restrict__ act, const void* __restrict__ wa, const void* __restrict__ wb,
+    const float* __restrict__ sa, const float* __restrict__ sb,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_asg, int K, int N,
+    int E, int ktop, void* __restrict__ out, int ntn) {
   int e, beg, M, m0, nt, sp;
   if (!decode_tile(offsets, E, ntn, 1, e, beg, M, m0, nt, sp)) return;
 
@@ -589,10 +593,11 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
   // registers) plus one per-lane offset
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint16_t* wbase[4];
+  const int8_t* qbase[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int row;
-    const uint16_t* base;
+    const void* base;
     if constexpr (GATE_UP) {
       row = nt * 128 + wv * 32 + (i & 1) * 16;
       base = (i < 2) ? wa : wb;
@@ -600,7 +605,12 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
       row = nt * 256 + wv * 64 + i * 16;
       base = wa;
     }
-    wbase[i] = base + wofs<PACKED>(e, row, 0, N, K);
+    if constexpr (W8)
+      qbase[i] = static_cast<const int8_t*>(base) +
+                 (static_cast<size_t>(e) * (N >> 4) + (row >> 4)) * static_cast<size_t>(K >> 6) *
+                     1024 + lane * 16;
+    else
+      wbase[i] = static_cast<const uint16_t*>(base) + wofs<PACKED>(e, row, 0, N, K);
   }
   const int wlane = static_cast<int>(wofs<PACKED>(0, fr, fg * 8, N, K));
 
@@ -629,13 +639,20 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
   const int last = nk - 1;
   const int nsteps = 2 * nk;  // 32-wide K steps
   // weights: a ring of RING K32 slots; the loads of step t+RING are issued
-  // as soon as step t has used its slot ((RING-1)/2 stages of lead time)
-  u32x4 wr[RING][4];   // [slot][row tile]
+  // as soon as step t has used its slot ((RING-1)/2 stages of lead time).
+  // W8: RING/2 slots of one 64-wide stage each, refilled when a stage is done.
+  constexpr int WSLOTS = W8 ? RING / 2 : RING;
+  u32x4 wr[WSLOTS][4];  // [slot][row tile]
   u32x4 rx[XSETS][4];   // token chunks in flight (XSETS stages)
-  auto issue_w = [&](int slot, int t) {
+  auto issue_w = [&](int slot, int t) {  // t: K32 step, or 64-wide stage (W8)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      wr[slot][i] = ldw<PACKED>(wbase[i] + static_cast<size_t>(t) * ST + wlane);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (W8)
+        wr[slot][i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(qbase[i] + static_cast<size_t>(t) * 1024));
+      else
+        wr[slot][i] = ldw<PACKED>(wbase[i] + static_cast<size_t>(t) * ST + wlane);
+    }
   };
   auto issue_x = [&](int set, int kb) {
 #pragma unroll
@@ -652,13 +669,20 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
   // weights of steps 0..RING-1 in flight (indices past the end clamp to the
   // last one); token stage s lives in register set s mod XSETS
 #pragma unroll
-  for (int t = 0; t < RING; ++t) issue_w(t, min(t, nsteps - 1));
+  for (int t = 0; t < WSLOTS; ++t) issue_w(t, min(t, (W8 ? nk : nsteps) - 1));
   issue_x(0, 0);
 #pragma unroll
   for (int q = 1; q < XSETS; ++q) issue_x(q, min(q, last));
   stash(0, 0);
   issue_x(0, min(XSETS, last));
   lds_barrier();
+  // W8: bf16 operands of steps t and t+1 (set t mod 2); each step converts
+  // the next one's while its own MFMAs run
+  u32x4 wcv[2][4];
+  if constexpr (W8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wcv[0][i] = i8_operand(wr[0][i], 0);
+  }
 
   // K32 step t (T = t mod U, compile-time; U a multiple of 4, of RING and of
   // 2*XSETS): stage kb = t / 2 lives in LDS buffer kb mod 2, half t mod 2 of it
@@ -666,7 +690,7 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
   int t0 = 0;
   auto step_body = [&](auto tm) {
     constexpr int T = decltype(tm)::value;
-    constexpr int SLOT = T % RING;
+    constexpr int SLOT = W8 ? (T >> 1) % WSLOTS : T % RING;
     constexpr int P = (T >> 1) & 1;  // LDS buffer of this stage
     constexpr int S = T & 1;         // which 32-wide half of the 64-wide stage
     constexpr int XN = ((T >> 1) + 1) % XSETS;  // token set of the next stage
@@ -674,6 +698,9 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
     const int kb = t >> 1;
     if (t < nsteps) {
       const int c = S * 4 + fg;
+      u32x4 wf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wf[i] = W8 ? wcv[T & 1][i] : wr[SLOT][i];
 #pragma unroll
       for (int jh = 0; jh < 2; ++jh) {  // token fragments four at a time
         u32x4 b[4];
@@ -684,11 +711,20 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][jh * 4 + j] = mfma16x16x32(wr[SLOT][i], b[j], acc[i][jh * 4 + j]);
+            acc[i][jh * 4 + j] = mfma16x16x32(wf[i], b[j], acc[i][jh * 4 + j]);
+      }
+      if constexpr (W8) {
+        constexpr int TN = T + 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          wcv[TN & 1][i] = i8_operand(wr[(TN >> 1) % WSLOTS][i], TN & 1);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    issue_w(SLOT, min(t + RING, nsteps - 1));
+    if constexpr (!W8)
+      issue_w(SLOT, min(t + RING, nsteps - 1));
+    else if constexpr (S == 1)
+      issue_w(SLOT, min(kb + WSLOTS, last));
     if constexpr (S == 1) {
       // end of stage kb: tokens of stage kb+1 (in registers for XSETS stages)
       // go to the other buffer; tokens of stage kb+1+XSETS start loading
@@ -700,7 +736,18 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
   for (; t0 < nsteps; t0 += U) unrolled(step_body, std::make_integer_sequence<int, U>{});
 
   // epilogue: lane holds token column fr of each 16x16 tile and weight rows
-  // 4*fg .. 4*fg+3 of it
+  // 4*fg .. 4*fg+3 of it (W8: their scales, loaded once)
+  f32x4 sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc[i] = f32x4{1.f, 1.f, 1.f, 1.f};
+    if constexpr (W8) {
+      const int n = GATE_UP ? nt * 128 + wave * 32 + (i & 1) * 16 + 4 * fg
+                            : nt * 256 + wave * 64 + i * 16 + 4 * fg;
+      sc[i] = *reinterpret_cast<const f32x4*>((GATE_UP && i >= 2 ? sb : sa) +
+                                              static_cast<size_t>(e) * N + n);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int m = m0 + j * 16 + fr;
@@ -709,8 +756,12 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int n = nt * 128 + wave * 32 + i * 16 + 4 * fg;
-        const f32x4 gt = acc[i][j];
-        const f32x4 up = acc[i + 2][j];
+        f32x4 gt = acc[i][j];
+        f32x4 up = acc[i + 2][j];
+        if constexpr (W8) {
+          gt *= sc[i];
+          up *= sc[i + 2];
+        }
         uint2 v;
         v.x = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
         v.y = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
@@ -721,8 +772,10 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = nt * 256 + wave * 64 + i * 16 + 4 * fg;
+        f32x4 v = acc[i][j];
+        if constexpr (W8) v *= sc[i];
         *reinterpret_cast<f32x4*>(static_cast<float*>(out) + static_cast<size_t>(beg + m) * N + n) =
-            acc[i][j];
+            v;
       }
     }
   }
@@ -730,6 +783,8 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
 
 // weight ring depth and workgroups per CU of wtiled_kernel
 constexpr int kWRing = 8, kWOcc = 1, kWXSets = 2;
+// int8 codes: ring depth in 32-wide K steps (RING/2 slots of 64)
+constexpr int kW8Ring = 8;
 
 inline unsigned tiled_grid(int64_t A, int E, int ntn, int nsplit = 1) {
   const int64_t mt = (A + BM - 1) / BM + E;
@@ -755,9 +810,10 @@ hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, cons
     return launch_gate_up_dma(PACKED, x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s);
   } else if (PACKED && ffn % 128 == 0) {
     const int ntn = ffn / 128;
-    hipLaunchKernelGGL((wtiled_kernel<true, PACKED, kWRing, kWOcc, kWXSets>), dim3(tiled_grid(A, E, ntn)),
-                       dim3(kTiledThreads), 0, s, x, w1, w3, offsets, sorted_asg, d, ffn, E, k,
-                       static_cast<void*>(h), ntn);
+    hipLaunchKernelGGL((wtiled_kernel<true, PACKED, false, kWRing, kWOcc, kWXSets>),
+                       dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0, s, x, w1, w3,
+                       static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
+                       offsets, sorted_asg, d, ffn, E, k, static_cast<void*>(h), ntn);
   } else {
     const int ntn = ffn / 64;
     hipLaunchKernelGGL((tiled_kernel<true, PACKED>), dim3(tiled_grid(A, E, ntn)),
@@ -790,9 +846,10 @@ hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const i
     return launch_down_dma(PACKED, h, w2, offsets, A, d, ffn, E, nsplit, part, s);
   } else if (PACKED && d % 256 == 0 && nsplit == 1) {
     const int ntn = d / 256;
-    hipLaunchKernelGGL((wtiled_kernel<false, PACKED, kWRing, kWOcc, kWXSets>), dim3(tiled_grid(A, E, ntn)),
-                       dim3(kTiledThreads), 0, s, h, w2, w2, offsets,
-                       static_cast<const int32_t*>(nullptr), ffn, d, E, 1,
+    hipLaunchKernelGGL((wtiled_kernel<false, PACKED, false, kWRing, kWOcc, kWXSets>),
+                       dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0, s, h, w2, w2,
+                       static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
+                       offsets, static_cast<const int32_t*>(nullptr), ffn, d, E, 1,
                        static_cast<void*>(part), ntn);
   } else {
     const int ntn = (d + BN - 1) / BN;
@@ -829,6 +886,29 @@ int down_splits(int variant, int64_t A, int d, int ffn, int E) {
   // weight layout)
   if (variant == 1) return A <= 4096 ? 2 : 1;
   return dma_down_splits(A, d, ffn, E);
+}
+
+hipError_t launch_gate_up_w8_tiled(const uint16_t* x, const void* q1, const void* q3,
+                                  const float* s1, const float* s3, const int32_t* offsets,
+                                  const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
+                                  int k, uint16_t* h, hipStream_t s) {
+  const int ntn = ffn / 128;
+  hipLaunchKernelGGL((wtiled_kernel<true, true, true, kW8Ring, kWOcc, kWXSets>),
+                     dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0, s, x, q1, q3, s1, s3,
+                     offsets, sorted_asg, d, ffn, E, k, static_cast<void*>(h), ntn);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_w8_tiled(const uint16_t* h, const void* q2, const float* s2,
+                               const int32_t* offsets, int64_t A, int d, int ffn, int E,
+                               float* part, hipStream_t s) {
+  const int ntn = d / 256;
+  hipLaunchKernelGGL((wtiled_kernel<false, true, true, kW8Ring, kWOcc, kWXSets>),
+                     dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0, s, h, q2, q2, s2,
+                     static_cast<const float*>(nullptr), offsets,
+                     static_cast<const int32_t*>(nullptr), ffn, d, E, 1, static_cast<void*>(part),
+                     ntn);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack_bf16(const uint16_t* w, int E, int R, int C, uint16_t* out, hipStream_t s) {

@@ -50,15 +50,9 @@ __device__ __forceinline__ size_t w8_block(int e, int rt, int s, int rows, int c
 }
 
 // 16 int8 codes -> two MFMA operands of 8 bf16 each (bytes 0-7 and 8-15)
-__device__ __forceinline__ uint32_t cvt2(uint32_t q, int b) {
-  const float lo = static_cast<float>(static_cast<int32_t>(q << (24 - 8 * b)) >> 24);
-  const float hi = static_cast<float>(static_cast<int32_t>(q << (16 - 8 * b)) >> 24);
-  // both are small integers: the top 16 bits are their exact bfloat16 encoding
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-}
 __device__ __forceinline__ void cvt16(u32x4 q, u32x4& lo, u32x4& hi) {
-  lo = u32x4{cvt2(q[0], 0), cvt2(q[0], 2), cvt2(q[1], 0), cvt2(q[1], 2)};
-  hi = u32x4{cvt2(q[2], 0), cvt2(q[2], 2), cvt2(q[3], 0), cvt2(q[3], 2)};
+  lo = i8_operand(q, 0);
+  hi = i8_operand(q, 1);
 }
 
 __device__ __forceinline__ u32x4 ldw8(const int8_t* p) {
@@ -375,18 +369,37 @@ hipError_t launch_widen_int8(const void* w, int E, int rows, int cols, uint16_t*
   return hipGetLastError();
 }
 
-// widening pays for itself once experts average a full 256-row tile
-// (measured at the 8x7B shape: T = 1024, 256 rows per expert, 1.73 ms against
-// 2.45 on the streaming kernels; T = 512, 128 rows, 1.40 against 1.32)
-bool int8_gate_up_dma(int64_t A, int k, int d, int ffn, int E) {
-  return A >= static_cast<int64_t>(256) * E && dma_gate_up_ok(A, k, d, ffn, E);
+// Kernel family for int8 weights when the caller does not force one. The
+// streaming kernels stay ahead of the tiled one longer than with bf16 weights
+// (half the bytes per pass over the weights). Measured at the 8x7B shape
+// (T tokens, k = 2, E = 8; us, streaming vs tiled): gate/up 242 vs 301 at 32
+// rows per expert, 333 vs 293 at 40; down 192 vs 229 at 48, 249 vs 228 at 56.
+int choose_int8_ffn_variant(int requested, int64_t A, int E) {
+  if (requested == 1 || requested == 2) return requested;
+  return (A <= static_cast<int64_t>(36) * E) ? 1 : 2;
 }
-bool int8_down_dma(int64_t A, int d, int ffn, int E) {
-  return A >= static_cast<int64_t>(256) * E && dma_down_ok(A, d, ffn, E);
+int choose_int8_down_variant(int requested, int64_t A, int E) {
+  if (requested == 1 || requested == 2) return requested;
+  return (A <= static_cast<int64_t>(52) * E) ? 1 : 2;
 }
 
-int int8_down_splits(int64_t A, int d, int ffn, int E) {
-  return int8_down_dma(A, d, ffn, E) ? dma_down_splits(A, d, ffn, E) : down_splits(1, A, d, ffn, E);
+// Widening the codes into the workspace and running the direct-to-LDS tiles
+// overtakes the tiled kernel's in-register widening only for large batches,
+// since the widening itself streams the codes and writes twice their bytes
+// (8x7B shape, us, tiled vs widened): gate/up 1930 vs 2082 at 1024 rows per
+// expert, 2797 vs 2775 at 1536; down 861 vs 869 at 768, 1053 vs 1042 at 1024,
+// 1478 vs 1398 at 1536.
+bool int8_gate_up_dma(int64_t A, int k, int d, int ffn, int E) {
+  return A >= static_cast<int64_t>(1536) * E && dma_gate_up_ok(A, k, d, ffn, E);
+}
+bool int8_down_dma(int64_t A, int d, int ffn, int E) {
+  return A >= static_cast<int64_t>(1024) * E && dma_down_ok(A, d, ffn, E);
+}
+
+int int8_down_splits(int variant, int64_t A, int d, int ffn, int E) {
+  if (variant != 1 && int8_down_dma(A, d, ffn, E)) return dma_down_splits(A, d, ffn, E);
+  if (variant != 1 && d % 256 == 0) return 1;  // tiled kernel
+  return down_splits(1, A, d, ffn, E);
 }
 
 size_t int8_wide_bytes(int64_t A, int k, int d, int ffn, int E) {
@@ -408,14 +421,16 @@ hipError_t launch_quantize_int8(const uint16_t* w, int E, int rows, int cols, vo
   return hipGetLastError();
 }
 
-hipError_t launch_gate_up_int8(const uint16_t* x, const void* w1, const void* w3,
-                               const int32_t* offsets, const int32_t* sorted_asg, int d, int ffn,
-                               int E, int k, uint16_t* h, hipStream_t s) {
+hipError_t launch_gate_up_int8(int variant, const uint16_t* x, const void* w1, const void* w3,
+                               const int32_t* offsets, const int32_t* sorted_asg, int64_t A,
+                               int d, int ffn, int E, int k, uint16_t* h, hipStream_t s) {
   const size_t cb = align256(static_cast<size_t>(E) * ffn * d);
   const int8_t* q1 = static_cast<const int8_t*>(w1);
   const int8_t* q3 = static_cast<const int8_t*>(w3);
   const float* s1 = reinterpret_cast<const float*>(static_cast<const char*>(w1) + cb);
   const float* s3 = reinterpret_cast<const float*>(static_cast<const char*>(w3) + cb);
+  if (variant != 1 && ffn % 128 == 0)
+    return launch_gate_up_w8_tiled(x, q1, q3, s1, s3, offsets, sorted_asg, A, d, ffn, E, k, h, s);
   if (ffn % (16 * kW8GateUpRT) != 0)
     hipLaunchKernelGGL((gate_up_w8_kernel<1, kW8GateUpU>), dim3(ffn / 16, E), dim3(kWave * kW8Waves),
                        0, s, x, q1, s1, q3, s3, offsets, sorted_asg, d, ffn, k, h);
@@ -426,11 +441,16 @@ hipError_t launch_gate_up_int8(const uint16_t* x, const void* w1, const void* w3
   return hipGetLastError();
 }
 
-hipError_t launch_down_int8(const uint16_t* h, const void* w2, const int32_t* offsets, int64_t A,
-                            int d, int ffn, int E, int nsplit, float* part, hipStream_t s) {
+hipError_t launch_down_int8(int variant, const uint16_t* h, const void* w2,
+                            const int32_t* offsets, int64_t A, int d, int ffn, int E, int nsplit,
+                            float* part, hipStream_t s) {
   const size_t cb = align256(static_cast<size_t>(E) * d * ffn);
   const int8_t* q2 = static_cast<const int8_t*>(w2);
   const float* s2 = reinterpret_cast<const float*>(static_cast<const char*>(w2) + cb);
+  if (variant != 1 && d % 256 == 0) {
+    if (nsplit != 1) return hipErrorInvalidValue;
+    return launch_down_w8_tiled(h, q2, s2, offsets, A, d, ffn, E, part, s);
+  }
   const int rt = (d % (16 * kW8DownRT) == 0) ? kW8DownRT : 1;
   const unsigned blocks = static_cast<unsigned>((d / (16 * rt) * nsplit + kW8Waves - 1) / kW8Waves);
   if (rt != kW8DownRT) {

@@ -53,15 +53,14 @@ def test_workspace_bytes():
     assert f(3200, 6144, 16384, 8, 2, moe.MOE_BF16) < big * 16384 * 2 + 2 * big * 6144 * 4
     # the K split needs the 256x256-tile down kernel (d % 256 == 0)
     assert f(4096, 4224, 14336, 8, 2, moe.MOE_BF16) < 8192 * 14336 * 2 + 2 * 8192 * 4224 * 4
-    # int8 weights: as bf16 at decode; once experts average a full 256-row tile
-    # (A >= 256 E) the workspace also holds w1 and w3 widened to bf16 (w2
-    # reuses it)
+    # int8 weights: as bf16, except for large prefill batches, where the
+    # workspace also holds w2 widened to bf16 (A >= 1024 E), then w1 and w3
+    # (A >= 1536 E; w2 reuses their room)
+    m = 8 * 14336 * 4096 * 2
     assert f(32, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) == n
-    for T in (1024, 4096):
+    for T, wide in ((4095, 0), (4096, m), (6143, m), (6144, 2 * m), (8192, 2 * m)):
         assert (f(T, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) -
-                f(T, 4096, 14336, 8, 2, moe.MOE_BF16)) == 2 * 8 * 14336 * 4096 * 2
-    assert f(1023, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) == f(1023, 4096, 14336, 8, 2,
-                                                                 moe.MOE_BF16)
+                f(T, 4096, 14336, 8, 2, moe.MOE_BF16)) == wide, T
     assert f(0, 128, 256, 8, 2, moe.MOE_F32) > 0                # counts/offsets still live
     for bad in [(-1, 128, 256, 8, 2, 0), (4, 128, 256, 8, 9, 0), (4, 128, 256, 33, 2, 0),
                 (4, 0, 256, 8, 2, 0), (4, 128, 256, 8, 0, 0), (4, 128, 256, 8, 2, 7),

@@ -1,6 +1,6 @@
 """CPU-only checks of the machine code hipcc makes for the prefill gate/up
-and down kernels (csrc/ffn_dma.hip), compiled with the exact flags the build
-uses.
+and down kernels (csrc/ffn_dma.hip), and for the tiled kernel on int8 codes
+(csrc/ffn_bf16.hip, last test), compiled with the exact flags the build uses.
 
 Their main loop is scheduled by hand; the properties its speed rests on are
 properties of the generated gfx950 code, so they are checked there: every
@@ -115,3 +115,38 @@ def test_kernels_have_no_scratch_and_two_waves_per_simd(asm):
     # the 8-wave workgroup needs two waves per SIMD: at most 256 registers per lane each
     occ = [int(o) for o in re.findall(r"; Occupancy: (\d+)", asm)]
     assert occ and min(occ) >= 2, occ
+
+
+@pytest.fixture(scope="module")
+def asm_bf16(tmp_path_factory):
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    out = str(tmp_path_factory.mktemp("asm") / "ffn_bf16.s")
+    cmd = B.compile_command(os.path.join(B.CSRC, "ffn_bf16.hip"), out,
+                            ["--cuda-device-only", "-S"])
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    return open(out).read()
+
+
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+def test_int8_tiled_kernel_code(asm_bf16, proj):
+    """The weights-in-registers tiled kernel on int8 codes (csrc/ffn_bf16.hip,
+    template argument W8): accumulators stay in place, nothing spills, every
+    code is converted once (one v_cvt_f32_i32 per code, one v_perm_b32 per
+    pair: 16 operands of 8 codes per unrolled trip of 8 K steps, plus the
+    first step's 4 before the loop), and the weight loads are the 16-byte
+    non-temporal ones, one per 64-wide stage and row tile (4 stages ahead
+    before the loop, 4 per trip)."""
+    tag = "wtiled_kernelILb1ELb1ELb1E" if proj == "gate_up" else "wtiled_kernelILb0ELb1ELb1E"
+    code = [c for n, c in _kernels(asm_bf16).items() if tag in n]
+    assert len(code) == 1
+    lines = code[0].split("\n")
+    mfma = [l.split() for l in lines if "v_mfma" in l]
+    assert len(mfma) == 8 * 32
+    assert not [m for m in mfma if m[1].rstrip(",") != m[-1]]
+    assert not [l for l in lines if "scratch_" in l]
+    perm = sum("v_perm_b32" in l for l in lines)
+    cvt = sum("v_cvt_f32_i32" in l for l in lines)
+    assert perm == (8 + 1) * 4 * 4 and cvt == 2 * perm, (perm, cvt)
+    assert sum("global_load_dwordx4" in l and " nt" in l for l in lines) == 2 * 4 * 4

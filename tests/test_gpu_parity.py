@@ -275,22 +275,25 @@ def test_prefill_tiles_many_experts(m, E, k):
     assert rel_err(host(y_q), ref_q) <= OUT_TOL[gen.BF16]
 
 
-MANY = [784, 816, 848, 896, 898, 0, 1024, 1018]
-AT_THRESHOLD = [300, 120, 260, 400, 0, 256, 511, 201]   # A = 256 E exactly
+# last 256-row tiles of 16, 48, 80, 128, 130, 0 (an exact multiple) and 250
+# rows, A just above 1536 E
+MANY = [1552, 1584, 1616, 1664, 1666, 0, 2560, 1786]
+DOWN_ONLY = [1200, 480, 1040, 1600, 0, 1024, 2044, 804]  # A = 1024 E exactly
 
 
-@pytest.mark.parametrize("d,ffn,counts", [(256, 512, MANY), (384, 640, MANY),
-                                          (256, 512, AT_THRESHOLD)])
-def test_int8_prefill_matches_oracle(m, d, ffn, counts):
-    """int8 weights at prefill sizes (A >= 256 E): the codes are widened to
-    bf16 in fragment order in the workspace and the 256x256-tile kernels apply
-    the row scales to their sums. Hand-made routing with the tail-tile row
-    counts (expert step alone), then the fused layer on the same weights with
-    its own routing; both against the oracle on its dequantized weights. At
-    d = 384 the down projection stays on the streaming int8 kernel (the tile
-    kernel needs d % 256 == 0); at d = 256, ffn = 512 it splits K in two.
-    The last case sits exactly on the widening threshold, with experts on
-    both sides of one 256-row tile."""
+@pytest.mark.parametrize("d,ffn,counts,wide", [(256, 512, MANY, 2), (384, 640, MANY, 2),
+                                               (256, 512, DOWN_ONLY, 1)])
+def test_int8_prefill_matches_oracle(m, d, ffn, counts, wide):
+    """int8 weights at large prefill sizes: the codes are widened to bf16 in
+    fragment order in the workspace (w1 and w3 from A >= 1536 E, w2 from 1024
+    E) and the 256x256-tile kernels apply the row scales to their sums.
+    Hand-made routing with the tail-tile row counts (expert step alone), then
+    the fused layer on the same weights with its own routing; both against
+    the oracle on its dequantized weights. At d = 384 the down projection
+    stays on the streaming int8 kernel (the tile kernel needs d % 256 == 0);
+    at d = 256, ffn = 512 it splits K in two. The last case sits exactly on
+    the threshold of w2: gate/up keeps the tiled kernel that converts the
+    codes in registers, down runs on the widened w2."""
     E, k = len(counts), 2
     A = sum(counts)
     inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=60 + d)
@@ -298,7 +301,7 @@ def test_int8_prefill_matches_oracle(m, d, ffn, counts):
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     ws_i8 = m.moe_workspace_bytes(A // k, d, ffn, E, k, m.MOE_INT8_PACKED)
     ws_b = m.moe_workspace_bytes(A // k, d, ffn, E, k, torch.bfloat16)
-    assert ws_i8 - ws_b == 2 * E * ffn * d * 2  # widened w1 and w3 (w2 reuses them)
+    assert ws_i8 - ws_b == wide * E * ffn * d * 2  # widened w1 and w3, or w2 alone
     print(f"[parity] int8 prefill d={d} ffn={ffn} counts={counts}", flush=True)
     dev = to_device(inp)
     qw = m.QuantizedWeights(dev["w1"], dev["w3"], dev["w2"])
@@ -320,6 +323,39 @@ def test_int8_prefill_matches_oracle(m, d, ffn, counts):
     assert np.bincount(idx_g.ravel(), minlength=E).min() > 0
     ref = expected_output(ref_inp, idx_g, None, np.arange(T), logits64)
     assert rel_err(host(out), ref) <= OUT_TOL[gen.BF16]
+
+
+@pytest.mark.parametrize("d,ffn", [(256, 384), (320, 256), (512, 192)])
+def test_int8_tiled_matches_oracle(m, d, ffn):
+    """int8 weights between the streaming and the widening sizes (52 E < A <
+    1024 E): the tiled kernel converts the codes to bf16 operands in registers
+    and scales the finished sums. Expert row counts around the 128-row token
+    tile (1, 127, 128, 129, 257, an empty expert); gate/up takes the tiled
+    kernel when ffn % 128 == 0 and down when d % 256 == 0, so the three shapes
+    cover both, gate/up alone and down alone. Forced streaming kernels on the
+    same inputs must meet the same bound."""
+    counts = [1, 127, 128, 129, 0, 300, 64, 257]
+    E, k = len(counts), 2
+    A = sum(counts)
+    inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=70 + d + ffn)
+    sasg = np.random.default_rng(71).permutation(A).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    print(f"[parity] int8 tiled d={d} ffn={ffn} counts={counts}", flush=True)
+    dev = to_device(inp)
+    qw = m.QuantizedWeights(dev["w1"], dev["w3"], dev["w2"])
+    deq = _quantized(inp)
+    y_ref = oracle.expert_ffn(inp["x"], deq["w1"][2], deq["w3"][2], deq["w2"][2], offs, sasg, k)
+    offs_d, sasg_d = torch.from_numpy(offs).cuda(), torch.from_numpy(sasg).cuda()
+    try:
+        for variant in (0, 1):
+            m.moe_set_ffn_variant(variant)
+            y = m.moe_expert_ffn(dev["x"], qw.w1, qw.w3, qw.w2, offs_d, sasg_d, k)
+            torch.cuda.synchronize()
+            err = rel_err(host(y), y_ref)
+            print(f"[parity]   variant {variant}: max|err|/rms {err:.2e}", flush=True)
+            assert err <= OUT_TOL[gen.BF16]
+    finally:
+        m.moe_set_ffn_variant(0)
 
 
 def _pack_reference(w):
@@ -600,9 +636,10 @@ def test_full_size_decode_int8_and_block(m):
 @pytest.mark.slow
 def test_full_size_prefill_int8(m):
     """Prefill 8x7B shape on int8 weights (the configuration the benchmark
-    times with --weights int8): widened codes on the 256x256-tile kernels,
-    routing on every token, sampled outputs against the oracle's dequantized
-    weights."""
+    times with --weights int8; 1024 rows per expert): gate/up on the tiled
+    kernel converting the codes in registers, down on w2 widened in the
+    workspace and the 256x256-tile kernel; routing on every token, sampled
+    outputs against the oracle's dequantized weights."""
     print("[parity] full-size prefill_8x7b int8", flush=True)
     m.moe_set_ffn_variant(0)
     inp = gen.make_config("prefill_8x7b")

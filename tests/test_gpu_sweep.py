@@ -27,7 +27,7 @@ def _case(i):
     k = int(rng.choice([1, 2, 2, min(4, E)]))
     d = 64 * int(rng.integers(1, 25))
     ffn = 64 * int(rng.integers(1, 21))
-    regime = i % 3      # 0: few rows per expert, 1: middle (int8 widened from 256), 2: many
+    regime = i % 3      # 0: few rows per expert, 1: middle, 2: many
     if regime == 2 and i % 6 != 5:  # widths the 256x256-tile kernels take (down: d % 256)
         d = 256 * int(rng.integers(1, 9))
         ffn = 128 * int(rng.integers(1, 17))
