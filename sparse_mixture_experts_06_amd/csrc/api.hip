@@ -31,7 +31,10 @@ inline bool is_bf16(int dtype) {
 int ws_splits(int64_t A, int d, int ffn, int E, int dtype) {
   if (!is_bf16(dtype)) return 1;
   const int a = moe::down_splits(1, A, d, ffn, E), b = moe::down_splits(2, A, d, ffn, E);
-  return a > b ? a : b;
+  // int8: its tiled kernel also runs where bf16 would take the direct-to-LDS one
+  const int c = dtype == MOE_INT8_PACKED ? moe::int8_down_splits(2, A, d, ffn, E) : 1;
+  const int ab = a > b ? a : b;
+  return ab > c ? ab : c;
 }
 
 Layout layout(int64_t T, int d, int ffn, int E, int k, int dtype) {

@@ -133,16 +133,19 @@ hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const u
                             const int32_t* offsets, int64_t A, int d, int ffn, int E, float* part,
                             hipStream_t s);
 int down_splits(int variant, int64_t A, int d, int ffn, int E);
+// K split of the tiled down kernels below the direct-to-LDS sizes: 2 while
+// the 256-row tiles would leave CUs idle (d % 256 == 0, ffn % 128 == 0), else 1
+int tiled_down_splits(int64_t A, int d, int ffn, int E);
 // int8 codes (16-row x 64-k blocks) with float32 row scales on the tiled
 // weights-in-registers kernel, operands widened in registers: gate/up needs
-// ffn % 128 == 0, down d % 256 == 0 (one partial, no K split)
+// ffn % 128 == 0, down d % 256 == 0 and nsplit partials as tiled_down_splits
 hipError_t launch_gate_up_w8_tiled(const uint16_t* x, const void* q1, const void* q3,
                                   const float* s1, const float* s3, const int32_t* offsets,
                                   const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
                                   int k, uint16_t* h, hipStream_t s);
 hipError_t launch_down_w8_tiled(const uint16_t* h, const void* q2, const float* s2,
                                const int32_t* offsets, int64_t A, int d, int ffn, int E,
-                               float* part, hipStream_t s);
+                               int nsplit, float* part, hipStream_t s);
 
 // gate/up and down for many rows per expert with direct-to-LDS loads
 // (ffn_dma.hip), for fragment-order (packed) or row-major weights: the sizes

@@ -576,9 +576,12 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
     const uint16_t* __restrict__ act, const void* __restrict__ wa, const void* __restrict__ wb,
     const float* __restrict__ sa, const float* __restrict__ sb,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_asg, int K, int N,
-    int E, int ktop, void* __restrict__ out, int ntn) {
+    int E, int ktop, void* __restrict__ out, int ntn, int nsplit, int64_t pstride) {
   int e, beg, M, m0, nt, sp;
-  if (!decode_tile(offsets, E, ntn, 1, e, beg, M, m0, nt, sp)) return;
+  if (!decode_tile(offsets, E, ntn, nsplit, e, beg, M, m0, nt, sp)) return;
+  // this tile's K range [k0, k0 + Kc) (split only for down; Kc % 64 == 0)
+  const int Kc = K / nsplit;
+  const int k0 = sp * Kc;
 
   __shared__ __attribute__((aligned(16))) uint16_t sX[2][BM * BK];
 
@@ -607,10 +610,10 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
     }
     if constexpr (W8)
       qbase[i] = static_cast<const int8_t*>(base) +
-                 (static_cast<size_t>(e) * (N >> 4) + (row >> 4)) * static_cast<size_t>(K >> 6) *
-                     1024 + lane * 16;
+                 ((static_cast<size_t>(e) * (N >> 4) + (row >> 4)) * static_cast<size_t>(K >> 6) +
+                  (k0 >> 6)) * 1024 + lane * 16;
     else
-      wbase[i] = static_cast<const uint16_t*>(base) + wofs<PACKED>(e, row, 0, N, K);
+      wbase[i] = static_cast<const uint16_t*>(base) + wofs<PACKED>(e, row, k0, N, K);
   }
   const int wlane = static_cast<int>(wofs<PACKED>(0, fr, fg * 8, N, K));
 
@@ -635,7 +638,7 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
+  const int nk = Kc / BK;
   const int last = nk - 1;
   const int nsteps = 2 * nk;  // 32-wide K steps
   // weights: a ring of RING K32 slots; the loads of step t+RING are issued
@@ -657,7 +660,7 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
   auto issue_x = [&](int set, int kb) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      rx[set][j] = ldg16(act + static_cast<int64_t>(xrow[j]) * K + kb * BK + xcol);
+      rx[set][j] = ldg16(act + static_cast<int64_t>(xrow[j]) * K + k0 + kb * BK + xcol);
   };
   auto stash = [&](int set, int buf) {
 #pragma unroll
@@ -774,8 +777,8 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
         const int n = nt * 256 + wave * 64 + i * 16 + 4 * fg;
         f32x4 v = acc[i][j];
         if constexpr (W8) v *= sc[i];
-        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + static_cast<size_t>(beg + m) * N + n) =
-            v;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + sp * pstride +
+                                  static_cast<size_t>(beg + m) * N + n) = v;
       }
     }
   }
@@ -813,7 +816,8 @@ hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, cons
     hipLaunchKernelGGL((wtiled_kernel<true, PACKED, false, kWRing, kWOcc, kWXSets>),
                        dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0, s, x, w1, w3,
                        static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
-                       offsets, sorted_asg, d, ffn, E, k, static_cast<void*>(h), ntn);
+                       offsets, sorted_asg, d, ffn, E, k, static_cast<void*>(h), ntn, 1,
+                       int64_t(0));
   } else {
     const int ntn = ffn / 64;
     hipLaunchKernelGGL((tiled_kernel<true, PACKED>), dim3(tiled_grid(A, E, ntn)),
@@ -844,13 +848,13 @@ hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const i
     }
   } else if (dma_down_ok(A, d, ffn, E)) {
     return launch_down_dma(PACKED, h, w2, offsets, A, d, ffn, E, nsplit, part, s);
-  } else if (PACKED && d % 256 == 0 && nsplit == 1) {
+  } else if (PACKED && d % 256 == 0) {
     const int ntn = d / 256;
     hipLaunchKernelGGL((wtiled_kernel<false, PACKED, false, kWRing, kWOcc, kWXSets>),
-                       dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0, s, h, w2, w2,
+                       dim3(tiled_grid(A, E, ntn, nsplit)), dim3(kTiledThreads), 0, s, h, w2, w2,
                        static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
                        offsets, static_cast<const int32_t*>(nullptr), ffn, d, E, 1,
-                       static_cast<void*>(part), ntn);
+                       static_cast<void*>(part), ntn, nsplit, A * d);
   } else {
     const int ntn = (d + BN - 1) / BN;
     hipLaunchKernelGGL((tiled_kernel<false, PACKED>), dim3(tiled_grid(A, E, ntn, nsplit)),
@@ -878,14 +882,22 @@ int choose_down_variant(int requested, int64_t A, int E) {
   return (A <= static_cast<int64_t>(27) * E) ? 1 : 2;
 }
 
+int tiled_down_splits(int64_t A, int d, int ffn, int E) {
+  if (d % 256 != 0 || ffn % 128 != 0) return 1;
+  const int64_t tiles = (A / BM + E) * (d / 256);  // at most this many 256-row tiles
+  return tiles < 256 ? 2 : 1;
+}
+
 int down_splits(int variant, int64_t A, int d, int ffn, int E) {
   // the streaming down kernel splits K two ways while its float32 partials
   // stay small; the tiled kernels split K where the 256-row tiles of the
-  // direct-to-LDS kernels would leave the last round over the CUs part-empty
-  // (all tiled kernels follow the same split, so y does not depend on the
-  // weight layout)
+  // direct-to-LDS kernels would leave the last round over the CUs part-empty,
+  // and below their sizes while the 256-row weights-in-registers tiles would
+  // not give every CU one (all tiled kernels follow the same split, so y does
+  // not depend on the weight layout)
   if (variant == 1) return A <= 4096 ? 2 : 1;
-  return dma_down_splits(A, d, ffn, E);
+  if (dma_down_ok(A, d, ffn, E)) return dma_down_splits(A, d, ffn, E);
+  return tiled_down_splits(A, d, ffn, E);
 }
 
 hipError_t launch_gate_up_w8_tiled(const uint16_t* x, const void* q1, const void* q3,
@@ -895,19 +907,19 @@ hipError_t launch_gate_up_w8_tiled(const uint16_t* x, const void* q1, const void
   const int ntn = ffn / 128;
   hipLaunchKernelGGL((wtiled_kernel<true, true, true, kW8Ring, kWOcc, kWXSets>),
                      dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0, s, x, q1, q3, s1, s3,
-                     offsets, sorted_asg, d, ffn, E, k, static_cast<void*>(h), ntn);
+                     offsets, sorted_asg, d, ffn, E, k, static_cast<void*>(h), ntn, 1, int64_t(0));
   return hipGetLastError();
 }
 
 hipError_t launch_down_w8_tiled(const uint16_t* h, const void* q2, const float* s2,
                                const int32_t* offsets, int64_t A, int d, int ffn, int E,
-                               float* part, hipStream_t s) {
+                               int nsplit, float* part, hipStream_t s) {
   const int ntn = d / 256;
   hipLaunchKernelGGL((wtiled_kernel<false, true, true, kW8Ring, kWOcc, kWXSets>),
-                     dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0, s, h, q2, q2, s2,
+                     dim3(tiled_grid(A, E, ntn, nsplit)), dim3(kTiledThreads), 0, s, h, q2, q2, s2,
                      static_cast<const float*>(nullptr), offsets,
                      static_cast<const int32_t*>(nullptr), ffn, d, E, 1, static_cast<void*>(part),
-                     ntn);
+                     ntn, nsplit, A * d);
   return hipGetLastError();
 }
 

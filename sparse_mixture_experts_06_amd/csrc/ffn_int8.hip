@@ -398,7 +398,7 @@ bool int8_down_dma(int64_t A, int d, int ffn, int E) {
 
 int int8_down_splits(int variant, int64_t A, int d, int ffn, int E) {
   if (variant != 1 && int8_down_dma(A, d, ffn, E)) return dma_down_splits(A, d, ffn, E);
-  if (variant != 1 && d % 256 == 0) return 1;  // tiled kernel
+  if (variant != 1 && d % 256 == 0) return tiled_down_splits(A, d, ffn, E);
   return down_splits(1, A, d, ffn, E);
 }
 
@@ -447,10 +447,8 @@ hipError_t launch_down_int8(int variant, const uint16_t* h, const void* w2,
   const size_t cb = align256(static_cast<size_t>(E) * d * ffn);
   const int8_t* q2 = static_cast<const int8_t*>(w2);
   const float* s2 = reinterpret_cast<const float*>(static_cast<const char*>(w2) + cb);
-  if (variant != 1 && d % 256 == 0) {
-    if (nsplit != 1) return hipErrorInvalidValue;
-    return launch_down_w8_tiled(h, q2, s2, offsets, A, d, ffn, E, part, s);
-  }
+  if (variant != 1 && d % 256 == 0)
+    return launch_down_w8_tiled(h, q2, s2, offsets, A, d, ffn, E, nsplit, part, s);
   const int rt = (d % (16 * kW8DownRT) == 0) ? kW8DownRT : 1;
   const unsigned blocks = static_cast<unsigned>((d / (16 * rt) * nsplit + kW8Waves - 1) / kW8Waves);
   if (rt != kW8DownRT) {
