@@ -83,7 +83,7 @@ const char* moe_strerror(int status);
  * function. Returns 0 for invalid arguments. With MOE_INT8_PACKED at large
  * prefill sizes (d and ffn multiples of 128) it includes room for weights
  * widened to bfloat16 (see moe_quantize_weight): E*ffn*d*2 bytes for w2 from
- * T*k >= 1024*E (d % 256 == 0), 2*E*ffn*d*2 for w1 and w3 from T*k >= 1536*E. */
+ * T*k >= 1024*E (d % 256 == 0), 2*E*ffn*d*2 for w1 and w3 from T*k >= 8192*E. */
 size_t moe_workspace_bytes(int64_t T, int d, int ffn, int E, int k, int dtype);
 
 /* Router + scoring (nnterp page, Notes: softmax over the experts in float32,
@@ -207,7 +207,7 @@ int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* o
  * get few rows (decode, where the weight bytes set the time); beyond that a
  * tiled MFMA kernel converts them to bfloat16 operands in registers (gate/up
  * when ffn % 128 == 0, down when d % 256 == 0); for large prefill batches
- * (T*k >= 1536*E for w1 and w3, >= 1024*E for w2) the codes are first widened
+ * (T*k >= 8192*E for w1 and w3, >= 1024*E for w2) the codes are first widened
  * to bfloat16 (exact) in the workspace and the direct-to-LDS tile kernels of
  * the bf16 path run on them. Every kernel applies the row scales to its
  * finished sums. */

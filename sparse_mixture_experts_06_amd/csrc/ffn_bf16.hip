@@ -556,8 +556,8 @@ __global__ __launch_bounds__(kTiledThreads, 2) void tiled_kernel(
 // only the token rows, shared by the four waves, are staged through LDS. Per
 // 64-wide K stage that is 16 KiB of LDS writes and 64 KiB of reads for
 // 4.2 MFLOP, against 32 + 64 KiB for 2.1 MFLOP when both operands go
-// through LDS. Weights are fetched 3.5 stages ahead (a ring of eight 32-wide
-// K steps), tokens two stages ahead (two register sets).
+// through LDS. Weights are fetched RING 32-wide K steps ahead, tokens XSETS
+// stages ahead (register sets).
 // GATE_UP: wave w's rows are w1 rows n+32w .. n+32w+31 then the same rows of
 // w3 (n = nt*128), so gate and up of one h column sit in the same lane.
 // Needs N % 256 == 0 (down) or ffn % 128 == 0 (gate/up). Used with
@@ -784,10 +784,17 @@ __global__ __launch_bounds__(kTiledThreads, OCC) void wtiled_kernel(
   }
 }
 
-// weight ring depth and workgroups per CU of wtiled_kernel
+// weight ring depth (32-wide K steps; int8 codes: RING/2 slots of 64),
+// workgroups per CU and token stages in registers of wtiled_kernel. Down:
+// one workgroup per CU with deep rings. Gate/up: two per CU with shallow ones
+// (at most 256 registers, no spills), since a second workgroup's MFMAs cover
+// this one's waits better than a deeper ring. Measured at 8x7B (gate/up us,
+// one per CU -> two): bf16 T = 128 365 -> 325, 384 375 -> 353; int8 codes
+// T = 512 443 -> 381, 1024 648 -> 539, 4096 2108 -> 1715; down kept one per CU
+// (two: bf16 about the same, int8 T = 512 238 -> 295).
 constexpr int kWRing = 8, kWOcc = 1, kWXSets = 2;
-// int8 codes: ring depth in 32-wide K steps (RING/2 slots of 64)
 constexpr int kW8Ring = 8;
+constexpr int kWGuRing = 4, kWGuOcc = 2, kWGuXSets = 1;
 
 inline unsigned tiled_grid(int64_t A, int E, int ntn, int nsplit = 1) {
   const int64_t mt = (A + BM - 1) / BM + E;
@@ -813,7 +820,7 @@ hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, cons
     return launch_gate_up_dma(PACKED, x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s);
   } else if (PACKED && ffn % 128 == 0) {
     const int ntn = ffn / 128;
-    hipLaunchKernelGGL((wtiled_kernel<true, PACKED, false, kWRing, kWOcc, kWXSets>),
+    hipLaunchKernelGGL((wtiled_kernel<true, PACKED, false, kWGuRing, kWGuOcc, kWGuXSets>),
                        dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0, s, x, w1, w3,
                        static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
                        offsets, sorted_asg, d, ffn, E, k, static_cast<void*>(h), ntn, 1,
@@ -905,7 +912,7 @@ hipError_t launch_gate_up_w8_tiled(const uint16_t* x, const void* q1, const void
                                   const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
                                   int k, uint16_t* h, hipStream_t s) {
   const int ntn = ffn / 128;
-  hipLaunchKernelGGL((wtiled_kernel<true, true, true, kW8Ring, kWOcc, kWXSets>),
+  hipLaunchKernelGGL((wtiled_kernel<true, true, true, kWGuRing, kWGuOcc, kWGuXSets>),
                      dim3(tiled_grid(A, E, ntn)), dim3(kTiledThreads), 0, s, x, q1, q3, s1, s3,
                      offsets, sorted_asg, d, ffn, E, k, static_cast<void*>(h), ntn, 1, int64_t(0));
   return hipGetLastError();

@@ -385,12 +385,15 @@ int choose_int8_down_variant(int requested, int64_t A, int E) {
 
 // Widening the codes into the workspace and running the direct-to-LDS tiles
 // overtakes the tiled kernel's in-register widening only for large batches,
-// since the widening itself streams the codes and writes twice their bytes
-// (8x7B shape, us, tiled vs widened): gate/up 1930 vs 2082 at 1024 rows per
-// expert, 2797 vs 2775 at 1536; down 861 vs 869 at 768, 1053 vs 1042 at 1024,
-// 1478 vs 1398 at 1536.
+// since the widening itself streams the codes and writes twice their bytes.
+// Down (8x7B shape, us, tiled vs widened): 861 vs 869 at 768 rows per expert,
+// 1053 vs 1042 at 1024, 1478 vs 1398 at 1536. Gate/up: the tiled kernel wins
+// at every size measured (1536 rows per expert: 2463 vs 2782; 2048: 3271 vs
+// 3495), being about 3% slower per row than the direct-to-LDS kernel while
+// widening w1 and w3 costs about 0.47 ms per call; the two meet near 8192 rows
+// per expert (extrapolated), where widening starts.
 bool int8_gate_up_dma(int64_t A, int k, int d, int ffn, int E) {
-  return A >= static_cast<int64_t>(1536) * E && dma_gate_up_ok(A, k, d, ffn, E);
+  return A >= static_cast<int64_t>(8192) * E && dma_gate_up_ok(A, k, d, ffn, E);
 }
 bool int8_down_dma(int64_t A, int d, int ffn, int E) {
   return A >= static_cast<int64_t>(1024) * E && dma_down_ok(A, d, ffn, E);

@@ -55,10 +55,10 @@ def test_workspace_bytes():
     assert f(4096, 4224, 14336, 8, 2, moe.MOE_BF16) < 8192 * 14336 * 2 + 2 * 8192 * 4224 * 4
     # int8 weights: as bf16, except for large prefill batches, where the
     # workspace also holds w2 widened to bf16 (A >= 1024 E), then w1 and w3
-    # (A >= 1536 E; w2 reuses their room)
+    # (A >= 8192 E; w2 reuses their room)
     m = 8 * 14336 * 4096 * 2
     assert f(32, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) == n
-    for T, wide in ((4095, 0), (4096, m), (6143, m), (6144, 2 * m), (8192, 2 * m)):
+    for T, wide in ((4095, 0), (4096, m), (32767, m), (32768, 2 * m)):
         assert (f(T, 4096, 14336, 8, 2, moe.MOE_INT8_PACKED) -
                 f(T, 4096, 14336, 8, 2, moe.MOE_BF16)) == wide, T
     assert f(0, 128, 256, 8, 2, moe.MOE_F32) > 0                # counts/offsets still live

@@ -129,24 +129,33 @@ def asm_bf16(tmp_path_factory):
     return open(out).read()
 
 
-@pytest.mark.parametrize("proj", ["gate_up", "down"])
+# ring depth in 32-wide K steps, workgroups per CU, token stages (the
+# template arguments after W8) and K steps per unrolled loop trip
+W8_TILED = {"gate_up": ("wtiled_kernelILb1ELb1ELb1ELi4ELi2ELi1E", 4, 2, 4),
+            "down": ("wtiled_kernelILb0ELb1ELb1ELi8ELi1ELi2E", 8, 1, 8)}
+
+
+@pytest.mark.parametrize("proj", list(W8_TILED))
 def test_int8_tiled_kernel_code(asm_bf16, proj):
     """The weights-in-registers tiled kernel on int8 codes (csrc/ffn_bf16.hip,
-    template argument W8): accumulators stay in place, nothing spills, every
-    code is converted once (one v_cvt_f32_i32 per code, one v_perm_b32 per
-    pair: 16 operands of 8 codes per unrolled trip of 8 K steps, plus the
-    first step's 4 before the loop), and the weight loads are the 16-byte
-    non-temporal ones, one per 64-wide stage and row tile (4 stages ahead
-    before the loop, 4 per trip)."""
-    tag = "wtiled_kernelILb1ELb1ELb1E" if proj == "gate_up" else "wtiled_kernelILb0ELb1ELb1E"
+    template argument W8): accumulators stay in place, nothing spills (gate/up
+    fits the 256 registers of two workgroups per CU), every code is converted
+    once (one v_cvt_f32_i32 per code, one v_perm_b32 per pair: 4 operands of
+    8 codes per K step of the unrolled trip, plus the first step's 4 before
+    the loop), and the weight loads are the 16-byte non-temporal ones, one
+    per 64-wide stage and row tile (RING/2 stages ahead before the loop, one
+    per two K steps in it)."""
+    tag, ring, occ, steps = W8_TILED[proj]
     code = [c for n, c in _kernels(asm_bf16).items() if tag in n]
     assert len(code) == 1
     lines = code[0].split("\n")
     mfma = [l.split() for l in lines if "v_mfma" in l]
-    assert len(mfma) == 8 * 32
+    assert len(mfma) == steps * 32
     assert not [m for m in mfma if m[1].rstrip(",") != m[-1]]
     assert not [l for l in lines if "scratch_" in l]
     perm = sum("v_perm_b32" in l for l in lines)
     cvt = sum("v_cvt_f32_i32" in l for l in lines)
-    assert perm == (8 + 1) * 4 * 4 and cvt == 2 * perm, (perm, cvt)
-    assert sum("global_load_dwordx4" in l and " nt" in l for l in lines) == 2 * 4 * 4
+    assert perm == (steps + 1) * 4 * 4 and cvt == 2 * perm, (perm, cvt)
+    assert sum("global_load_dwordx4" in l and " nt" in l for l in lines) == (ring // 2 + steps // 2) * 4
+    occupancy = re.search(r"; Occupancy: (\d+)", code[0])
+    assert occupancy and int(occupancy.group(1)) >= occ

@@ -276,24 +276,26 @@ def test_prefill_tiles_many_experts(m, E, k):
 
 
 # last 256-row tiles of 16, 48, 80, 128, 130, 0 (an exact multiple) and 250
-# rows, A just above 1536 E
+# rows, A above 1024 E
 MANY = [1552, 1584, 1616, 1664, 1666, 0, 2560, 1786]
 DOWN_ONLY = [1200, 480, 1040, 1600, 0, 1024, 2044, 804]  # A = 1024 E exactly
+BOTH = [8208, 8442]  # two experts, A just above 8192 E: w1 and w3 widened too
 
 
-@pytest.mark.parametrize("d,ffn,counts,wide", [(256, 512, MANY, 2), (384, 640, MANY, 2),
-                                               (256, 512, DOWN_ONLY, 1)])
+@pytest.mark.parametrize("d,ffn,counts,wide", [(256, 512, MANY, 1), (384, 640, MANY, 0),
+                                               (256, 512, DOWN_ONLY, 1), (256, 512, BOTH, 2)])
 def test_int8_prefill_matches_oracle(m, d, ffn, counts, wide):
-    """int8 weights at large prefill sizes: the codes are widened to bf16 in
-    fragment order in the workspace (w1 and w3 from A >= 1536 E, w2 from 1024
-    E) and the 256x256-tile kernels apply the row scales to their sums.
-    Hand-made routing with the tail-tile row counts (expert step alone), then
-    the fused layer on the same weights with its own routing; both against
-    the oracle on its dequantized weights. At d = 384 the down projection
-    stays on the streaming int8 kernel (the tile kernel needs d % 256 == 0);
-    at d = 256, ffn = 512 it splits K in two. The last case sits exactly on
-    the threshold of w2: gate/up keeps the tiled kernel that converts the
-    codes in registers, down runs on the widened w2."""
+    """int8 weights at large prefill sizes: the codes of w2 are widened to bf16
+    in fragment order in the workspace from A >= 1024 E, those of w1 and w3
+    from A >= 8192 E, and the 256x256-tile kernels apply the row scales to
+    their sums; below that, gate/up runs the tiled kernel that converts the
+    codes in registers. Hand-made routing with the tail-tile row counts
+    (expert step alone), then the fused layer on the same weights with its
+    own routing; both against the oracle on its dequantized weights. At d =
+    384 nothing is widened: down stays on the streaming int8 kernel (the tile
+    kernels need d % 256 == 0); at d = 256, ffn = 512 down splits K in two.
+    DOWN_ONLY sits exactly on the threshold of w2, BOTH (two experts) just
+    above that of w1 and w3."""
     E, k = len(counts), 2
     A = sum(counts)
     inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=60 + d)
