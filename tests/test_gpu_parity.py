@@ -334,8 +334,11 @@ def test_int8_tiled_matches_oracle(m, d, ffn):
     and scales the finished sums. Expert row counts around the 128-row token
     tile (1, 127, 128, 129, 257, an empty expert); gate/up takes the tiled
     kernel when ffn % 128 == 0 and down when d % 256 == 0, so the three shapes
-    cover both, gate/up alone and down alone. Forced streaming kernels on the
-    same inputs must meet the same bound."""
+    cover both, gate/up alone and down alone; at d = 256, ffn = 384 the few
+    256-row down tiles split K in two. Forced streaming kernels on the same
+    inputs must meet the same bound. The same routing on the bf16 weights
+    (tiled kernels, the same K split) in both layouts: bit-identical, and
+    within the bf16 bound of the oracle."""
     counts = [1, 127, 128, 129, 0, 300, 64, 257]
     E, k = len(counts), 2
     A = sum(counts)
@@ -358,6 +361,13 @@ def test_int8_tiled_matches_oracle(m, d, ffn):
             assert err <= OUT_TOL[gen.BF16]
     finally:
         m.moe_set_ffn_variant(0)
+    pw = m.PackedWeights(dev["w1"], dev["w3"], dev["w2"])
+    y_s = m.moe_expert_ffn(dev["x"], dev["w1"], dev["w3"], dev["w2"], offs_d, sasg_d, k)
+    y_p = m.moe_expert_ffn(dev["x"], pw.w1, pw.w3, pw.w2, offs_d, sasg_d, k, packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y_p, y_s)
+    yb_ref = oracle.expert_ffn(inp["x"], inp["w1"], inp["w3"], inp["w2"], offs, sasg, k)
+    assert rel_err(host(y_p), yb_ref) <= OUT_TOL[gen.BF16]
 
 
 def _pack_reference(w):
