@@ -31,11 +31,12 @@
 //    K, written as a float32 partial; the partials are summed later in a
 //    fixed order (by the combine, or by moe_expert_ffn before it returns).
 //    With fragment-order weights the weight loads are non-temporal.
-//  * tiled (many rows per expert, prefill). When experts average two or more
-//    full 256-row tiles (A >= 512 E; d and ffn multiples of 128, and for down
-//    d % 256 == 0) the 256x256-tile direct-to-LDS kernels of ffn_dma.hip run,
-//    for either layout. Below that: with fragment-order weights wtiled_kernel
-//    (256 weight rows x 128 tokens, weights straight into registers), with
+//  * tiled (many rows per expert, prefill). When experts average half a
+//    256-row tile or more for gate/up (A >= 128 E) and a full one for down
+//    (A >= 256 E; d and ffn multiples of 128, and for down d % 256 == 0) the
+//    256x256-tile direct-to-LDS kernels of ffn_dma.hip run, for either
+//    layout. Below that: with fragment-order weights wtiled_kernel (256
+//    weight rows x 128 tokens, weights straight into registers), with
 //    the standard layout tiled_kernel: 128 weight rows x 128 token rows x 64
 //    K per step, double-buffered in LDS with an XOR swizzle of the 16-byte
 //    chunks (conflict-free ds_read_b128 for the MFMA fragments); 4 waves each
