@@ -217,10 +217,12 @@ int moe_quantize_weight(const void* w, int dtype, int E, int rows, int cols, voi
 
 /* ---- tuning and profiling hooks (process-wide, not thread-safe) ---------- */
 
-/* Expert-FFN kernel family for MOE_BF16: 0 = choose by size, per projection
- * (default), 1 = weight-streaming kernels (few rows per expert), 2 = LDS-tiled
- * MFMA kernels (many rows per expert), for both projections. Returns
- * MOE_EINVAL for other values. */
+/* Expert-FFN kernel family for bf16 and int8 weights: 0 = choose by size,
+ * per projection and weight format (default), 1 = weight-streaming kernels
+ * (few rows per expert), 2 = tiled MFMA kernels (many rows per expert; which
+ * tile kernel, and for int8 whether the codes are widened in the workspace,
+ * still follows the size), for both projections. Returns MOE_EINVAL for
+ * other values. */
 int moe_set_ffn_variant(int variant);
 
 /* Profiling: when n == 6, moe_forward (and moe_block_forward) records events[0] before the router,
