@@ -21,14 +21,18 @@
 // 256-byte boundary, the float32 scales [E, rows]. A wave's 16-byte load of one
 // block is one contiguous KiB and feeds two 32-deep MFMA steps.
 //
-// Many rows per expert (prefill): the codes are widened to bfloat16 (exact)
-// in the fragment order of the bf16 path, into the caller's workspace, and
-// the direct-to-LDS tile kernels run on them with the row scales applied to
-// their finished sums. Block b of the codes holds exactly the bf16 fragments
-// 2b (its bytes 0-7 in each lane) and 2b+1 (bytes 8-15), since both layouts
-// order (expert, 16-row tile, K step) and put lane l's values in lane order.
+// More rows per expert: the weights-in-registers tile kernel of ffn_bf16.hip
+// (template argument W8) reads the code blocks and converts them to bf16
+// operands in registers. Large prefill batches: the codes are widened to
+// bfloat16 (exact) in the fragment order of the bf16 path, into the caller's
+// workspace, and the direct-to-LDS tile kernels run on them with the row
+// scales applied to their finished sums. Block b of the codes holds exactly
+// the bf16 fragments 2b (its bytes 0-7 in each lane) and 2b+1 (bytes 8-15),
+// since both layouts order (expert, 16-row tile, K step) and put lane l's
+// values in lane order.
 //
-// Kernels: the streaming decode kernels of ffn_bf16.hip with int8 weights.
+// Kernels here: the streaming decode kernels of ffn_bf16.hip with int8
+// weights.
 // gate/up: a workgroup owns two 16-row tiles of w1 and w3, its 4 waves split
 // K, partial sums meet in LDS, wave 0 scales, applies SiLU*mul and stores bf16
 // h. down: each wave streams four 16-row tiles of w2 over 1/nsplit of K and
