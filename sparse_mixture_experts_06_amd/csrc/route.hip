@@ -13,13 +13,15 @@
 // type, stores it to norm_out and feeds that stored value to the logits.
 //
 // Work split (latency first: a decode batch has only a few dozen tokens): a
-// workgroup of 256 threads takes kVals / EM tokens and splits the hidden
-// dimension across all its threads in 8-element chunks (16-byte loads), so
-// every load of a token row and of the router is in flight at once. Each
-// thread then holds kVals = 64 float32 partial sums (token x expert); a
-// reduce-scatter across the wave (63 shuffles) leaves lane l with the wave's
-// sum for value l, the four waves meet in LDS in a fixed order, and one
-// thread per token finishes the scoring.
+// workgroup of 256 threads takes TB tokens and splits the hidden dimension
+// across all its threads in 8-element chunks (16-byte loads), so every load
+// of a token row and of the router is in flight at once. Each thread then
+// holds TB x EM float32 partial sums (token x expert); a reduce-scatter
+// across the wave (halving steps, then butterflies) leaves lane l with the
+// wave's sum for value l, the four waves meet in LDS in a fixed order, and
+// one thread per token finishes the scoring. TB = 1 for batches of up to 256
+// tokens (one workgroup per token, the most CUs and the least arithmetic per
+// workgroup), else 64 / EM (fewer re-reads of the router rows).
 #include "common.h"
 
 namespace moe {
@@ -27,7 +29,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kVals = 64;  // partial sums per thread: tokens per block x EM
+constexpr int kVals = 64;  // partial sums per thread at most: tokens per block x EM
 
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* x, int64_t row, int d, int i, float* v) {
@@ -60,8 +62,8 @@ __device__ __forceinline__ float load1(const void* x, int64_t row, int d, int i)
 // One halving step of the reduce-scatter: lanes with bit O set keep the
 // upper half of the O*2 live values, the others the lower half, and each adds
 // the half its partner (lane ^ O) gives away.
-template <int O>
-__device__ __forceinline__ void reduce_scatter_step(float (&v)[kVals], bool upper) {
+template <int O, int NV>
+__device__ __forceinline__ void reduce_scatter_step(float (&v)[NV], bool upper) {
 #pragma unroll
   for (int i = 0; i < O; ++i) {
     const float keep = upper ? v[i + O] : v[i];
@@ -70,15 +72,21 @@ __device__ __forceinline__ void reduce_scatter_step(float (&v)[kVals], bool uppe
   }
 }
 
-// v[0..63] in every lane -> lane l returns the sum over the wave of v[l].
-__device__ __forceinline__ float wave_reduce_scatter64(float (&v)[kVals], int lane) {
-  reduce_scatter_step<32>(v, (lane & 32) != 0);
-  reduce_scatter_step<16>(v, (lane & 16) != 0);
-  reduce_scatter_step<8>(v, (lane & 8) != 0);
-  reduce_scatter_step<4>(v, (lane & 4) != 0);
-  reduce_scatter_step<2>(v, (lane & 2) != 0);
-  reduce_scatter_step<1>(v, (lane & 1) != 0);
-  return v[0];
+// v[0..NV-1] in every lane (NV a power of two <= 64) -> lane l returns the
+// sum over the wave of v[l % NV]: halving steps while values remain, then
+// butterflies between the lane groups that hold partial sums of one value.
+template <int NV>
+__device__ __forceinline__ float wave_reduce_scatter(float (&v)[NV], int lane) {
+  if constexpr (NV > 32) reduce_scatter_step<32>(v, (lane & 32) != 0);
+  if constexpr (NV > 16) reduce_scatter_step<16>(v, (lane & 16) != 0);
+  if constexpr (NV > 8) reduce_scatter_step<8>(v, (lane & 8) != 0);
+  if constexpr (NV > 4) reduce_scatter_step<4>(v, (lane & 4) != 0);
+  if constexpr (NV > 2) reduce_scatter_step<2>(v, (lane & 2) != 0);
+  if constexpr (NV > 1) reduce_scatter_step<1>(v, (lane & 1) != 0);
+  float r = v[0];
+#pragma unroll
+  for (int o = NV; o < kWave; o <<= 1) r += __shfl_xor(r, o, kWave);
+  return r;
 }
 
 // normed value of x (float32) at hidden index i, rounded to the stored type
@@ -103,27 +111,28 @@ __device__ __forceinline__ void store8(void* out, int64_t row, int d, int i, con
   }
 }
 
-// EM: compile-time bound on E (8 or 32); TB = kVals / EM tokens per block.
+// EM: compile-time bound on E (8 or 32); TB tokens per block (TB * EM <= 64).
 // VEC: x, router, gamma and norm_out rows are 16-byte aligned and d % 8 == 0.
 // NORM: route the RMS-normed rows (gamma [d] float32, eps) and store them.
-template <bool BF16, int EM, bool VEC, bool NORM>
+template <bool BF16, int EM, int TB, bool VEC, bool NORM>
 __global__ __launch_bounds__(kThreads, 1) void route_kernel(
     const void* __restrict__ x, const float* __restrict__ router, const float* __restrict__ bias,
     int64_t T, int d, int E, int k, float* __restrict__ logits_out, int32_t* __restrict__ idx,
     float* __restrict__ wout, const float* __restrict__ gamma, float eps,
     void* __restrict__ norm_out) {
-  constexpr int TB = kVals / EM;
-  __shared__ float s_part[kWavesPerBlock][kVals];
-  __shared__ float s_logit[kVals];
+  constexpr int NV = TB * EM;
+  static_assert(NV <= kVals && (NV & (NV - 1)) == 0, "TB * EM: a power of two up to 64");
+  __shared__ float s_part[kWavesPerBlock][NV];
+  __shared__ float s_logit[NV];
   __shared__ float s_ss[kWavesPerBlock][TB];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
 
-  float acc[kVals];
+  float acc[NV];
 #pragma unroll
-  for (int i = 0; i < kVals; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
 
   int64_t rows[TB];
   bool live[TB];
@@ -254,9 +263,10 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(
     }
   }
 
-  s_part[wave][lane] = wave_reduce_scatter64(acc, lane);
+  const float part = wave_reduce_scatter<NV>(acc, lane);
+  if (lane < NV) s_part[wave][lane] = part;
   __syncthreads();
-  if (tid < kVals) {
+  if (tid < NV) {
     float sum = s_part[0][tid];
 #pragma unroll
     for (int w = 1; w < kWavesPerBlock; ++w) sum += s_part[w][tid];
@@ -323,21 +333,35 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(
   for (int j = 0; j < k; ++j) wout[t * k + j] = wout[t * k + j] / psum;
 }
 
+constexpr int64_t kSmallBatch = 256;
+
 template <bool BF16, int EM, bool NORM>
 hipError_t launch_em(const void* x, const float* router, const float* bias, int64_t T, int d,
                      int E, int k, float* logits_out, int32_t* idx, float* w,
                      const float* gamma, float eps, void* norm_out, hipStream_t s) {
-  constexpr int64_t per_block = kVals / EM;
+  // one token per block while the batch leaves CUs free (a decode batch: each
+  // block then does 1/TB of the arithmetic), else kVals / EM tokens per block
+  // so that the router rows are read by fewer blocks
+  constexpr int kBig = kVals / EM;
+  const int64_t per_block = T <= kSmallBatch ? 1 : kBig;
   const dim3 grid(static_cast<unsigned>((T + per_block - 1) / per_block));
   const dim3 block(kThreads);
   const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool vec = (d % 8 == 0) && a16(x) && a16(router) && (!NORM || (a16(gamma) && a16(norm_out)));
-  if (vec)
-    hipLaunchKernelGGL((route_kernel<BF16, EM, true, NORM>), grid, block, 0, s, x, router, bias, T,
-                       d, E, k, logits_out, idx, w, gamma, eps, norm_out);
-  else
-    hipLaunchKernelGGL((route_kernel<BF16, EM, false, NORM>), grid, block, 0, s, x, router, bias,
-                       T, d, E, k, logits_out, idx, w, gamma, eps, norm_out);
+  if (per_block == 1) {
+    if (vec)
+      hipLaunchKernelGGL((route_kernel<BF16, EM, 1, true, NORM>), grid, block, 0, s, x, router,
+                         bias, T, d, E, k, logits_out, idx, w, gamma, eps, norm_out);
+    else
+      hipLaunchKernelGGL((route_kernel<BF16, EM, 1, false, NORM>), grid, block, 0, s, x, router,
+                         bias, T, d, E, k, logits_out, idx, w, gamma, eps, norm_out);
+  } else if (vec) {
+    hipLaunchKernelGGL((route_kernel<BF16, EM, kBig, true, NORM>), grid, block, 0, s, x, router,
+                       bias, T, d, E, k, logits_out, idx, w, gamma, eps, norm_out);
+  } else {
+    hipLaunchKernelGGL((route_kernel<BF16, EM, kBig, false, NORM>), grid, block, 0, s, x, router,
+                       bias, T, d, E, k, logits_out, idx, w, gamma, eps, norm_out);
+  }
   return hipGetLastError();
 }
 
