@@ -277,6 +277,24 @@ def test_prefill_tiles_many_experts(m, E, k):
 
 # last 256-row tiles of 16, 48, 80, 128, 130, 0 (an exact multiple) and 250
 # rows, A above 1024 E
+@pytest.mark.parametrize("T,E,k,dtype", [(256, 8, 2, gen.BF16), (257, 8, 2, gen.BF16),
+                                         (256, 32, 4, gen.F32), (257, 32, 4, gen.BF16)])
+def test_router_work_splits(m, T, E, k, dtype):
+    """The router on either side of its switch between one token per
+    workgroup (up to 256 tokens) and 64 / EM tokens per workgroup (beyond),
+    for the 8- and 32-expert bounds: logits within LOGIT_TOL of the oracle's,
+    routing and weights by the certified rule."""
+    inp = gen.make_inputs(T=T, d=512, ffn=64, E=E, k=k, dtype=dtype, seed=80 + T + E)
+    print(f"[parity] router T={T} E={E} k={k} {dtype}", flush=True)
+    dev = to_device(inp)
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    idx, w = m.moe_route(dev["x"], dev["router"], k, logit_bias=dev["bias"], logits_out=logits)
+    torch.cuda.synchronize()
+    logits64 = oracle.router_logits(inp["x"], inp["router"], inp["bias"])
+    assert np.abs(host(logits) - logits64).max() <= LOGIT_TOL
+    check_routing(logits64, k, host(idx), host(w))
+
+
 MANY = [1552, 1584, 1616, 1664, 1666, 0, 2560, 1786]
 DOWN_ONLY = [1200, 480, 1040, 1600, 0, 1024, 2044, 804]  # A = 1024 E exactly
 BOTH = [8208, 8442]  # two experts, A just above 8192 E: w1 and w3 widened too
