@@ -318,7 +318,6 @@ def main():
     else:
         sets = std_sets
     torch.cuda.synchronize()
-    moe.moe_set_ffn_variant(args.variant)
     wdt = dev["x"].dtype
     # (int8 weights at prefill sizes also need room for widened codes)
     ws = moe.workspace(T, d, F, E, k, moe.MOE_INT8_PACKED if int8 else wdt, "cuda")
@@ -332,15 +331,15 @@ def main():
 
     def step(i, use_sets, is_packed, events=None):
         s = use_sets[i % 2]
-        moe.moe_set_stage_events(events)
         if args.block:
             moe.moe_block_forward(s["x"], g_dev, s["router"], s["w1"], s["w3"], s["w2"], k,
                                   eps=1e-5, logit_bias=s["bias"], out=out, norm_out=norm_out,
-                                  ws=ws, counts_out=counts, packed=is_packed)
+                                  ws=ws, counts_out=counts, packed=is_packed,
+                                  variant=args.variant, events=events)
         else:
             moe.moe_forward(s["x"], s["router"], s["w1"], s["w3"], s["w2"], k,
                             logit_bias=s["bias"], out=out, ws=ws, counts_out=counts,
-                            packed=is_packed)
+                            packed=is_packed, variant=args.variant, events=events)
 
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device="cuda")
@@ -363,7 +362,6 @@ def main():
         step(i, sets, packed, evs.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    moe.moe_set_stage_events(None)
     stage_ms = {name: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs.values()]))
                 for j, name in enumerate(STAGES)}
     for e in evs.values():

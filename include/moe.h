@@ -26,10 +26,14 @@
  *   topk_idx [T, k] int32, topk_w [T, k] float32: slot j of token t is
  *   assignment a = t*k + j.
  * Stream: `stream` is a hipStream_t (NULL = the null stream). All work is
- *   enqueued on it in order and the call returns without waiting. Two calls
- *   may run concurrently on different streams if they use distinct outputs
- *   and workspaces.
- * Sizes: 0 <= T, T*k < 2^31; 1 <= k <= E <= MOE_MAX_EXPERTS; d, ffn >= 1.
+ *   enqueued on it in order and the call returns without waiting. The
+ *   library keeps no state between calls (per-call choices travel in a
+ *   moe_options argument), so calls are re-entrant: two calls may run
+ *   concurrently, from any threads, on different streams if they use
+ *   distinct outputs and workspaces (moe_forward_noalloc is the exception:
+ *   its calls on one GPU share one scratch area).
+ * Sizes: 0 <= T, T*k <= MOE_MAX_ASSIGNMENTS; 1 <= k <= E <= MOE_MAX_EXPERTS;
+ *   d, ffn >= 1.
  *   T == 0 is valid: nothing is computed, except that moe_permute (and
  *   moe_forward's counts_out) still write zero counts and offsets.
  *   MOE_BF16 additionally needs d % 64 == 0,
@@ -74,6 +78,30 @@ enum moe_status {
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_BF16_PACKED = 2, MOE_INT8_PACKED = 3 };
 
 #define MOE_MAX_EXPERTS 32
+/* Largest T*k: 2^31 - 1024, so that the permutation's 1024-wide steps over
+ * the assignments stay within 32-bit indices. */
+#define MOE_MAX_ASSIGNMENTS 2147482624
+
+/* Per-call options of moe_expert_ffn, moe_forward, moe_block_forward and
+ * moe_forward_noalloc; NULL means every field at its default (0 / NULL).
+ * The struct is read during the call only and nothing of it is kept.
+ *   ffn_variant   expert-FFN kernel family for bf16 and int8 weights (float32
+ *                 ignores it): 0 = chosen by size, per projection and weight
+ *                 format; 1 = weight-streaming kernels (meant for few rows per
+ *                 expert); 2 = tiled MFMA kernels (meant for many; which tile
+ *                 kernel, and for int8 whether the codes are widened, still
+ *                 follows the size), for both projections. Any other value is
+ *                 MOE_EINVAL. The results are correct for every choice.
+ *   stage_events  NULL, or an array of 6 hipEvent_t the caller created, for
+ *                 profiling: the fused calls record events[0] before the
+ *                 router, events[1] after it, then events[2..5] after the
+ *                 permutation, the gate/up step, the down step and the
+ *                 combine, all on their stream (a NULL entry is MOE_EINVAL).
+ *                 moe_expert_ffn ignores it. */
+typedef struct moe_options {
+  int ffn_variant;
+  void* const* stage_events;
+} moe_options;
 
 /* Static description of a status code. Never NULL. */
 const char* moe_strerror(int status);
@@ -126,10 +154,12 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* count
  * better onto the GPU, it splits K two ways and adds the two float32 partial
  * sums in a fixed order; the split depends on T, d, ffn, E and k only, so
  * MOE_BF16 and MOE_BF16_PACKED give bit-identical y). ws must hold
- * moe_workspace_bytes(T, d, ffn, E, k, dtype) bytes. */
+ * moe_workspace_bytes(T, d, ffn, E, k, dtype) bytes. options: NULL or
+ * per-call options (the kernel family). */
 int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
                    const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d,
-                   int ffn, int E, int k, float* y, void* ws, size_t ws_bytes, void* stream);
+                   int ffn, int E, int k, float* y, void* ws, size_t ws_bytes, void* stream,
+                   const moe_options* options);
 
 /* Gate-weighted sum back in token order (nnterp page, Notes: each slot's
  * weighted expert output, summed over the slots, is the layer output):
@@ -143,12 +173,13 @@ int moe_combine(const float* y, const int32_t* asg_pos, const float* topk_w, int
 /* The whole layer: moe_route, moe_permute, moe_expert_ffn and moe_combine
  * in one call on one stream. topk_idx_out [T,k], topk_w_out [T,k] and
  * counts_out [E] are optional (NULL) copies of the routing; logit_bias may be
- * NULL. ws must hold moe_workspace_bytes(T, d, ffn, E, k, dtype) bytes. */
+ * NULL. ws must hold moe_workspace_bytes(T, d, ffn, E, k, dtype) bytes.
+ * options: NULL or per-call options (kernel family, stage events). */
 int moe_forward(const void* x, int dtype, const float* router, const float* logit_bias,
                 const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
                 int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
                 float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                void* stream);
+                void* stream, const moe_options* options);
 
 /* The MLP half of the decoder block around the layer (nnterp Mixtral page,
  * "The Notes", the block in order: out = h + mlp(post_attention_layernorm(h));
@@ -170,7 +201,7 @@ int moe_block_forward(const void* hidden, int dtype, const float* norm_weight, f
                       const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
                       int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
                       float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                      void* stream);
+                      void* stream, const moe_options* options);
 
 /* One-time weight preparation for the MOE_BF16_PACKED path: copies the
  * bfloat16 matrices w [E, rows, cols] (standard layout, cols contiguous) into
@@ -214,23 +245,6 @@ int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* o
 size_t moe_quantized_weight_bytes(int E, int rows, int cols);
 int moe_quantize_weight(const void* w, int dtype, int E, int rows, int cols, void* out,
                         void* stream);
-
-/* ---- tuning and profiling hooks (process-wide, not thread-safe) ---------- */
-
-/* Expert-FFN kernel family for bf16 and int8 weights: 0 = choose by size,
- * per projection and weight format (default), 1 = weight-streaming kernels
- * (few rows per expert), 2 = tiled MFMA kernels (many rows per expert; which
- * tile kernel, and for int8 whether the codes are widened in the workspace,
- * still follows the size), for both projections. Returns MOE_EINVAL for
- * other values. */
-int moe_set_ffn_variant(int variant);
-
-/* Profiling: when n == 6, moe_forward (and moe_block_forward) records events[0] before the router,
- * events[1] after it, then events[2..5] after the permutation, the gate/up
- * kernel, the down kernel and the combine, on its stream. Each events[i] is
- * a hipEvent_t the caller created. n == 0 (events may be NULL) turns it off.
- * The array is copied. */
-int moe_set_stage_events(void* const* events, int n);
 
 #ifdef __cplusplus
 }

@@ -21,11 +21,20 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16, MOE_BF16_PACKED, MOE_INT8_PACKED = 0, 1, 2, 3
 MOE_MAX_EXPERTS = 32
+MOE_MAX_ASSIGNMENTS = 2 ** 31 - 1024
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
 _c_sz = ctypes.c_size_t
 _vp = ctypes.c_void_p
+
+
+class MoeOptions(ctypes.Structure):
+    """struct moe_options (include/moe.h): per-call kernel family and stage events."""
+    _fields_ = [("ffn_variant", ctypes.c_int), ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+
+
+_opts_p = ctypes.POINTER(MoeOptions)
 
 _SIGNATURES = {
     "moe_strerror": (ctypes.c_char_p, [_c_int]),
@@ -34,18 +43,17 @@ _SIGNATURES = {
                            _vp]),
     "moe_permute": (_c_int, [_vp, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
     "moe_expert_ffn": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _c_int,
-                                _c_int, _c_int, _vp, _vp, _c_sz, _vp]),
+                                _c_int, _c_int, _vp, _vp, _c_sz, _vp, _opts_p]),
     "moe_combine": (_c_int, [_vp, _vp, _vp, _c_i64, _c_int, _c_int, _vp, _c_int, _vp]),
     "moe_forward": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _c_int,
-                             _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _c_sz, _vp]),
+                             _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _c_sz, _vp,
+                             _opts_p]),
     "moe_block_forward": (_c_int, [_vp, _c_int, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _vp, _c_int,
-                                   _vp, _vp, _vp, _vp, _c_sz, _vp]),
+                                   _vp, _vp, _vp, _vp, _c_sz, _vp, _opts_p]),
     "moe_pack_weight": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_quantized_weight_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
     "moe_quantize_weight": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
-    "moe_set_ffn_variant": (_c_int, [_c_int]),
-    "moe_set_stage_events": (_c_int, [_vp, _c_int]),
 }
 
 _lib = None
@@ -99,17 +107,41 @@ def _dtype_code(t: torch.dtype) -> int:
     raise ValueError(f"unsupported dtype {t} (float32 or bfloat16)")
 
 
-def _weight_code(t: torch.dtype, packed: bool, w=None) -> int:
+def _weight_code(t: torch.dtype, packed: bool, w1, w3, w2) -> int:
+    """The dtype code of the expert weights: all three int8 matrices
+    (QuantizedMatrix), or all three tensors of the activations' dtype
+    (fragment order when packed). A mix is refused before any library call."""
     code = _dtype_code(t)
-    if isinstance(w, QuantizedMatrix):
+    quant = [isinstance(w, QuantizedMatrix) for w in (w1, w3, w2)]
+    if any(quant) and not all(quant):
+        raise ValueError("w1, w3 and w2 must all be int8 (QuantizedMatrix) or all tensors")
+    if all(quant):
         if code != MOE_BF16:
             raise ValueError("int8 weights take bfloat16 activations")
+        if packed:
+            raise ValueError("int8 weights have their own layout (packed=False)")
         return MOE_INT8_PACKED
     if packed:
         if code != MOE_BF16:
             raise ValueError("packed weights are bfloat16 only")
         return MOE_BF16_PACKED
     return code
+
+
+def _options(variant: int = 0, events=None):
+    """A moe_options for one call (None when everything is at its default).
+    The returned object keeps the event array alive for the call."""
+    if not variant and not events:
+        return None
+    opts = MoeOptions()
+    opts.ffn_variant = int(variant)
+    if events:
+        if len(events) != 6:
+            raise ValueError("stage events: a sequence of 6 hipEvent_t handles")
+        arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(int(e)) for e in events])
+        opts.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        opts._keep = arr
+    return ctypes.pointer(opts)
 
 
 def _ptr(t):
@@ -126,9 +158,15 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, name, dtype, shape, device):
-    if isinstance(t, QuantizedMatrix):  # int8 codes + scales: shape and device only
+def _need(t, name, dtype, shape, device, code=None):
+    """Checks dtype, shape and device. An int8 QuantizedMatrix passes only where
+    the weight code is MOE_INT8_PACKED, and then on shape and device alone."""
+    if isinstance(t, QuantizedMatrix):
+        if code != MOE_INT8_PACKED:
+            raise ValueError(f"{name}: an int8 matrix where {dtype} weights are expected")
         dtype = t.dtype
+    elif code == MOE_INT8_PACKED:
+        raise ValueError(f"{name}: a tensor where int8 weights (QuantizedMatrix) are expected")
     if t.dtype != dtype:
         raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -138,20 +176,6 @@ def _need(t, name, dtype, shape, device):
 
 
 # ---------------------------------------------------------------------------
-def moe_set_ffn_variant(variant: int) -> None:
-    _check("moe_set_ffn_variant", load().moe_set_ffn_variant(int(variant)))
-
-
-def moe_set_stage_events(events) -> None:
-    """events: a sequence of 6 hipEvent_t handles (ints), or None to turn off."""
-    lib = load()
-    if not events:
-        _check("moe_set_stage_events", lib.moe_set_stage_events(None, 0))
-        return
-    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(int(e)) for e in events])
-    _check("moe_set_stage_events", lib.moe_set_stage_events(arr, len(events)))
-
-
 def moe_pack_weight(w, out=None):
     """Fragment-order copy of bf16 weights w [E, rows, cols] (see moe.h)."""
     if w.dtype != torch.bfloat16 or w.dim() != 3:
@@ -285,25 +309,27 @@ def moe_permute(topk_idx, E: int, counts=None, offsets=None, sorted_asg=None, as
     return counts, offsets, sorted_asg, asg_pos
 
 
-def moe_expert_ffn(x, w1, w3, w2, offsets, sorted_asg, k: int, y=None, ws=None, packed=False):
+def moe_expert_ffn(x, w1, w3, w2, offsets, sorted_asg, k: int, y=None, ws=None, packed=False,
+                   variant: int = 0):
     """Returns y [T*k, d] float32 (unweighted expert outputs, grouped order).
-    packed=True: w1/w3/w2 come from moe_pack_weight."""
+    packed=True: w1/w3/w2 come from moe_pack_weight. variant: the expert-FFN
+    kernel family (0 = by size, 1 = streaming, 2 = tiled)."""
     T, d = x.shape
     E, ffn, _ = w1.shape
     dev = x.device
+    code = _weight_code(x.dtype, packed, w1, w3, w2)
     for name, t, shp in (("w1", w1, (E, ffn, d)), ("w3", w3, (E, ffn, d)), ("w2", w2, (E, d, ffn))):
-        _need(t, name, x.dtype, shp, dev)
+        _need(t, name, x.dtype, shp, dev, code)
     _need(offsets, "offsets", torch.int32, (E + 1,), dev)
     _need(sorted_asg, "sorted_asg", torch.int32, (T * k,), dev)
     if y is None:
         y = torch.empty(T * k, d, dtype=torch.float32, device=dev)
     _need(y, "y", torch.float32, (T * k, d), dev)
-    code = _weight_code(x.dtype, packed, w1)
     if ws is None:
         ws = workspace(T, d, ffn, E, k, code, dev)
     st = load().moe_expert_ffn(_ptr(x), code, _ptr(w1), _ptr(w3), _ptr(w2),
                                _ptr(offsets), _ptr(sorted_asg), T, d, ffn, E, k, _ptr(y),
-                               _ptr(ws), ws.numel(), _stream(dev))
+                               _ptr(ws), ws.numel(), _stream(dev), _options(variant))
     _check("moe_expert_ffn", st)
     return y
 
@@ -326,15 +352,18 @@ def moe_combine(y, asg_pos, topk_w, out=None, out_dtype=torch.float32):
 
 
 def moe_forward(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dtype=None,
-                ws=None, topk_idx_out=None, topk_w_out=None, counts_out=None, packed=False):
+                ws=None, topk_idx_out=None, topk_w_out=None, counts_out=None, packed=False,
+                variant: int = 0, events=None):
     """The whole layer; returns out [T, d] (dtype out_dtype, default x.dtype).
-    packed=True: w1/w3/w2 come from moe_pack_weight."""
+    packed=True: w1/w3/w2 come from moe_pack_weight. variant: the expert-FFN
+    kernel family; events: 6 hipEvent_t handles recorded between the stages."""
     T, d = x.shape
     E, ffn, _ = w1.shape
     dev = x.device
+    code = _weight_code(x.dtype, packed, w1, w3, w2)
     _need(router, "router", torch.float32, (E, d), dev)
     for name, t, shp in (("w1", w1, (E, ffn, d)), ("w3", w3, (E, ffn, d)), ("w2", w2, (E, d, ffn))):
-        _need(t, name, x.dtype, shp, dev)
+        _need(t, name, x.dtype, shp, dev, code)
     if logit_bias is not None:
         _need(logit_bias, "logit_bias", torch.float32, (E,), dev)
     if out is None:
@@ -346,29 +375,31 @@ def moe_forward(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dt
         _need(topk_w_out, "topk_w_out", torch.float32, (T, k), dev)
     if counts_out is not None:
         _need(counts_out, "counts_out", torch.int32, (E,), dev)
-    code = _weight_code(x.dtype, packed, w1)
     if ws is None:
         ws = workspace(T, d, ffn, E, k, code, dev)
     st = load().moe_forward(_ptr(x), code, _ptr(router), _ptr(logit_bias),
                             _ptr(w1), _ptr(w3), _ptr(w2), T, d, ffn, E, k, _ptr(out),
                             _dtype_code(out.dtype), _ptr(topk_idx_out), _ptr(topk_w_out),
-                            _ptr(counts_out), _ptr(ws), ws.numel(), _stream(dev))
+                            _ptr(counts_out), _ptr(ws), ws.numel(), _stream(dev),
+                            _options(variant, events))
     _check("moe_forward", st)
     return out
 
 
 def moe_block_forward(hidden, norm_weight, router, w1, w3, w2, k: int, eps: float = 1e-5,
                       logit_bias=None, out=None, out_dtype=None, norm_out=None, ws=None,
-                      topk_idx_out=None, topk_w_out=None, counts_out=None, packed=False):
+                      topk_idx_out=None, topk_w_out=None, counts_out=None, packed=False,
+                      variant: int = 0, events=None):
     """out = hidden + layer(RMSNorm(hidden)); returns (out, norm_out).
     norm_weight [d] float32; norm_out [T, d] has hidden's dtype."""
     T, d = hidden.shape
     E, ffn, _ = w1.shape
     dev = hidden.device
+    code = _weight_code(hidden.dtype, packed, w1, w3, w2)
     _need(norm_weight, "norm_weight", torch.float32, (d,), dev)
     _need(router, "router", torch.float32, (E, d), dev)
     for name, t, shp in (("w1", w1, (E, ffn, d)), ("w3", w3, (E, ffn, d)), ("w2", w2, (E, d, ffn))):
-        _need(t, name, hidden.dtype, shp, dev)
+        _need(t, name, hidden.dtype, shp, dev, code)
     if logit_bias is not None:
         _need(logit_bias, "logit_bias", torch.float32, (E,), dev)
     if norm_out is None:
@@ -383,13 +414,13 @@ def moe_block_forward(hidden, norm_weight, router, w1, w3, w2, k: int, eps: floa
         _need(topk_w_out, "topk_w_out", torch.float32, (T, k), dev)
     if counts_out is not None:
         _need(counts_out, "counts_out", torch.int32, (E,), dev)
-    code = _weight_code(hidden.dtype, packed, w1)
     if ws is None:
         ws = workspace(T, d, ffn, E, k, code, dev)
     st = load().moe_block_forward(_ptr(hidden), code, _ptr(norm_weight), float(eps),
                                   _ptr(norm_out), _ptr(router), _ptr(logit_bias), _ptr(w1),
                                   _ptr(w3), _ptr(w2), T, d, ffn, E, k, _ptr(out),
                                   _dtype_code(out.dtype), _ptr(topk_idx_out), _ptr(topk_w_out),
-                                  _ptr(counts_out), _ptr(ws), ws.numel(), _stream(dev))
+                                  _ptr(counts_out), _ptr(ws), ws.numel(), _stream(dev),
+                                  _options(variant, events))
     _check("moe_block_forward", st)
     return out, norm_out

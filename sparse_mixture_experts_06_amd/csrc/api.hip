@@ -1,5 +1,7 @@
 // libmoe C ABI: argument checks, workspace carving and stream-ordered
-// launches. Nothing here allocates, frees or synchronises.
+// launches. Nothing here allocates, frees or synchronises, and nothing is
+// kept between calls: the per-call choices (kernel family, profiling events)
+// arrive in a moe_options argument.
 #include "moe.h"
 
 #include <string.h>
@@ -8,11 +10,26 @@
 
 namespace {
 
-constexpr int64_t kMaxAssignments = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxAssignments = MOE_MAX_ASSIGNMENTS;
+static_assert(kMaxAssignments + 1024 <= (int64_t(1) << 31), "the permutation's steps use int");
 
-int g_ffn_variant = 0;
-void* g_events[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-int g_nevents = 0;
+// a call's options, checked
+struct Opts {
+  int variant = 0;                     // expert-FFN kernel family (0 = by size)
+  void* const* events = nullptr;       // 6 stage events, or none
+};
+
+int read_options(const moe_options* o, Opts* out) {
+  *out = Opts{};
+  if (!o) return MOE_OK;
+  if (o->ffn_variant < 0 || o->ffn_variant > 2) return MOE_EINVAL;
+  if (o->stage_events)
+    for (int i = 0; i < 6; ++i)
+      if (!o->stage_events[i]) return MOE_EINVAL;
+  out->variant = o->ffn_variant;
+  out->events = o->stage_events;
+  return MOE_OK;
+}
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -91,8 +108,8 @@ int check_ffn_shape(int64_t T, int d, int ffn, int E, int k, int dtype) {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
-inline void stage(int i, hipStream_t s) {
-  if (g_nevents == 6 && g_events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(g_events[i]), s);
+inline void stage(const Opts& o, int i, hipStream_t s) {
+  if (o.events) (void)hipEventRecord(static_cast<hipEvent_t>(o.events[i]), s);
 }
 
 // gate/up then down; the down result is left as `nsplit_out` partial arrays
@@ -100,8 +117,8 @@ inline void stage(int i, hipStream_t s) {
 // the workspace region for int8 weights widened to bf16 (prefill sizes)
 int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
             const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d, int ffn, int E,
-            int k, float* part, void* h, void* wide, hipStream_t s, bool with_events,
-            int* nsplit_out) {
+            int k, float* part, void* h, void* wide, hipStream_t s, const Opts& opt,
+            bool with_events, int* nsplit_out) {
   const int64_t A = T * k;
   hipError_t err;
   if (dtype == MOE_INT8_PACKED) {
@@ -109,8 +126,8 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
     // the tiled kernel widening its operands in registers (more), or the
     // codes widened to bf16 in the workspace and the direct-to-LDS kernels
     // with row scales (many rows per expert)
-    const int variant = moe::choose_int8_ffn_variant(g_ffn_variant, A, E);
-    const int dvariant = moe::choose_int8_down_variant(g_ffn_variant, A, E);
+    const int variant = moe::choose_int8_ffn_variant(opt.variant, A, E);
+    const int dvariant = moe::choose_int8_down_variant(opt.variant, A, E);
     *nsplit_out = moe::int8_down_splits(dvariant, A, d, ffn, E);
     uint16_t* wb = static_cast<uint16_t*>(wide);
     if (variant != 1 && moe::int8_gate_up_dma(A, k, d, ffn, E)) {
@@ -127,7 +144,7 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
                                      sorted_asg, A, d, ffn, E, k, static_cast<uint16_t*>(h), s);
     }
     if (err != hipSuccess) return MOE_EHIP;
-    if (with_events) stage(3, s);
+    if (with_events) stage(opt, 3, s);
     if (dvariant != 1 && moe::int8_down_dma(A, d, ffn, E)) {
       // (stream order: gate/up has finished with the widened w1 and w3)
       err = moe::launch_widen_int8(w2, E, d, ffn, wb, s);
@@ -139,8 +156,8 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
                                   ffn, E, *nsplit_out, part, s);
     }
   } else if (is_bf16(dtype)) {
-    const int variant = moe::choose_ffn_variant(g_ffn_variant, A, E);
-    const int dvariant = moe::choose_down_variant(g_ffn_variant, A, E);
+    const int variant = moe::choose_ffn_variant(opt.variant, A, E);
+    const int dvariant = moe::choose_down_variant(opt.variant, A, E);
     const bool packed = dtype == MOE_BF16_PACKED;
     *nsplit_out = moe::down_splits(dvariant, A, d, ffn, E);
     err = moe::launch_gate_up_bf16(variant, packed, static_cast<const uint16_t*>(x),
@@ -148,7 +165,7 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
                                    static_cast<const uint16_t*>(w3), offsets, sorted_asg, A, d,
                                    ffn, E, k, static_cast<uint16_t*>(h), s);
     if (err != hipSuccess) return MOE_EHIP;
-    if (with_events) stage(3, s);
+    if (with_events) stage(opt, 3, s);
     err = moe::launch_down_bf16(dvariant, packed, static_cast<const uint16_t*>(h),
                                 static_cast<const uint16_t*>(w2), offsets, A, d, ffn, E, part, s);
   } else {
@@ -157,7 +174,7 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
                                   static_cast<const float*>(w3), offsets, sorted_asg, A, d, ffn,
                                   E, k, static_cast<float*>(h), s);
     if (err != hipSuccess) return MOE_EHIP;
-    if (with_events) stage(3, s);
+    if (with_events) stage(opt, 3, s);
     err = moe::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w2),
                                offsets, A, d, ffn, E, part, s);
   }
@@ -213,8 +230,12 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* count
 
 int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
                    const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d,
-                   int ffn, int E, int k, float* y, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_sizes(T, E, k);
+                   int ffn, int E, int k, float* y, void* ws, size_t ws_bytes, void* stream,
+                   const moe_options* options) {
+  Opts opt;
+  int st = read_options(options, &opt);
+  if (st != MOE_OK) return st;
+  st = check_sizes(T, E, k);
   if (st != MOE_OK) return st;
   st = check_ffn_shape(T, d, ffn, E, k, dtype);
   if (st != MOE_OK) return st;
@@ -231,15 +252,14 @@ int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, con
   const int64_t A = T * k;
   const int nsplit =
       dtype == MOE_INT8_PACKED
-          ? moe::int8_down_splits(moe::choose_int8_down_variant(g_ffn_variant, A, E), A, d, ffn, E)
+          ? moe::int8_down_splits(moe::choose_int8_down_variant(opt.variant, A, E), A, d, ffn, E)
       : is_bf16(dtype)
-          ? moe::down_splits(moe::choose_down_variant(g_ffn_variant, A, E), A, d, ffn, E)
+          ? moe::down_splits(moe::choose_down_variant(opt.variant, A, E), A, d, ffn, E)
           : 1;
   float* part = nsplit > 1 ? reinterpret_cast<float*>(base + L.y) : y;
   int used = 1;
   st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, part, base + L.h,
-               base + L.wide, s,
-               false, &used);
+               base + L.wide, s, opt, false, &used);
   if (st != MOE_OK) return st;
   if (used > 1)
     return hip_status(moe::launch_sum_partials(part, used, A * static_cast<int64_t>(d), y, s));
@@ -266,8 +286,11 @@ int forward_impl(const void* x, int dtype, const float* gamma, float eps, void* 
                  const float* router, const float* logit_bias, const void* w1, const void* w3,
                  const void* w2, int64_t T, int d, int ffn, int E, int k, void* out,
                  int out_dtype, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
-                 void* ws, size_t ws_bytes, void* stream) {
-  int st = check_sizes(T, E, k);
+                 void* ws, size_t ws_bytes, void* stream, const moe_options* options) {
+  Opts opt;
+  int st = read_options(options, &opt);
+  if (st != MOE_OK) return st;
+  st = check_sizes(T, E, k);
   if (st != MOE_OK) return st;
   st = check_ffn_shape(T, d, ffn, E, k, dtype);
   if (st != MOE_OK) return st;
@@ -292,27 +315,27 @@ int forward_impl(const void* x, int dtype, const float* gamma, float eps, void* 
   float* y = reinterpret_cast<float*>(base + L.y);
   const void* xin = gamma ? norm_out : x;  // what the experts read
 
-  stage(0, s);
+  stage(opt, 0, s);
   if (T > 0 && moe::launch_route(x, is_bf16(dtype), router, logit_bias, T, d, E, k, nullptr,
                                  idx, w, s, gamma, eps, norm_out) != hipSuccess)
     return MOE_EHIP;
-  stage(1, s);
+  stage(opt, 1, s);
   if (moe::launch_permute(idx, T * k, E, counts, offsets, sorted_asg, asg_pos, s) != hipSuccess)
     return MOE_EHIP;
-  stage(2, s);
+  stage(opt, 2, s);
   if (T == 0) {
-    for (int i = 3; i < 6; ++i) stage(i, s);
+    for (int i = 3; i < 6; ++i) stage(opt, i, s);
     return MOE_OK;
   }
   int nsplit = 1;
   st = run_ffn(xin, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, h, base + L.wide,
-               s, true, &nsplit);
+               s, opt, true, &nsplit);
   if (st != MOE_OK) return st;
-  stage(4, s);
+  stage(opt, 4, s);
   if (moe::launch_combine(y, nsplit, asg_pos, w, T, d, k, out, out_dtype == MOE_BF16, s,
                           gamma ? x : nullptr, is_bf16(dtype)) != hipSuccess)
     return MOE_EHIP;
-  stage(5, s);
+  stage(opt, 5, s);
   return MOE_OK;
 }
 
@@ -330,10 +353,10 @@ int moe_forward(const void* x, int dtype, const float* router, const float* logi
                 const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
                 int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
                 float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                void* stream) {
+                void* stream, const moe_options* options) {
   return forward_impl(x, dtype, nullptr, 0.0f, nullptr, router, logit_bias, w1, w3, w2, T, d,
                       ffn, E, k, out, out_dtype, topk_idx_out, topk_w_out, counts_out, ws,
-                      ws_bytes, stream);
+                      ws_bytes, stream, options);
 }
 
 int moe_block_forward(const void* hidden, int dtype, const float* norm_weight, float eps,
@@ -341,7 +364,7 @@ int moe_block_forward(const void* hidden, int dtype, const float* norm_weight, f
                       const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
                       int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
                       float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      void* stream, const moe_options* options) {
   if (!(eps >= 0.0f) || eps > 3.0e38f) return MOE_EINVAL;  // rejects NaN and infinity too
   if (T > 0) {
     if (!norm_weight || !norm_out || !hidden || !out) return MOE_EINVAL;
@@ -356,7 +379,7 @@ int moe_block_forward(const void* hidden, int dtype, const float* norm_weight, f
   }
   return forward_impl(hidden, dtype, norm_weight, eps, norm_out, router, logit_bias, w1, w3, w2,
                       T, d, ffn, E, k, out, out_dtype, topk_idx_out, topk_w_out, counts_out, ws,
-                      ws_bytes, stream);
+                      ws_bytes, stream, options);
 }
 
 size_t moe_quantized_weight_bytes(int E, int rows, int cols) {
@@ -395,25 +418,6 @@ int moe_pack_weight(const void* w, int dtype, int E, int rows, int cols, void* o
   return hip_status(moe::launch_pack_bf16(static_cast<const uint16_t*>(w), E, rows, cols,
                                           static_cast<uint16_t*>(out),
                                           static_cast<hipStream_t>(stream)));
-}
-
-int moe_set_ffn_variant(int variant) {
-  if (variant < 0 || variant > 2) return MOE_EINVAL;
-  g_ffn_variant = variant;
-  return MOE_OK;
-}
-
-int moe_set_stage_events(void* const* events, int n) {
-  if (n == 0) {
-    g_nevents = 0;
-    return MOE_OK;
-  }
-  if (n != 6 || !events) return MOE_EINVAL;
-  for (int i = 0; i < 6; ++i)
-    if (!events[i]) return MOE_EINVAL;
-  memcpy(g_events, events, sizeof(g_events));
-  g_nevents = 6;
-  return MOE_OK;
 }
 
 }  // extern "C"

@@ -93,7 +93,7 @@ def test_expert_ffn_rejects_bad_arguments():
     ws = moe.moe_workspace_bytes(4, 128, 256, 8, 2, moe.MOE_BF16)
     args = lambda **kw: [kw.get("x", BAD), kw.get("dtype", moe.MOE_BF16), BAD, BAD, BAD, BAD, BAD,
                          kw.get("T", 4), kw.get("d", 128), kw.get("ffn", 256), 8, 2, BAD,
-                         kw.get("ws", BAD), kw.get("wsb", ws), None]
+                         kw.get("ws", BAD), kw.get("wsb", ws), None, None]
     assert f(*args(d=100)) == moe.MOE_ENOTSUP                  # bf16 needs d % 64 == 0
     assert f(*args(ffn=96)) == moe.MOE_ENOTSUP                 # and ffn % 64 == 0
     assert f(*args(dtype=9)) == moe.MOE_EINVAL
@@ -116,7 +116,7 @@ def test_combine_and_forward_reject_bad_arguments():
         return fw(kw.get("x", BAD), kw.get("dtype", moe.MOE_BF16), BAD, None, BAD, BAD, BAD,
                   kw.get("T", 4), kw.get("d", 128), 256, kw.get("E", 8), kw.get("k", 2), BAD,
                   kw.get("odt", moe.MOE_BF16), None, None, None, kw.get("ws", BAD),
-                  kw.get("wsb", ws), None)
+                  kw.get("wsb", ws), None, kw.get("opts"))
 
     assert call(k=0) == moe.MOE_EINVAL
     assert call(E=40) == moe.MOE_EINVAL
@@ -147,7 +147,7 @@ def test_int8_weights_share_the_bf16_rules():
     ws = moe.moe_workspace_bytes(4, 128, 256, 8, 2, moe.MOE_INT8_PACKED)
     assert ws == moe.moe_workspace_bytes(4, 128, 256, 8, 2, moe.MOE_BF16)    # h is bf16 too
     base = [BAD, moe.MOE_INT8_PACKED, BAD, BAD, BAD, BAD, BAD, 4, 128, 256, 8, 2, BAD, BAD, ws,
-            None]
+            None, None]
     bad_d = list(base)
     bad_d[8] = 100
     assert f(*bad_d) == moe.MOE_ENOTSUP
@@ -167,18 +167,94 @@ def test_pack_weight_rejects_bad_arguments():
               ctypes.c_void_p((1 << 40) + 4096), None) == moe.MOE_EINVAL   # overlapping buffers
 
 
-def test_tuning_hooks_validate():
-    assert lib.moe_set_ffn_variant(3) == moe.MOE_EINVAL
-    assert lib.moe_set_ffn_variant(-1) == moe.MOE_EINVAL
-    assert lib.moe_set_ffn_variant(0) == moe.MOE_OK
-    assert lib.moe_set_stage_events(None, 3) == moe.MOE_EINVAL
-    assert lib.moe_set_stage_events(None, 6) == moe.MOE_EINVAL
-    assert lib.moe_set_stage_events(None, 0) == moe.MOE_OK
+def _options(variant=0, events=None):
+    o = moe.MoeOptions()
+    o.ffn_variant = variant
+    if events is not None:
+        arr = (ctypes.c_void_p * 6)(*events)
+        o.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        o._keep = arr
+    return ctypes.pointer(o)
+
+
+def test_options_are_checked_per_call():
+    """The kernel family and the stage events travel with each call (nothing
+    is kept between calls); bad values are refused before anything runs."""
+    fw = lib.moe_forward
+    f = lib.moe_expert_ffn
+    ws = moe.moe_workspace_bytes(4, 128, 256, 8, 2, moe.MOE_BF16)
+
+    def fwd(opts):
+        return fw(BAD, moe.MOE_BF16, BAD, None, BAD, BAD, BAD, 4, 128, 256, 8, 2, BAD,
+                  moe.MOE_BF16, None, None, None, BAD, ws, None, opts)
+
+    def ffn(opts):
+        return f(BAD, moe.MOE_BF16, BAD, BAD, BAD, BAD, BAD, 4, 128, 256, 8, 2, BAD, BAD, ws,
+                 None, opts)
+
+    for bad in (_options(3), _options(-1), _options(0, [1, 2, 3, None, 5, 6])):
+        assert fwd(bad) == moe.MOE_EINVAL
+        assert ffn(bad) == moe.MOE_EINVAL
+    # valid options leave the other checks in charge (here: the workspace)
+    assert fw(BAD, moe.MOE_BF16, BAD, None, BAD, BAD, BAD, 4, 128, 256, 8, 2, BAD, moe.MOE_BF16,
+              None, None, None, BAD, 0, None, _options(2, [1, 2, 3, 4, 5, 6])) == \
+        moe.MOE_EWORKSPACE
+    # T == 0 with valid options: nothing to do
+    assert f(None, moe.MOE_BF16, None, None, None, None, None, 0, 128, 256, 8, 2, None, None, 0,
+             None, _options(1)) == moe.MOE_OK
+
+
+def test_assignment_cap():
+    """T*k is capped at 2^31 - 1024 so the permutation's 1024-wide steps stay
+    inside 32-bit indices."""
+    cap = moe.MOE_MAX_ASSIGNMENTS
+    assert cap == 2 ** 31 - 1024
+    p = lib.moe_permute
+    assert p(BAD, cap // 2 + 1, 8, 2, BAD, BAD, BAD, BAD, None, 0, None) == moe.MOE_EINVAL
+    assert p(BAD, cap + 1, 8, 1, BAD, BAD, BAD, BAD, None, 0, None) == moe.MOE_EINVAL
+    assert moe.moe_workspace_bytes(cap // 2, 64, 64, 8, 2, moe.MOE_F32) > 0
+    assert moe.moe_workspace_bytes(cap // 2 + 1, 64, 64, 8, 2, moe.MOE_F32) == 0
+    assert moe.moe_workspace_bytes(cap + 1, 64, 64, 8, 1, moe.MOE_F32) == 0
 
 
 def test_binding_raises_on_error_status():
+    from sparse_mixture_experts_06_amd import _lib
+    st = lib.moe_forward(BAD, moe.MOE_BF16, BAD, None, BAD, BAD, BAD, 4, 128, 256, 8, 2, BAD,
+                         moe.MOE_BF16, None, None, None, BAD, 1 << 20, None, _lib._options(7))
+    assert st == moe.MOE_EINVAL          # kernel family 7, refused before anything runs
     with pytest.raises(moe.MoeError):
-        moe.moe_set_ffn_variant(7)
+        _lib._check("moe_forward", st)
+
+
+def test_binding_refuses_mixed_weight_formats(monkeypatch):
+    """w1, w3 and w2 must be all int8 matrices or all tensors of x's dtype:
+    a mix is refused before the library is called."""
+    import torch
+    from sparse_mixture_experts_06_amd import _lib
+
+    def no_call():
+        raise AssertionError("the library must not be called")
+    monkeypatch.setattr(_lib, "load", no_call)
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    r = torch.zeros(8, 128, dtype=torch.float32)
+    w13 = torch.zeros(8, 256, 128, dtype=torch.bfloat16)
+    w2 = torch.zeros(8, 128, 256, dtype=torch.bfloat16)
+    q13 = _lib.QuantizedMatrix(torch.zeros(8 * 256 * 128 + 8 * 256 * 4, dtype=torch.uint8),
+                               (8, 256, 128))
+    q2 = _lib.QuantizedMatrix(torch.zeros(8 * 128 * 256 + 8 * 128 * 4, dtype=torch.uint8),
+                              (8, 128, 256))
+    off = torch.zeros(9, dtype=torch.int32)
+    sasg = torch.zeros(8, dtype=torch.int32)
+    g = torch.ones(128)
+    for w1, w3, w2_ in ((w13, q13, q2), (q13, w13, w2), (q13, q13, w2), (w13, w13, q2)):
+        with pytest.raises(ValueError):
+            moe.moe_forward(x, r, w1, w3, w2_, 2)
+        with pytest.raises(ValueError):
+            moe.moe_expert_ffn(x, w1, w3, w2_, off, sasg, 2)
+        with pytest.raises(ValueError):
+            moe.moe_block_forward(x, g, r, w1, w3, w2_, 2)
+    with pytest.raises(ValueError):     # int8 matrices are not fragment order
+        moe.moe_forward(x, r, q13, q13, q2, 2, packed=True)
 
 
 def test_block_forward_rejects_bad_arguments():
@@ -192,7 +268,7 @@ def test_block_forward_rejects_bad_arguments():
         return fb(kw.get("h", H), kw.get("dtype", moe.MOE_BF16), kw.get("g", BAD),
                   ctypes.c_float(kw.get("eps", 1e-5)), kw.get("n", N), BAD, None, BAD, BAD, BAD,
                   kw.get("T", 4), 128, 256, 8, 2, kw.get("o", O), kw.get("odt", moe.MOE_F32),
-                  None, None, None, BAD, ws, None)
+                  None, None, None, BAD, ws, None, None)
 
     assert call(eps=-1e-5) == moe.MOE_EINVAL
     assert call(eps=float("nan")) == moe.MOE_EINVAL
@@ -207,5 +283,6 @@ def test_block_forward_rejects_bad_arguments():
     assert call(o=ctypes.c_void_p((1 << 40) + 4096 + 64)) == moe.MOE_EINVAL
     # the rest as for moe_forward: shape, workspace and alignment checks
     assert fb(H, moe.MOE_BF16, BAD, ctypes.c_float(1e-5), N, BAD, None, BAD, BAD, BAD, 4, 128,
-              256, 8, 2, O, moe.MOE_F32, None, None, None, BAD, 0, None) == moe.MOE_EWORKSPACE
+              256, 8, 2, O, moe.MOE_F32, None, None, None, BAD, 0, None,
+              None) == moe.MOE_EWORKSPACE
     assert call(h=ctypes.c_void_p((1 << 40) + 8)) == moe.MOE_ENOTSUP

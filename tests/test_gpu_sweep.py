@@ -43,7 +43,6 @@ def _case(i):
 @pytest.fixture(scope="module")
 def m():
     import sparse_mixture_experts_06_amd as lib
-    lib.moe_set_ffn_variant(0)
     yield lib
 
 
