@@ -21,7 +21,12 @@ with the standard [E, ffn, d] layout is measured too and reported beside it.
 and the residual add after it (the MLP half of the decoder block).
 
 Prints one JSON line: tokens/s for the whole job, the dominant kernel's
-roofline position and the CPU oracle's throughput on a bounded sample.
+roofline position and the CPU oracle's throughput on a bounded sample. The
+default run (the decode workload) also times the other named workloads --
+prefill and skewed prefill at the 8x7B shape, prefill at the 8x22B shape and
+the tiny float32 layer -- and reports each under "workloads" with its own
+rooflines (gate/up and down, against the bf16 MFMA peak where the experts
+get many rows); --no-extra-workloads (or naming a --workload) times one.
 """
 from __future__ import annotations
 
@@ -58,7 +63,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="decode_8x7b",
+    p.add_argument("--workload", default=None,
                    help="decode_8x7b (default), prefill_8x7b, skew_8x7b, prefill_8x22b, tiny")
     p.add_argument("--tokens", type=int, default=0,
                    help="override the workload's batch size T (same shapes and seed otherwise)")
@@ -76,6 +81,11 @@ def parse():
                    help="time the MLP half of the decoder block instead of the bare layer: "
                         "RMS norm in front (eps 1e-5) and the residual add after "
                         "(moe_block_forward)")
+    p.add_argument("--no-extra-workloads", action="store_true",
+                   help="time only --workload (the default run also times prefill_8x7b, "
+                        "skew_8x7b, prefill_8x22b and tiny)")
+    p.add_argument("--extra-steps", type=int, default=20,
+                   help="timed steps of each extra workload (after 5 warm-up steps)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first copy a buffer of this many MiB once (a known-size kernel that "
                         "calibrates hardware byte counters under a profiler)")
@@ -145,6 +155,18 @@ def algorithmic_work(cfg, counts, block=False, int8=False):
     return layer_bytes, layer_flops, gate_up_bytes, gate_up_flops
 
 
+def down_work(cfg, counts, int8=False):
+    """Algorithmic bytes and flops of the down projection: w2 of the active
+    experts, h read (A rows of ffn, the gate/up output) and y written (A rows
+    of d, float32)."""
+    T, d, F, E, k = cfg["T"], cfg["d"], cfg["ffn"], cfg["E"], cfg["k"]
+    wb = 2 if cfg["dtype"] == "bf16" else 4
+    A = T * k
+    active = sum(1 for c in counts if c > 0)
+    w = active * (d * F + d * 4) if int8 else active * d * F * wb
+    return w + A * F * wb + A * d * 4, 2 * A * F * d
+
+
 def ffn_sources_sha():
     """Hash of the expert-kernel sources with comments and layout removed, so
     that the traffic records follow the code, not its comments."""
@@ -158,9 +180,9 @@ def ffn_sources_sha():
     return h.hexdigest()
 
 
-def traffic_entry(workload):
-    """rocprofv3 FETCH/WRITE bytes of the gate/up kernel, if they were taken
-    on the current kernel source."""
+def traffic_entry(workload, kernel="gate_up"):
+    """rocprofv3 FETCH/WRITE bytes of the gate/up (or down) kernel, if they were
+    taken on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -170,11 +192,15 @@ def traffic_entry(workload):
     ent = rec.get("workloads", {}).get(workload)
     if not ent or rec.get("ffn_sources_sha256") != sha:
         return None
+    if kernel == "down":
+        ent = ent.get("down") or {}
     return ent.get("hbm_bytes_per_launch")
 
 
 GATE_UP_KERNELS = ("gate_up_stream_kernel", "gate_up_dma_kernel", "tiled_kernel<true",
-                   "gate_up_w8_kernel")
+                   "wtiled_kernel<true", "gate_up_w8_kernel")
+DOWN_KERNELS = ("down_stream_kernel", "down_dma_kernel", "tiled_kernel<false",
+                "wtiled_kernel<false", "down_w8_kernel")
 
 
 def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
@@ -191,16 +217,24 @@ def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
                and abs(float(r["Counter_Value"]) - calib) < 0.6 * calib]
         gu = [float(r["Counter_Value"]) for r in rows
               if any(k in r["Kernel_Name"] for k in GATE_UP_KERNELS)]
-        return cal, gu, rows
+        dn = [float(r["Counter_Value"]) for r in rows
+              if any(k in r["Kernel_Name"] for k in DOWN_KERNELS)]
+        return cal, gu, dn
 
-    f_cal, f_gu, _ = load(fetch_csv)
-    w_cal, w_gu, _ = load(write_csv)
+    f_cal, f_gu, f_dn = load(fetch_csv)
+    w_cal, w_gu, w_dn = load(write_csv)
     if not (f_cal and w_cal and f_gu and w_gu):
         raise SystemExit("calibration copy or gate/up kernel not found in the counter files")
     f_factor = f_cal[-1] / calib
     w_factor = w_cal[-1] / calib
     fetch = sum(f_gu) / len(f_gu) / f_factor * 1024
     write = sum(w_gu) / len(w_gu) / w_factor * 1024
+    down = None
+    if f_dn and w_dn:
+        dfetch = sum(f_dn) / len(f_dn) / f_factor * 1024
+        dwrite = sum(w_dn) / len(w_dn) / w_factor * 1024
+        down = {"hbm_bytes_per_launch": int(dfetch + dwrite), "fetch_bytes": int(dfetch),
+                "write_bytes": int(dwrite), "dispatches": len(f_dn)}
     sha = ffn_sources_sha()
     try:
         with open(TRAFFIC_FILE) as f:
@@ -215,6 +249,8 @@ def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
         "write_bytes": int(write), "fetch_counter_per_byte": round(f_factor, 5),
         "write_counter_per_byte": round(w_factor, 5), "dispatches": len(f_gu),
         "calibration": f"one {calib_mib} MiB device-to-device copy"}
+    if down is not None:
+        rec["workloads"][workload]["down"] = down
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec["workloads"][workload]))
@@ -263,43 +299,85 @@ def cpu_baseline(cfg, inp, budget_s=10.0, gamma=None):
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
-def main():
-    args = parse()
-    if args.pmc_summary:
-        key = args.workload + ("+block" if args.block else "") + \
-            ("+int8" if args.weights == "int8" else "")
-        pmc_summary(key, args.pmc_summary[0], args.pmc_summary[1],
-                    args.calib_copy_mib or 1024)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "the layer's multi-GPU path is not built in this library.", file=sys.stderr)
-        sys.exit(2)
-
+def cpu_info():
+    """The host's CPU model and NumPy's BLAS (name, version, threading layer)."""
     import numpy as np
-    import torch
+    import threadpoolctl
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [f"{p.get('internal_api')} {p.get('version')} ({p.get('threading_layer')}, "
+            f"{p.get('num_threads')} threads)"
+            for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    try:
+        deps = np.show_config(mode="dicts").get("Build Dependencies", {})
+        built = deps.get("blas", {}).get("name")
+    except Exception:  # pragma: no cover
+        built = None
+    return {"cpu_model": model, "blas": "; ".join(blas) or "unknown", "numpy_blas_build": built,
+            "numpy": np.__version__}
+
+
+def cpu_single_thread(names, reps=5):
+    """The float64 oracle on the whole batch of each named workload with BLAS
+    held to one thread: best of `reps` wall-clock runs (seconds, tokens/s)."""
+    import threadpoolctl
 
     import gen
-    import sparse_mixture_experts_06_amd as moe
+    import oracle
+    out = {}
+    for name in names:
+        cfg = dict(gen.CONFIGS[name])
+        inp = gen.make_inputs(**cfg)
+        best = None
+        with threadpoolctl.threadpool_limits(1):
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                oracle.forward(inp["x"], inp["router"], inp["w1"], inp["w3"], inp["w2"], cfg["k"],
+                               inp["bias"])
+                dt = time.perf_counter() - t0
+                best = dt if best is None else min(best, dt)
+        out[name] = {"seconds": round(best, 4), "tokens_per_s": round(cfg["T"] / best, 2),
+                     "tokens": cfg["T"], "threads": 1, "repeats": reps, "statistic": "best"}
+        del inp
+    return out
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
-    cfg = dict(gen.CONFIGS[args.workload])
-    if args.tokens > 0:
-        cfg["T"] = args.tokens
+
+def roofline(bytes_, flops, seconds, bound):
+    if bound == "hbm":
+        ach = bytes_ / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    ach = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+
+
+def time_workload(moe, torch, hip, cfg, key, steps, warmup, variant=0, layout="packed",
+                  compare=True, int8=False, block=False, calib_mib=0, inp=None):
+    """Times `steps` layer calls on one workload (after `warmup`), alternating
+    between two copies of the expert weights, with the library's stage events
+    on every EVENT_EVERY-th timed step. `inp`: the host inputs when already
+    drawn. Returns (record, host inputs, gamma)."""
+    import numpy as np
+
+    import gen
     T, d, F, E, k = cfg["T"], cfg["d"], cfg["ffn"], cfg["E"], cfg["k"]
-    print(f"[bench] workload {args.workload}: T={T} d={d} ffn={F} E={E} k={k} {cfg['dtype']}",
+    print(f"[bench] workload {key}: T={T} d={d} ffn={F} E={E} k={k} {cfg['dtype']}",
           file=sys.stderr, flush=True)
-    inp = gen.make_inputs(**cfg)
+    if inp is None:
+        inp = gen.make_inputs(**cfg)
     dev = upload(inp, torch)
     std_sets = [dev, dict(dev, w1=dev["w1"].clone(), w3=dev["w3"].clone(), w2=dev["w2"].clone())]
-    int8 = args.weights == "int8"
     if int8 and cfg["dtype"] != "bf16":
         raise SystemExit("int8 weights go with bfloat16 activations")
-    packed = args.layout == "packed" and cfg["dtype"] == "bf16" and not int8
+    packed = layout == "packed" and cfg["dtype"] == "bf16" and not int8
     if int8:
         q_sets = []
         for st in std_sets:
@@ -312,7 +390,7 @@ def main():
         for st in std_sets:
             pw = moe.PackedWeights(st["w1"], st["w3"], st["w2"])
             pk_sets.append(dict(st, w1=pw.w1, w3=pw.w3, w2=pw.w2))
-        if args.no_compare:
+        if not compare:
             std_sets = None
         sets = pk_sets
     else:
@@ -323,42 +401,41 @@ def main():
     ws = moe.workspace(T, d, F, E, k, moe.MOE_INT8_PACKED if int8 else wdt, "cuda")
     out = torch.empty(T, d, dtype=wdt, device="cuda")
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
-    hip = Hip()
-    gamma = gen.make_norm_weight(d, cfg["seed"]) if args.block else None
-    if args.block:
+    gamma = gen.make_norm_weight(d, cfg["seed"]) if block else None
+    if block:
         g_dev = torch.from_numpy(gamma).cuda()
         norm_out = torch.empty(T, d, dtype=wdt, device="cuda")
 
     def step(i, use_sets, is_packed, events=None):
         s = use_sets[i % 2]
-        if args.block:
+        if block:
             moe.moe_block_forward(s["x"], g_dev, s["router"], s["w1"], s["w3"], s["w2"], k,
                                   eps=1e-5, logit_bias=s["bias"], out=out, norm_out=norm_out,
-                                  ws=ws, counts_out=counts, packed=is_packed,
-                                  variant=args.variant, events=events)
+                                  ws=ws, counts_out=counts, packed=is_packed, variant=variant,
+                                  events=events)
         else:
             moe.moe_forward(s["x"], s["router"], s["w1"], s["w3"], s["w2"], k,
                             logit_bias=s["bias"], out=out, ws=ws, counts_out=counts,
-                            packed=is_packed, variant=args.variant, events=events)
+                            packed=is_packed, variant=variant, events=events)
 
-    if args.calib_copy_mib:
-        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device="cuda")
+    if calib_mib:
+        src = torch.ones(calib_mib << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, sets, packed)
     torch.cuda.synchronize()
     # stage events on every EVENT_EVERY-th timed step: each event record makes the
     # GPU idle a few microseconds between kernels, so recording all six on
     # every step would itself slow the step down by about 5% at decode
-    ev_steps = list(range(0, args.steps, EVENT_EVERY))
+    ev_steps = list(range(0, steps, EVENT_EVERY))
     evs = {i: [hip.event() for _ in range(6)] for i in ev_steps}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, sets, packed, evs.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -370,60 +447,132 @@ def main():
 
     other = None
     if packed and std_sets is not None:
-        for i in range(args.warmup):
+        for i in range(warmup):
             step(i, std_sets, False)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             step(i, std_sets, False)
         torch.cuda.synchronize()
-        ms_std = (time.perf_counter() - t1) * 1e3 / args.steps
+        ms_std = (time.perf_counter() - t1) * 1e3 / steps
         other = {"layout": "standard [E, ffn, d]", "value": round(T / (ms_std / 1e3), 1),
                  "ms_per_step": round(ms_std, 4)}
 
     cnt = counts.cpu().tolist()
-    workload_key = (args.workload + (f"+T{T}" if args.tokens > 0 else "") +
-                    ("+block" if args.block else "") + ("+int8" if int8 else ""))
-    layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt, args.block, int8)
-    ms_step = wall * 1e3 / args.steps
+    layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt, block, int8)
+    dn_bytes, dn_flops = down_work(cfg, cnt, int8)
+    ms_step = wall * 1e3 / steps
     tok_s = T / (ms_step / 1e3)
-    decode_like = (T * k) <= 32 * E  # the streaming kernels' regime: weight-bandwidth bound
-    gu_s = stage_ms["gate_up"] / 1e3
-    if decode_like:
-        ach = gu_bytes / gu_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4)}
-    else:
-        ach = gu_flops / gu_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    # the streaming kernels' regime (few rows per expert): weight-bandwidth
+    # bound; beyond it the tiled kernels are bound by the bf16 MFMA rate
+    bound = "hbm" if (T * k) <= 32 * E else "mfma"
+    roof = roofline(gu_bytes, gu_flops, stage_ms["gate_up"] / 1e3, bound)
     roof.update({"kernel": "gate_up (w1/w3 grouped GEMM + SiLU*mul)",
                  "avg_us": round(stage_ms["gate_up"] * 1e3, 2),
                  "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops,
-                 "traffic": traffic_entry(workload_key)})
+                 "traffic": traffic_entry(key)})
+    droof = roofline(dn_bytes, dn_flops, stage_ms["down"] / 1e3, bound)
+    droof.update({"kernel": "down (w2 grouped GEMM)", "avg_us": round(stage_ms["down"] * 1e3, 2),
+                  "algorithmic_bytes": dn_bytes, "algorithmic_flops": dn_flops,
+                  "traffic": traffic_entry(key, "down")})
     layer_tflops = layer_flops / (ms_step / 1e3) / 1e12
     layer_gbs = layer_bytes / (ms_step / 1e3) / 1e9
     rec = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg["dtype"], "data": "synthetic",
-        "config": {"workload": workload_key, "T": T, "d": d,
-                   "ffn": F, "E": E, "k": k, "seed": cfg["seed"], "logit_bias": cfg["bias"]},
+        "value": round(tok_s, 1), "unit": "tokens/s", "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_step, 4), "dtype": cfg["dtype"],
+        "config": {"workload": key, "T": T, "d": d, "ffn": F, "E": E, "k": k,
+                   "seed": cfg["seed"], "logit_bias": cfg["bias"]},
         "roofline": roof,
+        "down_roofline": droof,
         "layer": {"tflops": round(layer_tflops, 2),
                   "tflops_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
                   "gbs": round(layer_gbs, 1), "gbs_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                   "algorithmic_bytes": layer_bytes, "algorithmic_flops": layer_flops,
                   "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
                   "expert_counts": cnt},
+        "weights_layout": ("weight-only int8, float32 row scales (moe_quantize_weight once at "
+                           "load time)" if int8 else
+                           "fragment order (moe_pack_weight once at load time)" if packed
+                           else "standard [E, ffn, d]" if cfg["dtype"] == "bf16"
+                           else "standard [E, ffn, d] float32"),
     }
-    rec["weights_layout"] = ("weight-only int8, float32 row scales (moe_quantize_weight once at "
-                             "load time)" if int8 else
-                             "fragment order (moe_pack_weight once at load time)" if packed
-                             else "standard [E, ffn, d]")
     if other is not None:
         rec["other_layout"] = other
+    del std_sets, sets, dev, ws, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, inp, gamma
+
+
+EXTRA_WORKLOADS = ("prefill_8x7b", "skew_8x7b", "prefill_8x22b", "tiny")
+# other routing settings at the 8x7B widths, (decode, prefill) pairs drawn once:
+# the decode batch is the first 32 rows of the prefill batch, same weights
+ROUTING_WORKLOADS = (("decode_8x7b_k1", "prefill_8x7b_k1"), ("decode_e16", "prefill_e16"),
+                     ("decode_e32", "prefill_e32"))
+
+
+def main():
+    args = parse()
+    workload = args.workload or "decode_8x7b"
+    if args.pmc_summary:
+        key = workload + ("+block" if args.block else "") + \
+            ("+int8" if args.weights == "int8" else "")
+        pmc_summary(key, args.pmc_summary[0], args.pmc_summary[1],
+                    args.calib_copy_mib or 1024)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the layer's multi-GPU path is not built in this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gen
+    import sparse_mixture_experts_06_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    hip = Hip()
+    cfg = dict(gen.CONFIGS[workload])
+    if args.tokens > 0:
+        cfg["T"] = args.tokens
+    int8 = args.weights == "int8"
+    key = (workload + (f"+T{cfg['T']}" if args.tokens > 0 else "") +
+           ("+block" if args.block else "") + ("+int8" if int8 else ""))
+    rec, inp, gamma = time_workload(moe, torch, hip, cfg, key, args.steps, args.warmup,
+                                    variant=args.variant, layout=args.layout,
+                                    compare=not args.no_compare, int8=int8, block=args.block,
+                                    calib_mib=args.calib_copy_mib)
+    line = {"metric": METRIC, "value": rec["value"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": rec["dtype"], "data": "synthetic", "config": rec["config"],
+            "roofline": rec["roofline"]}
+    for name in ("down_roofline", "layer", "weights_layout", "other_layout"):
+        if name in rec:
+            line[name] = rec[name]
+
+    extras = (args.workload is None and not args.no_extra_workloads and args.tokens == 0
+              and not args.block and not int8 and args.variant == 0 and args.layout == "packed")
+    if extras:
+        line["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            wrec, _, _ = time_workload(moe, torch, hip, dict(gen.CONFIGS[name]), name,
+                                       args.extra_steps, 5, compare=name != "tiny")
+            line["workloads"][name] = wrec
+        for dname, pname in ROUTING_WORKLOADS:
+            pcfg, dcfg = dict(gen.CONFIGS[pname]), dict(gen.CONFIGS[dname])
+            pinp = gen.make_inputs(**pcfg)
+            dinp = dict(pinp, T=dcfg["T"], x=pinp["x"][:dcfg["T"]])
+            for name, c, i in ((dname, dcfg, dinp), (pname, pcfg, pinp)):
+                wrec, _, _ = time_workload(moe, torch, hip, c, name, args.extra_steps, 5,
+                                           compare=False, inp=i)
+                line["workloads"][name] = wrec
+            del pinp, dinp
+
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         base_inp = inp
@@ -432,8 +581,14 @@ def main():
             for name in ("w1", "w3", "w2"):
                 q, sc = oracle_quantized(name, inp)
                 base_inp[name] = q
-        rec["cpu_baseline"] = cpu_baseline(cfg, base_inp, gamma=gamma)
-    print(json.dumps(rec), flush=True)
+        cb = cpu_baseline(cfg, base_inp, gamma=gamma)
+        cb.update(cpu_info())
+        if extras:
+            print("[bench] timing the CPU oracle single-threaded (tiny, decode_8x7b)",
+                  file=sys.stderr, flush=True)
+            cb["single_thread"] = cpu_single_thread(("tiny", "decode_8x7b"))
+        line["cpu_baseline"] = cb
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

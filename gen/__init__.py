@@ -42,6 +42,16 @@ CONFIGS = {
                       bias=[3.0, 1.0, 0.0, 0.0, 0.0, 0.0, -1.0, -2.0]),
     # Mixtral-8x22B shape
     "prefill_8x22b": dict(T=2048, d=6144, ffn=16384, E=8, k=2, dtype=BF16, seed=4, bias=None),
+    # Mixtral-8x7B widths with other routing settings (MixtralConfig num_experts_per_tok and
+    # num_local_experts): one expert per token, and 16 or 32 experts with two per token,
+    # each at a decode batch (32 tokens) and a prefill batch (4096 tokens). A decode
+    # batch's x is the first 32 rows of the prefill batch's (same seed, same weights).
+    "decode_8x7b_k1": dict(T=32, d=4096, ffn=14336, E=8, k=1, dtype=BF16, seed=5, bias=None),
+    "prefill_8x7b_k1": dict(T=4096, d=4096, ffn=14336, E=8, k=1, dtype=BF16, seed=5, bias=None),
+    "decode_e16": dict(T=32, d=4096, ffn=14336, E=16, k=2, dtype=BF16, seed=6, bias=None),
+    "prefill_e16": dict(T=4096, d=4096, ffn=14336, E=16, k=2, dtype=BF16, seed=6, bias=None),
+    "decode_e32": dict(T=32, d=4096, ffn=14336, E=32, k=2, dtype=BF16, seed=7, bias=None),
+    "prefill_e32": dict(T=4096, d=4096, ffn=14336, E=32, k=2, dtype=BF16, seed=7, bias=None),
 }
 
 

@@ -56,3 +56,27 @@ def test_committed_traffic_record_is_current():
         pytest.skip("gate/up kernel sources changed since the counters were taken")
     ent = rec["workloads"]["decode_8x7b"]
     assert ent["hbm_bytes_per_launch"] == ent["fetch_bytes"] + ent["write_bytes"]
+
+
+def test_routing_workload_pairs_share_their_inputs():
+    """Each (decode, prefill) pair of the routing-setting workloads differs only
+    in T, so one draw serves both: the decode batch's x is the first rows of
+    the prefill batch's (the generator fills x row by row), weights equal."""
+    import numpy as np
+
+    import gen
+    for dname, pname in bench.ROUTING_WORKLOADS:
+        dc, pc = dict(gen.CONFIGS[dname]), dict(gen.CONFIGS[pname])
+        assert dc.pop("T") < pc.pop("T")
+        assert dc == pc
+    small = dict(d=64, ffn=64, E=4, k=1, dtype=gen.BF16, seed=5)
+    a, b = gen.make_inputs(T=32, **small), gen.make_inputs(T=96, **small)
+    assert np.array_equal(a["x"], b["x"][:32])
+    assert all(np.array_equal(a[n], b[n]) for n in ("router", "w1", "w3", "w2"))
+
+
+def test_down_work():
+    cfg = dict(T=4096, d=4096, ffn=14336, E=8, k=2, dtype="bf16")
+    b, f = bench.down_work(cfg, [1024] * 8)
+    assert f == 2 * 8192 * 14336 * 4096
+    assert b == 8 * 4096 * 14336 * 2 + 8192 * 14336 * 2 + 8192 * 4096 * 4
