@@ -118,7 +118,7 @@ inline void stage(const Opts& o, int i, hipStream_t s) {
 int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
             const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d, int ffn, int E,
             int k, float* part, void* h, void* wide, hipStream_t s, const Opts& opt,
-            bool with_events, int* nsplit_out) {
+            bool with_events, int* nsplit_out, const moe::FusedPermute* fp = nullptr) {
   const int64_t A = T * k;
   hipError_t err;
   if (dtype == MOE_INT8_PACKED) {
@@ -163,7 +163,7 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
     err = moe::launch_gate_up_bf16(variant, packed, static_cast<const uint16_t*>(x),
                                    static_cast<const uint16_t*>(w1),
                                    static_cast<const uint16_t*>(w3), offsets, sorted_asg, A, d,
-                                   ffn, E, k, static_cast<uint16_t*>(h), s);
+                                   ffn, E, k, static_cast<uint16_t*>(h), s, fp);
     if (err != hipSuccess) return MOE_EHIP;
     if (with_events) stage(opt, 3, s);
     err = moe::launch_down_bf16(dvariant, packed, static_cast<const uint16_t*>(h),
@@ -315,12 +315,20 @@ int forward_impl(const void* x, int dtype, const float* gamma, float eps, void* 
   float* y = reinterpret_cast<float*>(base + L.y);
   const void* xin = gamma ? norm_out : x;  // what the experts read
 
+  // few assignments on the bf16 streaming kernels: the gate/up kernel does the
+  // permutation itself (one launch less; the same arrays, bit for bit)
+  const int64_t A = T * k;
+  const bool fuse = T > 0 && (dtype == MOE_BF16 || dtype == MOE_BF16_PACKED) &&
+                    moe::gate_up_fuses_permute(moe::choose_ffn_variant(opt.variant, A, E), A);
+  const moe::FusedPermute fp{idx, counts, offsets, sorted_asg, asg_pos};
+
   stage(opt, 0, s);
   if (T > 0 && moe::launch_route(x, is_bf16(dtype), router, logit_bias, T, d, E, k, nullptr,
                                  idx, w, s, gamma, eps, norm_out) != hipSuccess)
     return MOE_EHIP;
   stage(opt, 1, s);
-  if (moe::launch_permute(idx, T * k, E, counts, offsets, sorted_asg, asg_pos, s) != hipSuccess)
+  if (!fuse &&
+      moe::launch_permute(idx, A, E, counts, offsets, sorted_asg, asg_pos, s) != hipSuccess)
     return MOE_EHIP;
   stage(opt, 2, s);
   if (T == 0) {
@@ -329,7 +337,7 @@ int forward_impl(const void* x, int dtype, const float* gamma, float eps, void* 
   }
   int nsplit = 1;
   st = run_ffn(xin, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, h, base + L.wide,
-               s, opt, true, &nsplit);
+               s, opt, true, &nsplit, fuse ? &fp : nullptr);
   if (st != MOE_OK) return st;
   stage(opt, 4, s);
   if (moe::launch_combine(y, nsplit, asg_pos, w, T, d, k, out, out_dtype == MOE_BF16, s,

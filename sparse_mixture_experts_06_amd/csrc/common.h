@@ -119,16 +119,32 @@ hipError_t launch_permute(const int32_t* idx, int64_t A, int E, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_asg, int32_t* asg_pos,
                           hipStream_t s);
 
+// The permutation done by the streaming gate/up kernel itself (few
+// assignments): the expert ids and the arrays moe_permute would write.
+struct FusedPermute {
+  const int32_t* idx;  // [A] expert ids (topk_idx)
+  int32_t* counts;     // [E]
+  int32_t* offsets;    // [E + 1]
+  int32_t* sorted_asg; // [A]
+  int32_t* asg_pos;    // [A]
+};
+constexpr int kFusedPermuteMaxA = 512;
+// whether the bf16 gate/up kernel of this resolved family takes the
+// permutation over for A assignments
+bool gate_up_fuses_permute(int variant, int64_t A);
 // bf16 experts: gate/up (+SiLU*mul) -> h [A, ffn] bf16, down -> y [A, d] f32.
 // `variant` is resolved (1 streaming, 2 tiled); `packed` selects the
 // fragment-order weight layout. The down kernel writes
 // down_splits(variant, A, d, ffn, E) float32 partial results [nsplit, A, d]
 // whose sum (in split order) is y; the count depends on the sizes only, not
 // on the layout, so both layouts give bit-identical y.
+// fp non-null (only where gate_up_fuses_permute): offsets and sorted_asg
+// are not read, the kernel writes fp's arrays
 hipError_t launch_gate_up_bf16(int variant, bool packed, const uint16_t* x, const uint16_t* w1,
                                const uint16_t* w3, const int32_t* offsets,
                                const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
-                               int k, uint16_t* h, hipStream_t s);
+                               int k, uint16_t* h, hipStream_t s,
+                               const FusedPermute* fp = nullptr);
 hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const uint16_t* w2,
                             const int32_t* offsets, int64_t A, int d, int ffn, int E, float* part,
                             hipStream_t s);

@@ -90,22 +90,105 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 // ----------------------------------------------------------------------------
 constexpr int kStreamWaves = 4;
 
+// The grouping of the assignments by expert, from the expert ids alone, for
+// few assignments (A <= kFusedPermuteMaxA): the same stable counting sort as
+// permute.hip (assignments of an expert in increasing id order; ids outside
+// [0, E) ignored), by wave ballots over the ids in steps of 64.
+// count_expert: the first grouped row `beg` of expert e (assignments of lower
+// experts) and its count M.
+__device__ __forceinline__ void count_expert(const int32_t* __restrict__ idx, int A, int e,
+                                             int lane, int& beg, int& M) {
+  beg = 0;
+  M = 0;
+  for (int a0 = 0; a0 < A; a0 += kWave) {
+    const int a = a0 + lane;
+    const int ea = a < A ? idx[a] : -1;
+    beg += __popcll(__ballot(ea >= 0 && ea < e));
+    M += __popcll(__ballot(ea == e));
+  }
+}
+
+// rank_expert: row(rank, a) for each assignment a of expert e, rank = its
+// position among the expert's assignments
+template <typename F>
+__device__ __forceinline__ void rank_expert(const int32_t* __restrict__ idx, int A, int e, int lane,
+                                            F&& row) {
+  const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  int M = 0;
+  for (int a0 = 0; a0 < A; a0 += kWave) {
+    const int a = a0 + lane;
+    const int ea = a < A ? idx[a] : -1;
+    const uint64_t eq = __ballot(ea == e);
+    if (ea == e) row(M + __popcll(eq & lower), a);
+    M += __popcll(eq);
+  }
+}
+
+// Start of a streaming gate/up workgroup that does the permutation itself:
+// the waves of workgroup (0, 0) write counts, offsets, sorted_asg and
+// asg_pos for the kernels that follow; in every workgroup wave 0 puts the
+// token rows of expert e, in grouped order, into s_rows. Returns the expert's
+// first grouped row and its row count (every wave; one barrier).
+__device__ __forceinline__ void fused_permute(const FusedPermute& fp, int A, int E, int e,
+                                              int ktop, int lane, int wave, int* s_rows,
+                                              int* s_begm, int& beg, int& M) {
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int ee = wave; ee < E; ee += kStreamWaves) {
+      int b, m;
+      count_expert(fp.idx, A, ee, lane, b, m);
+      rank_expert(fp.idx, A, ee, lane, [&](int rank, int a) {
+        fp.sorted_asg[b + rank] = a;
+        fp.asg_pos[a] = b + rank;
+      });
+      if (lane == 0) {
+        fp.counts[ee] = m;
+        fp.offsets[ee] = b;
+        if (ee == E - 1) fp.offsets[E] = b + m;
+      }
+    }
+  }
+  if (wave == 0) {
+    int b, m;
+    count_expert(fp.idx, A, e, lane, b, m);
+    rank_expert(fp.idx, A, e, lane, [&](int rank, int a) { s_rows[rank] = a / ktop; });
+    if (lane == 0) {
+      s_begm[0] = b;
+      s_begm[1] = m;
+    }
+  }
+  __syncthreads();
+  beg = s_begm[0];
+  M = s_begm[1];
+}
+
 // x [T, K=d] rows gathered through sorted_asg / ktop; w1, w3 [E, N=ffn, K];
 // h bf16 [A, N]. Token rows go 32 at a time (two 16-row MFMA column tiles;
 // the second is skipped when the rows run out).
-template <int RT, int U, bool PACKED, bool NT>
+// FUSED: the permutation is done here instead of by a kernel of its own (few
+// assignments: the expert ids fp.idx [A] of E experts), by fused_permute;
+// offsets and sorted_asg are not read then.
+template <int RT, int U, bool PACKED, bool NT, bool FUSED>
 __global__ __launch_bounds__(kWave* kStreamWaves) void gate_up_stream_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
     const uint16_t* __restrict__ w3, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_asg, int K, int N, int ktop, uint16_t* __restrict__ h) {
+    const int32_t* __restrict__ sorted_asg, int K, int N, int ktop, uint16_t* __restrict__ h,
+    FusedPermute fp, int A, int E) {
   const int e = blockIdx.y;
   const int n0 = blockIdx.x * (16 * RT);
-  const int beg = offsets[e];
-  const int M = offsets[e + 1] - beg;
-  if (M <= 0) return;
-
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
+  __shared__ int s_rows[FUSED ? kFusedPermuteMaxA : 1];
+  __shared__ int s_begm[2];
+  int beg, M;
+  if constexpr (FUSED) {
+    fused_permute(fp, A, E, e, ktop, lane, wave, s_rows, s_begm, beg, M);
+  } else {
+    beg = offsets[e];
+    M = offsets[e + 1] - beg;
+  }
+  if (M <= 0) return;
+  // token row of the expert's m-th assignment
+  auto token = [&](int m) { return FUSED ? s_rows[m] : sorted_asg[beg + m] / ktop; };
   const int r = lane & 15;
   const int g = lane >> 4;
   const int S = K / 32;
@@ -127,8 +210,8 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void gate_up_stream_kernel(
     const bool two = (M - mb) > 16;  // wave-uniform
     const int m0 = min(mb + r, M - 1);
     const int m1 = min(mb + 16 + r, M - 1);
-    const uint16_t* px0 = x + static_cast<int64_t>(sorted_asg[beg + m0] / ktop) * K + g * 8;
-    const uint16_t* px1 = x + static_cast<int64_t>(sorted_asg[beg + m1] / ktop) * K + g * 8;
+    const uint16_t* px0 = x + static_cast<int64_t>(token(m0)) * K + g * 8;
+    const uint16_t* px1 = x + static_cast<int64_t>(token(m1)) * K + g * 8;
 
     f32x4 ag[RT][2], au[RT][2];
 #pragma unroll
@@ -294,6 +377,271 @@ __global__ __launch_bounds__(kWave* kStreamWaves) void down_stream_kernel(
       if (m < M) {
 #pragma unroll
         for (int t = 0; t < RT; ++t)
+          *reinterpret_cast<f32x4*>(dst + static_cast<size_t>(beg + m) * N + n0 + t * 16 + 4 * g) =
+              acc[t][c];
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// streaming kernels for standard-layout weights, whole cache lines per load
+// ----------------------------------------------------------------------------
+// A weight fragment (16 rows x 32 k) read straight from the standard layout
+// is 16 half cache lines (64 B of each row), and the other halves come with
+// the next k step's load: measured on MI355X, that access streams at 6.2 TB/s
+// with or without the non-temporal hint, while loads of whole 128-byte lines
+// (8 rows x 128 B per wave load) reach 7.0 TB/s with it. These kernels load
+// whole lines and rearrange them through a small LDS buffer of each wave:
+// one 64-wide k block of 16 rows is two wave loads; lane l of the load for
+// rows 8q .. 8q+7 takes row 8q + l/8 and 16-byte chunk (l % 8) ^ ((row / 2)
+// % 8) of the block, and writes it to slot l of a 1 KiB LDS area (lane
+// order); the MFMA operand of k step s (chunk 4s + g of row r for lane
+// 16g + r) is then read from slot 8 (r % 8) + ((4s + g) ^ ((r / 2) % 8)) of
+// area q = r / 8: the swizzle puts the 16 rows of a fragment read on 16
+// different bank groups. The operands, and the MFMAs and their order, are
+// those of the kernels above on fragment-order weights, so both layouts give
+// the same bits. A wave's k range must be whole 64-wide blocks.
+constexpr int kRmBlocks = 4;  // 64-wide k blocks in flight per wave (8 k steps)
+
+// this lane's element offsets, within a 16-row tile, of its two line loads
+// (rows 0-7 and 8-15) of k block 0
+__device__ __forceinline__ void rm_load_offsets(int lane, int K, int (&off)[2]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 8 * q + (lane >> 3);
+    off[q] = row * K + (((lane & 7) ^ ((row >> 1) & 7)) << 3);
+  }
+}
+
+// byte offset in a wave's LDS buffer of this lane's operand for k step s of
+// 16-row tile t (areas 2t and 2t + 1 hold its rows 0-7 and 8-15)
+__device__ __forceinline__ int rm_read_offset(int lane, int t, int s) {
+  const int r = lane & 15, g = lane >> 4;
+  return ((2 * t + (r >> 3)) * 64 + 8 * (r & 7) + ((4 * s + g) ^ ((r >> 1) & 7))) * 16;
+}
+
+// gate/up as gate_up_stream_kernel (RT = 1: 16 rows of w1 and of w3 per
+// workgroup, 4 waves splitting K = d; FUSED as there), standard-layout
+// weights loaded in whole lines.
+template <bool FUSED>
+__global__ __launch_bounds__(kWave* kStreamWaves) void gate_up_stream_rm_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
+    const uint16_t* __restrict__ w3, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_asg, int K, int N, int ktop, uint16_t* __restrict__ h,
+    FusedPermute fp, int A, int E) {
+  const int e = blockIdx.y;
+  const int n0 = blockIdx.x * 16;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  __shared__ int s_rows[FUSED ? kFusedPermuteMaxA : 1];
+  __shared__ int s_begm[2];
+  __shared__ __attribute__((aligned(16))) uint8_t stg[kStreamWaves][4096];
+  __shared__ f32x4 red[kStreamWaves - 1][2][2][kWave];
+  int beg, M;
+  if constexpr (FUSED) {
+    fused_permute(fp, A, E, e, ktop, lane, wave, s_rows, s_begm, beg, M);
+  } else {
+    beg = offsets[e];
+    M = offsets[e + 1] - beg;
+  }
+  if (M <= 0) return;
+  auto token = [&](int m) { return FUSED ? s_rows[m] : sorted_asg[beg + m] / ktop; };
+
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int S = K / 32;
+  const int b_lo = (wave * S) / kStreamWaves / 2;  // 64-wide k blocks of this wave
+  const int b_hi = ((wave + 1) * S) / kStreamWaves / 2;
+  int off[2];
+  rm_load_offsets(lane, K, off);
+  const uint16_t* pg = w1 + (static_cast<size_t>(e) * N + n0) * K;
+  const uint16_t* pu = w3 + (static_cast<size_t>(e) * N + n0) * K;
+  uint8_t* buf = stg[wave];
+  const int rd0 = rm_read_offset(lane, 0, 0), rd1 = rm_read_offset(lane, 0, 1);
+
+  for (int mb = 0; mb < M; mb += 32) {
+    const bool two = (M - mb) > 16;  // wave-uniform
+    const int m0 = min(mb + r, M - 1);
+    const int m1 = min(mb + 16 + r, M - 1);
+    const uint16_t* px0 = x + static_cast<int64_t>(token(m0)) * K + g * 8;
+    const uint16_t* px1 = x + static_cast<int64_t>(token(m1)) * K + g * 8;
+    f32x4 ag[2], au[2];
+    ag[0] = ag[1] = au[0] = au[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // one 64-wide k block: the line loads (issued by the caller) into LDS,
+    // its four operands back, and the MFMAs of its two k steps
+    auto consume = [&](const u32x4 (&W)[4], const u32x4 (&B0)[2], const u32x4 (&B1)[2]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // areas: w1 rows 0-7, 8-15, w3 rows 0-7, 8-15
+        *reinterpret_cast<u32x4*>(buf + (i * 64 + lane) * 16) = W[i];
+      const u32x4 G0 = *reinterpret_cast<const u32x4*>(buf + rd0);
+      const u32x4 G1 = *reinterpret_cast<const u32x4*>(buf + rd1);
+      const u32x4 V0 = *reinterpret_cast<const u32x4*>(buf + 2048 + rd0);
+      const u32x4 V1 = *reinterpret_cast<const u32x4*>(buf + 2048 + rd1);
+      ag[0] = mfma16x16x32(G0, B0[0], ag[0]);
+      au[0] = mfma16x16x32(V0, B0[0], au[0]);
+      if (two) {
+        ag[1] = mfma16x16x32(G0, B1[0], ag[1]);
+        au[1] = mfma16x16x32(V0, B1[0], au[1]);
+      }
+      ag[0] = mfma16x16x32(G1, B0[1], ag[0]);
+      au[0] = mfma16x16x32(V1, B0[1], au[0]);
+      if (two) {
+        ag[1] = mfma16x16x32(G1, B1[1], ag[1]);
+        au[1] = mfma16x16x32(V1, B1[1], au[1]);
+      }
+    };
+    auto load = [&](int b, u32x4 (&W)[4], u32x4 (&B0)[2], u32x4 (&B1)[2]) {
+      W[0] = ldw<true>(pg + off[0] + b * 64);
+      W[1] = ldw<true>(pg + off[1] + b * 64);
+      W[2] = ldw<true>(pu + off[0] + b * 64);
+      W[3] = ldw<true>(pu + off[1] + b * 64);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        B0[s2] = ldg16(px0 + (2 * b + s2) * 32);
+        B1[s2] = two ? ldg16(px1 + (2 * b + s2) * 32) : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    int b = b_lo;
+    for (; b + kRmBlocks <= b_hi; b += kRmBlocks) {
+      u32x4 W[kRmBlocks][4], B0[kRmBlocks][2], B1[kRmBlocks][2];
+#pragma unroll
+      for (int u = 0; u < kRmBlocks; ++u) load(b + u, W[u], B0[u], B1[u]);
+#pragma unroll
+      for (int u = 0; u < kRmBlocks; ++u) consume(W[u], B0[u], B1[u]);
+    }
+    for (; b < b_hi; ++b) {
+      u32x4 W[4], B0[2], B1[2];
+      load(b, W, B0, B1);
+      consume(W, B0, B1);
+    }
+
+    if (wave > 0) {
+      red[wave - 1][0][0][lane] = ag[0];
+      red[wave - 1][1][0][lane] = au[0];
+      if (two) {
+        red[wave - 1][0][1][lane] = ag[1];
+        red[wave - 1][1][1][lane] = au[1];
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < kStreamWaves - 1; ++w) {
+        ag[0] += red[w][0][0][lane];
+        au[0] += red[w][1][0][lane];
+        if (two) {
+          ag[1] += red[w][0][1][lane];
+          au[1] += red[w][1][1][lane];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int m = mb + c * 16 + r;
+        if (m < M) {
+          const f32x4 gt = ag[c];
+          const f32x4 up = au[c];
+          uint2 v;
+          v.x = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
+          v.y = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
+          *reinterpret_cast<uint2*>(h + static_cast<size_t>(beg + m) * N + n0 + 4 * g) = v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// down as down_stream_kernel (RT = 2: 32 rows of w2 per wave, each wave its
+// own task over 1/nsplit of K = ffn), standard-layout weights loaded in whole
+// lines.
+__global__ __launch_bounds__(kWave* kStreamWaves) void down_stream_rm_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w2,
+    const int32_t* __restrict__ offsets, int K, int N, int A, int nsplit,
+    float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t stg[kStreamWaves][4096];
+  const int e = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = static_cast<int>(threadIdx.x) / kWave;
+  const int task = blockIdx.x * kStreamWaves + wave;
+  const int ngroups = N / 32;
+  if (task >= ngroups * nsplit) return;
+  const int sp = task % nsplit;
+  const int n0 = (task / nsplit) * 32;
+  const int beg = offsets[e];
+  const int M = offsets[e + 1] - beg;
+  if (M <= 0) return;
+
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int S = K / 32;
+  const int b_lo = (sp * S) / nsplit / 2;
+  const int b_hi = ((sp + 1) * S) / nsplit / 2;
+  int off[2];
+  rm_load_offsets(lane, K, off);
+  const uint16_t* pw = w2 + (static_cast<size_t>(e) * N + n0) * K;
+  const size_t tile1 = static_cast<size_t>(16) * K;  // rows 16-31
+  uint8_t* buf = stg[wave];
+  int rd[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) rd[t][s2] = rm_read_offset(lane, t, s2);
+  float* dst = part + static_cast<size_t>(sp) * A * N;
+
+  for (int mb = 0; mb < M; mb += 32) {
+    const bool two = (M - mb) > 16;
+    const uint16_t* px0 = h + static_cast<int64_t>(beg + min(mb + r, M - 1)) * K + g * 8;
+    const uint16_t* px1 = h + static_cast<int64_t>(beg + min(mb + 16 + r, M - 1)) * K + g * 8;
+    f32x4 acc[2][2];
+    acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto consume = [&](const u32x4 (&W)[4], const u32x4 (&B0)[2], const u32x4 (&B1)[2]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // areas: rows 0-7, 8-15, 16-23, 24-31
+        *reinterpret_cast<u32x4*>(buf + (i * 64 + lane) * 16) = W[i];
+      u32x4 F[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) F[t][s2] = *reinterpret_cast<const u32x4*>(buf + rd[t][s2]);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          acc[t][0] = mfma16x16x32(F[t][s2], B0[s2], acc[t][0]);
+          if (two) acc[t][1] = mfma16x16x32(F[t][s2], B1[s2], acc[t][1]);
+        }
+    };
+    auto load = [&](int b, u32x4 (&W)[4], u32x4 (&B0)[2], u32x4 (&B1)[2]) {
+      W[0] = ldw<true>(pw + off[0] + b * 64);
+      W[1] = ldw<true>(pw + off[1] + b * 64);
+      W[2] = ldw<true>(pw + tile1 + off[0] + b * 64);
+      W[3] = ldw<true>(pw + tile1 + off[1] + b * 64);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        B0[s2] = ldg16(px0 + (2 * b + s2) * 32);
+        B1[s2] = two ? ldg16(px1 + (2 * b + s2) * 32) : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    int b = b_lo;
+    for (; b + kRmBlocks <= b_hi; b += kRmBlocks) {
+      u32x4 W[kRmBlocks][4], B0[kRmBlocks][2], B1[kRmBlocks][2];
+#pragma unroll
+      for (int u = 0; u < kRmBlocks; ++u) load(b + u, W[u], B0[u], B1[u]);
+#pragma unroll
+      for (int u = 0; u < kRmBlocks; ++u) consume(W[u], B0[u], B1[u]);
+    }
+    for (; b < b_hi; ++b) {
+      u32x4 W[4], B0[2], B1[2];
+      load(b, W, B0, B1);
+      consume(W, B0, B1);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int m = mb + c * 16 + r;
+      if (m < M) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
           *reinterpret_cast<f32x4*>(dst + static_cast<size_t>(beg + m) * N + n0 + t * 16 + 4 * g) =
               acc[t][c];
       }
@@ -803,20 +1151,48 @@ inline unsigned tiled_grid(int64_t A, int E, int ntn, int nsplit = 1) {
   return static_cast<unsigned>((tiles + 7) / 8 * 8);
 }
 
+template <bool PACKED, int RT, bool FUSED>
+void launch_gate_up_stream(const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
+                           const int32_t* offsets, const int32_t* sorted_asg, int64_t A, int d,
+                           int ffn, int E, int k, uint16_t* h, const FusedPermute& fp,
+                           hipStream_t s) {
+  hipLaunchKernelGGL((gate_up_stream_kernel<RT, kGateUpU, PACKED, kStreamNT<PACKED>, FUSED>),
+                     dim3(ffn / (16 * RT), E), dim3(kWave * kStreamWaves), 0, s, x, w1, w3,
+                     offsets, sorted_asg, d, ffn, k, h, fp, static_cast<int>(A), E);
+}
+
 template <bool PACKED>
 hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
                         const int32_t* offsets, const int32_t* sorted_asg, int64_t A, int d,
-                        int ffn, int E, int k, uint16_t* h, hipStream_t s) {
+                        int ffn, int E, int k, uint16_t* h, hipStream_t s,
+                        const FusedPermute* fp) {
   if (variant == 1) {
     constexpr int rows = 16 * kGateUpRT;
-    if (ffn % rows != 0)
-      hipLaunchKernelGGL((gate_up_stream_kernel<1, kGateUpU, PACKED, kStreamNT<PACKED>>), dim3(ffn / 16, E),
-                         dim3(kWave * kStreamWaves), 0, s, x, w1, w3, offsets, sorted_asg, d, ffn,
-                         k, h);
-    else
-      hipLaunchKernelGGL((gate_up_stream_kernel<kGateUpRT, kGateUpU, PACKED, kStreamNT<PACKED>>),
-                         dim3(ffn / rows, E), dim3(kWave * kStreamWaves), 0, s, x, w1, w3,
-                         offsets, sorted_asg, d, ffn, k, h);
+    const FusedPermute none{};
+    if (!PACKED && d % 256 == 0) {  // whole-line loads: each wave's k range whole 64-blocks
+      const bool fused = fp && A <= kFusedPermuteMaxA;
+      if (fused)
+        hipLaunchKernelGGL(gate_up_stream_rm_kernel<true>, dim3(ffn / 16, E),
+                           dim3(kWave * kStreamWaves), 0, s, x, w1, w3, offsets, sorted_asg, d,
+                           ffn, k, h, *fp, static_cast<int>(A), E);
+      else
+        hipLaunchKernelGGL(gate_up_stream_rm_kernel<false>, dim3(ffn / 16, E),
+                           dim3(kWave * kStreamWaves), 0, s, x, w1, w3, offsets, sorted_asg, d,
+                           ffn, k, h, none, static_cast<int>(A), E);
+    } else if (fp && A <= kFusedPermuteMaxA) {
+      if (ffn % rows != 0)
+        launch_gate_up_stream<PACKED, 1, true>(x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h,
+                                               *fp, s);
+      else
+        launch_gate_up_stream<PACKED, kGateUpRT, true>(x, w1, w3, offsets, sorted_asg, A, d, ffn,
+                                                       E, k, h, *fp, s);
+    } else if (ffn % rows != 0) {
+      launch_gate_up_stream<PACKED, 1, false>(x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h,
+                                              none, s);
+    } else {
+      launch_gate_up_stream<PACKED, kGateUpRT, false>(x, w1, w3, offsets, sorted_asg, A, d, ffn,
+                                                      E, k, h, none, s);
+    }
   } else if (dma_gate_up_ok(A, k, d, ffn, E)) {
     return launch_gate_up_dma(PACKED, x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s);
   } else if (PACKED && ffn % 128 == 0) {
@@ -841,7 +1217,13 @@ hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const i
   const int nsplit = down_splits(variant, A, d, ffn, E);
   if (variant == 1) {
     constexpr int rows = 16 * kDownRT;
-    if (d % rows != 0) {
+    if (!PACKED && d % 32 == 0 && (ffn / 32) % (2 * nsplit) == 0) {
+      // whole-line loads: each wave's k range whole 64-blocks
+      const unsigned blocks =
+          static_cast<unsigned>((d / 32 * nsplit + kStreamWaves - 1) / kStreamWaves);
+      hipLaunchKernelGGL(down_stream_rm_kernel, dim3(blocks, E), dim3(kWave * kStreamWaves), 0, s,
+                         h, w2, offsets, ffn, d, static_cast<int>(A), nsplit, part);
+    } else if (d % rows != 0) {
       const unsigned blocks =
           static_cast<unsigned>((d / 16 * nsplit + kStreamWaves - 1) / kStreamWaves);
       hipLaunchKernelGGL((down_stream_kernel<1, kDownU, PACKED, kStreamNT<PACKED>>), dim3(blocks, E),
@@ -943,10 +1325,15 @@ hipError_t launch_pack_bf16(const uint16_t* w, int E, int R, int C, uint16_t* ou
 hipError_t launch_gate_up_bf16(int variant, bool packed, const uint16_t* x, const uint16_t* w1,
                                const uint16_t* w3, const int32_t* offsets,
                                const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
-                               int k, uint16_t* h, hipStream_t s) {
+                               int k, uint16_t* h, hipStream_t s, const FusedPermute* fp) {
   if (A == 0) return hipSuccess;
-  return packed ? gate_up_impl<true>(variant, x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s)
-                : gate_up_impl<false>(variant, x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s);
+  if (fp && !gate_up_fuses_permute(variant, A)) return hipErrorInvalidValue;
+  return packed ? gate_up_impl<true>(variant, x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s, fp)
+                : gate_up_impl<false>(variant, x, w1, w3, offsets, sorted_asg, A, d, ffn, E, k, h, s, fp);
+}
+
+bool gate_up_fuses_permute(int variant, int64_t A) {
+  return variant == 1 && A > 0 && A <= kFusedPermuteMaxA;
 }
 
 hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const uint16_t* w2,

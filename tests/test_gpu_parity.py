@@ -52,6 +52,11 @@ SMALL = [
     ("bf16_E16_k4", dict(T=200, d=128, ffn=128, E=16, k=4, dtype=gen.BF16, seed=27)),
     ("bf16_E32_k1", dict(T=64, d=64, ffn=128, E=32, k=1, dtype=gen.BF16, seed=28)),
     ("bf16_k_eq_E", dict(T=50, d=64, ffn=64, E=4, k=4, dtype=gen.BF16, seed=29)),
+    # d % 256 == 0 and few assignments: standard-layout weights take the
+    # whole-line streaming kernels, and moe_forward's gate/up kernel does the
+    # permutation itself (A <= 512)
+    ("bf16_lines_fused", dict(T=100, d=256, ffn=256, E=8, k=2, dtype=gen.BF16, seed=34)),
+    ("bf16_lines_e4", dict(T=5, d=512, ffn=384, E=4, k=2, dtype=gen.BF16, seed=35)),
     ("f32_odd", dict(T=37, d=70, ffn=50, E=8, k=2, dtype=gen.F32, seed=30)),
     ("f32_E1", dict(T=20, d=32, ffn=48, E=1, k=1, dtype=gen.F32, seed=31)),
 ]
@@ -289,14 +294,21 @@ def test_prefill_tiles_many_experts(m, E, k):
 
 @pytest.mark.parametrize("T,E,k,dtype,d", [(256, 8, 2, gen.BF16, 512), (257, 8, 2, gen.BF16, 512),
                                            (256, 32, 4, gen.F32, 512), (257, 32, 4, gen.BF16, 512),
-                                           (263, 8, 2, gen.F32, 70), (257, 32, 4, gen.F32, 70)])
+                                           (263, 8, 2, gen.F32, 70), (257, 32, 4, gen.F32, 70),
+                                           (1000, 8, 2, gen.BF16, 2048),
+                                           (257, 16, 2, gen.BF16, 2048),
+                                           (1000, 32, 4, gen.BF16, 2048),
+                                           (300, 32, 1, gen.BF16, 4096)])
 def test_router_work_splits(m, T, E, k, dtype, d):
     """The router on either side of its switch between one token per
     workgroup (up to 256 tokens) and 64 / EM tokens per workgroup (beyond),
     for the 8- and 32-expert bounds: logits within LOGIT_TOL of the oracle's,
     routing and weights by the certified rule. d = 70 (not a multiple of 8)
     takes the scalar loads, here with several tokens per workgroup and a last
-    workgroup holding fewer tokens than its slots (263 = 32 * 8 + 7)."""
+    workgroup holding fewer tokens than its slots (263 = 32 * 8 + 7). bf16
+    batches above 256 tokens with d a multiple of 2048 take the fp32-MFMA
+    router (16 tokens per workgroup, one or two 16-expert tiles; 1000 and
+    257 tokens leave a part-filled last workgroup)."""
     inp = gen.make_inputs(T=T, d=d, ffn=64, E=E, k=k, dtype=dtype, seed=80 + T + E)
     print(f"[parity] router T={T} E={E} k={k} d={d} {dtype}", flush=True)
     dev = to_device(inp)
