@@ -203,6 +203,29 @@ int moe_block_forward(const void* hidden, int dtype, const float* norm_weight, f
                       float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                       void* stream, const moe_options* options);
 
+/* moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The library calls no hipMalloc, hipFree
+ * or allocating routine: the workspace is a scratch array built into the
+ * library, MOE_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on, held from
+ * its first use there until the process ends. Arguments, results and options
+ * are those of moe_forward (the same kernels, bit-identical output); sizes
+ * whose moe_workspace_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES are refused with
+ * MOE_EWORKSPACE before anything is enqueued (with bf16 or int8 weights at
+ * k = 2 that admits batches of up to 545 tokens at the Mixtral-8x7B shape,
+ * 409 at the 8x22B shape). Every call on a GPU
+ * uses that GPU's one array and nothing in it needs to start at a particular
+ * value, so calls that overlap on one GPU (concurrent streams, or threads
+ * without ordering between their streams) race and give wrong results: order
+ * them. The scratch of the current device is used; MOE_EHIP if its address
+ * cannot be obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const void* x, int dtype, const float* router, const float* logit_bias,
+                        const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
+                        int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
+                        float* topk_w_out, int32_t* counts_out, void* stream,
+                        const moe_options* options);
+
 /* One-time weight preparation for the MOE_BF16_PACKED path: copies the
  * bfloat16 matrices w [E, rows, cols] (standard layout, cols contiguous) into
  * `out` (same size, E*rows*cols*2 bytes, must not overlap w) in fragment

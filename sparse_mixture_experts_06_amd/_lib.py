@@ -22,6 +22,7 @@ MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16, MOE_BF16_PACKED, MOE_INT8_PACKED = 0, 1, 2, 3
 MOE_MAX_EXPERTS = 32
 MOE_MAX_ASSIGNMENTS = 2 ** 31 - 1024
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
@@ -48,6 +49,9 @@ _SIGNATURES = {
     "moe_forward": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _c_int,
                              _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _c_sz, _vp,
                              _opts_p]),
+    "moe_forward_noalloc": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_int,
+                                     _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp,
+                                     _opts_p]),
     "moe_block_forward": (_c_int, [_vp, _c_int, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _vp, _c_int,
                                    _vp, _vp, _vp, _vp, _c_sz, _vp, _opts_p]),
@@ -424,3 +428,37 @@ def moe_block_forward(hidden, norm_weight, router, w1, w3, w2, k: int, eps: floa
                                   _options(variant, events))
     _check("moe_block_forward", st)
     return out, norm_out
+
+
+def moe_forward_noalloc(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dtype=None,
+                        topk_idx_out=None, topk_w_out=None, counts_out=None, packed=False,
+                        variant: int = 0, events=None):
+    """moe_forward on the library's built-in scratch instead of a workspace (the
+    C call allocates nothing; this wrapper allocates `out` only when it is not
+    passed). Sizes needing more than MOE_NOALLOC_SCRATCH_BYTES raise MoeError
+    (MOE_EWORKSPACE). Calls that overlap on one GPU race (one shared scratch)."""
+    T, d = x.shape
+    E, ffn, _ = w1.shape
+    dev = x.device
+    code = _weight_code(x.dtype, packed, w1, w3, w2)
+    _need(router, "router", torch.float32, (E, d), dev)
+    for name, t, shp in (("w1", w1, (E, ffn, d)), ("w3", w3, (E, ffn, d)), ("w2", w2, (E, d, ffn))):
+        _need(t, name, x.dtype, shp, dev, code)
+    if logit_bias is not None:
+        _need(logit_bias, "logit_bias", torch.float32, (E,), dev)
+    if out is None:
+        out = torch.empty(T, d, dtype=out_dtype or x.dtype, device=dev)
+    _need(out, "out", out.dtype, (T, d), dev)
+    if topk_idx_out is not None:
+        _need(topk_idx_out, "topk_idx_out", torch.int32, (T, k), dev)
+    if topk_w_out is not None:
+        _need(topk_w_out, "topk_w_out", torch.float32, (T, k), dev)
+    if counts_out is not None:
+        _need(counts_out, "counts_out", torch.int32, (E,), dev)
+    st = load().moe_forward_noalloc(_ptr(x), code, _ptr(router), _ptr(logit_bias), _ptr(w1),
+                                    _ptr(w3), _ptr(w2), T, d, ffn, E, k, _ptr(out),
+                                    _dtype_code(out.dtype), _ptr(topk_idx_out),
+                                    _ptr(topk_w_out), _ptr(counts_out), _stream(dev),
+                                    _options(variant, events))
+    _check("moe_forward_noalloc", st)
+    return out

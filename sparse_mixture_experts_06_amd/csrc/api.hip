@@ -6,7 +6,14 @@
 
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
+
+// Workspace of moe_forward_noalloc: one array per GPU (the code object's copy
+// on each device), never passed to a kernel by this name: host code takes its
+// device address from hipGetSymbolAddress once per device and uses that.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -32,6 +39,25 @@ int read_options(const moe_options* o, Opts* out) {
 }
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there (with that device current) and kept per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
 
 struct Layout {
   size_t idx, w, counts, offsets, sorted, pos, h, y, wide, total;
@@ -191,7 +217,7 @@ const char* moe_strerror(int status) {
     case MOE_OK: return "success";
     case MOE_EINVAL: return "invalid argument (pointer, size, dtype, k or E)";
     case MOE_ENOTSUP: return "unsupported shape or alignment (bf16 needs d, ffn % 64 == 0 and 16-byte aligned buffers)";
-    case MOE_EWORKSPACE: return "workspace missing or smaller than moe_workspace_bytes()";
+    case MOE_EWORKSPACE: return "workspace missing or smaller than moe_workspace_bytes() (moe_forward_noalloc: more than its built-in scratch)";
     case MOE_EHIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -388,6 +414,24 @@ int moe_block_forward(const void* hidden, int dtype, const float* norm_weight, f
   return forward_impl(hidden, dtype, norm_weight, eps, norm_out, router, logit_bias, w1, w3, w2,
                       T, d, ffn, E, k, out, out_dtype, topk_idx_out, topk_w_out, counts_out, ws,
                       ws_bytes, stream, options);
+}
+
+int moe_forward_noalloc(const void* x, int dtype, const float* router, const float* logit_bias,
+                        const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
+                        int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,
+                        float* topk_w_out, int32_t* counts_out, void* stream,
+                        const moe_options* options) {
+  // sizes beyond the scratch (or invalid ones) reach forward_impl without a
+  // workspace, which reports them before anything is enqueued
+  const size_t need = moe_workspace_bytes(T, d, ffn, E, k, dtype);
+  void* ws = nullptr;
+  if (need > 0 && need <= MOE_NOALLOC_SCRATCH_BYTES) {
+    const int st = scratch_address(&ws);
+    if (st != MOE_OK) return st;
+  }
+  return forward_impl(x, dtype, nullptr, 0.0f, nullptr, router, logit_bias, w1, w3, w2, T, d,
+                      ffn, E, k, out, out_dtype, topk_idx_out, topk_w_out, counts_out, ws,
+                      ws ? MOE_NOALLOC_SCRATCH_BYTES : 0, stream, options);
 }
 
 size_t moe_quantized_weight_bytes(int E, int rows, int cols) {
