@@ -13,9 +13,11 @@ records on its stream between the stages, on every 4th timed step (an event
 record leaves the GPU idle for a few microseconds, so recording them on every
 step would slow the decode step by about 5%).
 
-By default the expert weights are held in fragment order (moe_pack_weight,
-run once when the weights are loaded, outside the timed region); the rate
-with the standard [E, ffn, d] layout is measured too and reported beside it.
+bf16 expert weights are timed in both layouts: fragment order
+(moe_pack_weight, run once when the weights are loaded, outside the timed
+region) and the standard [E, ffn, d] layout; the faster is the record's
+value ("weights_layout" names it) and the other is reported beside it
+("other_layout"). --layout standard, or --no-compare, times one.
 
 --block times moe_block_forward instead: the RMS norm in front of the layer
 and the residual add after it (the MLP half of the decoder block).
@@ -360,11 +362,14 @@ def roofline(bytes_, flops, seconds, bound):
 
 
 def time_workload(moe, torch, hip, cfg, key, steps, warmup, variant=0, layout="packed",
-                  compare=True, int8=False, block=False, calib_mib=0, inp=None):
+                  compare=True, int8=False, block=False, calib_mib=0, inp=None,
+                  best_layout=True):
     """Times `steps` layer calls on one workload (after `warmup`), alternating
     between two copies of the expert weights, with the library's stage events
-    on every EVENT_EVERY-th timed step. `inp`: the host inputs when already
-    drawn. Returns (record, host inputs, gamma)."""
+    on every EVENT_EVERY-th timed step. bf16 weights are timed in fragment
+    order and (compare) in the standard layout; with best_layout the faster
+    one is the record's value and the other is reported beside it. `inp`: the
+    host inputs when already drawn. Returns (record, host inputs, gamma)."""
     import numpy as np
 
     import gen
@@ -425,43 +430,47 @@ def time_workload(moe, torch, hip, cfg, key, steps, warmup, variant=0, layout="p
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for i in range(warmup):
-        step(i, sets, packed)
-    torch.cuda.synchronize()
-    # stage events on every EVENT_EVERY-th timed step: each event record makes the
-    # GPU idle a few microseconds between kernels, so recording all six on
-    # every step would itself slow the step down by about 5% at decode
-    ev_steps = list(range(0, steps, EVENT_EVERY))
-    evs = {i: [hip.event() for _ in range(6)] for i in ev_steps}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i, sets, packed, evs.get(i))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs.values()]))
-                for j, name in enumerate(STAGES)}
-    for e in evs.values():
-        for ev in e:
-            hip.destroy(ev)
 
+    def timed(use_sets, is_packed):
+        """(ms per step, per-stage ms) of one weight layout."""
+        for i in range(warmup):
+            step(i, use_sets, is_packed)
+        torch.cuda.synchronize()
+        # stage events on every EVENT_EVERY-th timed step: each event record makes
+        # the GPU idle a few microseconds between kernels, so recording all six on
+        # every step would itself slow the step down by about 5% at decode
+        evs = {i: [hip.event() for _ in range(6)] for i in range(0, steps, EVENT_EVERY)}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i, use_sets, is_packed, evs.get(i))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        stage = {name: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs.values()]))
+                 for j, name in enumerate(STAGES)}
+        for e in evs.values():
+            for ev in e:
+                hip.destroy(ev)
+        return wall * 1e3 / steps, stage
+
+    ms_step, stage_ms = timed(sets, packed)
+    layout_name = ("weight-only int8, float32 row scales (moe_quantize_weight once at load time)"
+                   if int8 else "fragment order (moe_pack_weight once at load time)" if packed
+                   else "standard [E, ffn, d]" if cfg["dtype"] == "bf16"
+                   else "standard [E, ffn, d] float32")
     other = None
     if packed and std_sets is not None:
-        for i in range(warmup):
-            step(i, std_sets, False)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for i in range(steps):
-            step(i, std_sets, False)
-        torch.cuda.synchronize()
-        ms_std = (time.perf_counter() - t1) * 1e3 / steps
+        ms_std, stage_std = timed(std_sets, False)
         other = {"layout": "standard [E, ffn, d]", "value": round(T / (ms_std / 1e3), 1),
                  "ms_per_step": round(ms_std, 4)}
+        if best_layout and ms_std < ms_step:  # report the faster layout, the other beside it
+            other = {"layout": layout_name, "value": round(T / (ms_step / 1e3), 1),
+                     "ms_per_step": round(ms_step, 4)}
+            ms_step, stage_ms, layout_name = ms_std, stage_std, "standard [E, ffn, d]"
 
     cnt = counts.cpu().tolist()
     layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt, block, int8)
     dn_bytes, dn_flops = down_work(cfg, cnt, int8)
-    ms_step = wall * 1e3 / steps
     tok_s = T / (ms_step / 1e3)
     # the streaming kernels' regime (few rows per expert): weight-bandwidth
     # bound; beyond it the tiled kernels are bound by the bf16 MFMA rate
@@ -490,11 +499,7 @@ def time_workload(moe, torch, hip, cfg, key, steps, warmup, variant=0, layout="p
                   "algorithmic_bytes": layer_bytes, "algorithmic_flops": layer_flops,
                   "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
                   "expert_counts": cnt},
-        "weights_layout": ("weight-only int8, float32 row scales (moe_quantize_weight once at "
-                           "load time)" if int8 else
-                           "fragment order (moe_pack_weight once at load time)" if packed
-                           else "standard [E, ffn, d]" if cfg["dtype"] == "bf16"
-                           else "standard [E, ffn, d] float32"),
+        "weights_layout": layout_name,
     }
     if other is not None:
         rec["other_layout"] = other
@@ -569,7 +574,7 @@ def main():
             dinp = dict(pinp, T=dcfg["T"], x=pinp["x"][:dcfg["T"]])
             for name, c, i in ((dname, dcfg, dinp), (pname, pcfg, pinp)):
                 wrec, _, _ = time_workload(moe, torch, hip, c, name, args.extra_steps, 5,
-                                           compare=False, inp=i)
+                                           inp=i)
                 line["workloads"][name] = wrec
             del pinp, dinp
 

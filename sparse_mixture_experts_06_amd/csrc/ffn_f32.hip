@@ -1,6 +1,10 @@
 // Expert SwiGLU in float32 (the all-fp32 workloads): the same two grouped
 // steps as the bf16 path, one thread per output element, float32 FMA
-// accumulation, h kept in float32. Any d and ffn.
+// accumulation, h kept in float32. Any d and ffn. When the rows are 16-byte
+// aligned (K % 4 == 0 and aligned arrays) a thread reads them 4 floats at a
+// time into 4 partial sums (the products of element i go to sum i % 4,
+// added as (s0 + s1) + (s2 + s3) at the end), with several loads in flight:
+// the dot products are short, so their time is load latency.
 //   gate/up: h[p, n] = silu(x[r] . w1[e, n]) * (x[r] . w3[e, n]),  r = sorted_asg[p] / k
 //   down:    y[p, n] = h[p] . w2[e, n]
 // (nnterp Mixtral page, support(): act(gate) * up feeds the down projection.)
@@ -33,6 +37,32 @@ __device__ __forceinline__ bool decode(const int32_t* __restrict__ offsets, int 
   return false;
 }
 
+// sum_i a[i] * b[i] over n floats: in order (VEC false) or with 16-byte
+// loads into 4 partial sums (VEC: n % 4 == 0, both 16-byte aligned)
+template <bool VEC>
+__device__ __forceinline__ float dot_f32(const float* __restrict__ a, const float* __restrict__ b,
+                                         int n) {
+  if constexpr (VEC) {
+    const float4* a4 = reinterpret_cast<const float4*>(a);
+    const float4* b4 = reinterpret_cast<const float4*>(b);
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll 8
+    for (int i = 0; i < n / 4; ++i) {
+      const float4 u = a4[i], v = b4[i];
+      s0 = fmaf(u.x, v.x, s0);
+      s1 = fmaf(u.y, v.y, s1);
+      s2 = fmaf(u.z, v.z, s2);
+      s3 = fmaf(u.w, v.w, s3);
+    }
+    return (s0 + s1) + (s2 + s3);
+  } else {
+    float acc = 0.0f;
+    for (int i = 0; i < n; ++i) acc = fmaf(a[i], b[i], acc);
+    return acc;
+  }
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(TM* TN) void gate_up_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ w1, const float* __restrict__ w3,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_asg, int d, int ffn,
@@ -46,14 +76,12 @@ __global__ __launch_bounds__(TM* TN) void gate_up_f32_kernel(
   const float* xr = x + row * d;
   const float* g1 = w1 + (static_cast<int64_t>(e) * ffn + n) * d;
   const float* g3 = w3 + (static_cast<int64_t>(e) * ffn + n) * d;
-  float g = 0.0f, u = 0.0f;
-  for (int i = 0; i < d; ++i) {
-    g = fmaf(xr[i], g1[i], g);
-    u = fmaf(xr[i], g3[i], u);
-  }
+  const float g = dot_f32<VEC>(xr, g1, d);
+  const float u = dot_f32<VEC>(xr, g3, d);
   h[static_cast<int64_t>(beg + m) * ffn + n] = g / (1.0f + expf(-g)) * u;
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(TM* TN) void down_f32_kernel(const float* __restrict__ h,
                                                          const float* __restrict__ w2,
                                                          const int32_t* __restrict__ offsets,
@@ -66,14 +94,14 @@ __global__ __launch_bounds__(TM* TN) void down_f32_kernel(const float* __restric
   if (m >= M || n >= d) return;
   const float* hr = h + static_cast<int64_t>(beg + m) * ffn;
   const float* wr = w2 + (static_cast<int64_t>(e) * d + n) * ffn;
-  float acc = 0.0f;
-  for (int f = 0; f < ffn; ++f) acc = fmaf(hr[f], wr[f], acc);
-  y[static_cast<int64_t>(beg + m) * d + n] = acc;
+  y[static_cast<int64_t>(beg + m) * d + n] = dot_f32<VEC>(hr, wr, ffn);
 }
 
 inline unsigned grid_for(int64_t A, int E, int ntn) {
   return static_cast<unsigned>(((A + TM - 1) / TM + E) * ntn);
 }
+
+inline bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
 
@@ -82,8 +110,12 @@ hipError_t launch_gate_up_f32(const float* x, const float* w1, const float* w3,
                               int d, int ffn, int E, int k, float* h, hipStream_t s) {
   if (A == 0) return hipSuccess;
   const int ntn = (ffn + TN - 1) / TN;
-  hipLaunchKernelGGL(gate_up_f32_kernel, dim3(grid_for(A, E, ntn)), dim3(TM * TN), 0, s, x, w1,
-                     w3, offsets, sorted_asg, d, ffn, E, k, h, ntn);
+  if (d % 4 == 0 && a16(x) && a16(w1) && a16(w3))
+    hipLaunchKernelGGL(gate_up_f32_kernel<true>, dim3(grid_for(A, E, ntn)), dim3(TM * TN), 0, s,
+                       x, w1, w3, offsets, sorted_asg, d, ffn, E, k, h, ntn);
+  else
+    hipLaunchKernelGGL(gate_up_f32_kernel<false>, dim3(grid_for(A, E, ntn)), dim3(TM * TN), 0, s,
+                       x, w1, w3, offsets, sorted_asg, d, ffn, E, k, h, ntn);
   return hipGetLastError();
 }
 
@@ -91,8 +123,13 @@ hipError_t launch_down_f32(const float* h, const float* w2, const int32_t* offse
                            int d, int ffn, int E, float* y, hipStream_t s) {
   if (A == 0) return hipSuccess;
   const int ntn = (d + TN - 1) / TN;
-  hipLaunchKernelGGL(down_f32_kernel, dim3(grid_for(A, E, ntn)), dim3(TM * TN), 0, s, h, w2,
-                     offsets, d, ffn, E, y, ntn);
+  // (h rows are ffn floats apart from an aligned workspace region)
+  if (ffn % 4 == 0 && a16(h) && a16(w2))
+    hipLaunchKernelGGL(down_f32_kernel<true>, dim3(grid_for(A, E, ntn)), dim3(TM * TN), 0, s, h,
+                       w2, offsets, d, ffn, E, y, ntn);
+  else
+    hipLaunchKernelGGL(down_f32_kernel<false>, dim3(grid_for(A, E, ntn)), dim3(TM * TN), 0, s, h,
+                       w2, offsets, d, ffn, E, y, ntn);
   return hipGetLastError();
 }
 
