@@ -472,6 +472,9 @@ def time_workload(moe, torch, hip, cfg, key, steps, warmup, variant=0, layout="p
     layer_bytes, layer_flops, gu_bytes, gu_flops = algorithmic_work(cfg, cnt, block, int8)
     dn_bytes, dn_flops = down_work(cfg, cnt, int8)
     tok_s = T / (ms_step / 1e3)
+    # traffic records are kept per weight layout (standard-layout ones end in "+standard")
+    tkey = key + ("+standard" if layout_name.startswith("standard") and cfg["dtype"] == "bf16"
+                  else "")
     # the streaming kernels' regime (few rows per expert): weight-bandwidth
     # bound; beyond it the tiled kernels are bound by the bf16 MFMA rate
     bound = "hbm" if (T * k) <= 32 * E else "mfma"
@@ -479,11 +482,11 @@ def time_workload(moe, torch, hip, cfg, key, steps, warmup, variant=0, layout="p
     roof.update({"kernel": "gate_up (w1/w3 grouped GEMM + SiLU*mul)",
                  "avg_us": round(stage_ms["gate_up"] * 1e3, 2),
                  "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops,
-                 "traffic": traffic_entry(key)})
+                 "traffic": traffic_entry(tkey)})
     droof = roofline(dn_bytes, dn_flops, stage_ms["down"] / 1e3, bound)
     droof.update({"kernel": "down (w2 grouped GEMM)", "avg_us": round(stage_ms["down"] * 1e3, 2),
                   "algorithmic_bytes": dn_bytes, "algorithmic_flops": dn_flops,
-                  "traffic": traffic_entry(key, "down")})
+                  "traffic": traffic_entry(tkey, "down")})
     layer_tflops = layer_flops / (ms_step / 1e3) / 1e12
     layer_gbs = layer_bytes / (ms_step / 1e3) / 1e9
     rec = {
@@ -521,7 +524,8 @@ def main():
     workload = args.workload or "decode_8x7b"
     if args.pmc_summary:
         key = workload + ("+block" if args.block else "") + \
-            ("+int8" if args.weights == "int8" else "")
+            ("+int8" if args.weights == "int8" else "") + \
+            ("+standard" if args.layout == "standard" and args.weights == "bf16" else "")
         pmc_summary(key, args.pmc_summary[0], args.pmc_summary[1],
                     args.calib_copy_mib or 1024)
         return

@@ -5,21 +5,27 @@
 // One workgroup of 16 waves does the whole job, so there is no
 // inter-workgroup synchronisation and the result is deterministic. Wave w
 // owns the contiguous slice of assignments [w C, (w+1) C), C = A / 16
-// rounded up to a multiple of 64, and walks it in steps of 64:
-//   1. counts: per step one ballot per expert; lane e keeps expert e's count
-//      of the slice, written to LDS;
+// rounded up to a multiple of 64, and walks it in steps of 64. In a step,
+// each lane finds the lanes holding the same expert id as its own from one
+// ballot per bit of the id (an id has at most 5 bits, E <= 32): the AND of
+// the ballots its bits select; its rank in the step is the number of those
+// lanes below it, and the lowest of them (rank 0) speaks for the group.
+//   1. counts: the speaking lane of each group adds the group's size to its
+//      expert's count of the slice in LDS;
 //   2. one thread per expert sums the slices' counts in slice order: counts,
 //      offsets (exclusive scan over experts) and each slice's first position
-//      per expert (offsets[e] + the counts of the earlier slices);
-//   3. each wave walks its slice again: an assignment's position is its
-//      slice's first position for its expert, plus the expert's count in the
-//      earlier steps of the slice, plus its rank among the earlier lanes of
-//      its step with the same expert (a ballot).
-// Each walk loads 8 steps of ids at a time, all in flight before the first
-// is used (one memory latency per 512 ids, not per 64).
+//      per expert (offsets[e] + the counts of the earlier slices), written to
+//      an array of their own (the counts stay unchanged while other threads
+//      read them);
+//   3. each wave walks its slice again: an assignment's position is the
+//      running position of its expert in the slice (its slice's first
+//      position plus the expert's count in the earlier steps) plus its rank;
+//      the speaking lane then advances the running position.
 // Slices, steps and lanes are all in increasing assignment order, so within
-// an expert the assignments keep their order (a stable sort). Two barriers.
-// Expert ids outside [0, E) are ignored (no out-of-bounds access).
+// an expert the assignments keep their order (a stable sort). Each walk
+// loads 8 steps of ids at a time, all in flight before the first is used.
+// Two barriers (after zeroing the counts, one more). Expert ids outside
+// [0, E) are ignored (no out-of-bounds access).
 #include "common.h"
 
 namespace moe {
@@ -29,23 +35,39 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kSteps = 8;  // steps of 64 expert ids a wave loads at once
 
+// lanes of the wave whose id equals this lane's (valid lanes only; nb = bits of
+// an id): the AND, over the nb bits, of the ballot of lanes with that bit set
+// or of its complement
+__device__ __forceinline__ uint64_t same_id_lanes(int e, bool valid, int nb) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nb; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t set = __ballot(valid && bit);
+    m &= bit ? set : ~set;
+  }
+  return m;
+}
+
 __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ idx,
                                                            int A, int E,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ sorted_asg,
                                                            int32_t* __restrict__ asg_pos) {
-  __shared__ int s_cnt[kWaves][kMaxExperts];   // slice counts, then slice first positions
+  __shared__ int s_cnt[kWaves][kMaxExperts];  // count of each expert in each slice
+  __shared__ int s_pos[kWaves][kMaxExperts];  // each slice's running position per expert
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  if (tid < kWaves * kMaxExperts) (&s_cnt[0][0])[tid] = 0;
+  __syncthreads();
+  int nb = 0;  // bits of the largest id
+  while ((1 << nb) < E) ++nb;
+  const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
   // slice of this wave, in whole steps of 64 (A <= 2^31 - 1024, so no overflow)
   const int per = ((A + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
   const int lo = min(A, wave * per), hi = min(A, lo + per);
 
-  // the slice's expert ids are loaded kSteps steps of 64 at a time, all in
-  // flight together, before any is used
-  int cnt = 0;  // lane e: expert e's count in this slice
   for (int c0 = lo; c0 < hi; c0 += kSteps * kWave) {
     int ev[kSteps];
 #pragma unroll
@@ -55,13 +77,11 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     }
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
-      for (int ee = 0; ee < E; ++ee) {
-        const int c = __popcll(__ballot(ev[u] == ee));
-        if (lane == ee) cnt += c;
-      }
+      const bool valid = ev[u] >= 0 && ev[u] < E;
+      const uint64_t m = same_id_lanes(ev[u], valid, nb);
+      if (valid && (m & lower) == 0) s_cnt[wave][ev[u]] += __popcll(m);
     }
   }
-  if (lane < E) s_cnt[wave][lane] = cnt;
   __syncthreads();
 
   if (tid < E) {
@@ -70,9 +90,8 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
       for (int w = 0; w < kWaves; ++w) before += s_cnt[w][e];
     int run = before;
     for (int w = 0; w < kWaves; ++w) {
-      const int c = s_cnt[w][tid];
-      s_cnt[w][tid] = run;
-      run += c;
+      s_pos[w][tid] = run;
+      run += s_cnt[w][tid];
     }
     counts[tid] = run - before;
     offsets[tid] = before;
@@ -80,29 +99,24 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
   }
   __syncthreads();
 
-  const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-  int next = lane < E ? s_cnt[wave][lane] : 0;  // lane e: next position of expert e
   for (int c0 = lo; c0 < hi; c0 += kSteps * kWave) {
     int ev[kSteps];
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       const int a = c0 + u * kWave + lane;
-      const int e = a < hi ? idx[a] : -1;
-      ev[u] = e < E ? e : -1;
+      ev[u] = a < hi ? idx[a] : -1;
     }
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       const int a = c0 + u * kWave + lane;
-      int pos = 0;
-      for (int ee = 0; ee < E; ++ee) {
-        const uint64_t m = __ballot(ev[u] == ee);
-        const int first = __builtin_amdgcn_readlane(next, ee);
-        if (ev[u] == ee) pos = first + __popcll(m & lower);
-        if (lane == ee) next += __popcll(m);
-      }
-      if (ev[u] >= 0) {
+      const bool valid = ev[u] >= 0 && ev[u] < E;
+      const uint64_t m = same_id_lanes(ev[u], valid, nb);
+      if (valid) {
+        const uint64_t below = m & lower;
+        const int pos = s_pos[wave][ev[u]] + __popcll(below);
         sorted_asg[pos] = a;
         asg_pos[a] = pos;
+        if (below == 0) s_pos[wave][ev[u]] = pos + __popcll(m);
       }
     }
   }
