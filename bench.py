@@ -199,10 +199,10 @@ def traffic_entry(workload, kernel="gate_up"):
     return ent.get("hbm_bytes_per_launch")
 
 
-GATE_UP_KERNELS = ("gate_up_stream_kernel", "gate_up_dma_kernel", "tiled_kernel<true",
-                   "wtiled_kernel<true", "gate_up_w8_kernel")
-DOWN_KERNELS = ("down_stream_kernel", "down_dma_kernel", "tiled_kernel<false",
-                "wtiled_kernel<false", "down_w8_kernel")
+GATE_UP_KERNELS = ("gate_up_stream_kernel", "gate_up_stream_rm_kernel", "gate_up_dma_kernel",
+                   "tiled_kernel<true", "wtiled_kernel<true", "gate_up_w8_kernel")
+DOWN_KERNELS = ("down_stream_kernel", "down_stream_rm_kernel", "down_dma_kernel",
+                "tiled_kernel<false", "wtiled_kernel<false", "down_w8_kernel")
 
 
 def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
