@@ -54,8 +54,14 @@ def test_committed_traffic_record_is_current():
         rec = json.load(f)
     if rec.get("ffn_sources_sha256") != bench.ffn_sources_sha():
         pytest.skip("gate/up kernel sources changed since the counters were taken")
-    ent = rec["workloads"]["decode_8x7b"]
-    assert ent["hbm_bytes_per_launch"] == ent["fetch_bytes"] + ent["write_bytes"]
+    assert rec["workloads"], "no workload recorded"
+    for key, ent in rec["workloads"].items():
+        assert ent["hbm_bytes_per_launch"] == ent["fetch_bytes"] + ent["write_bytes"], key
+        if "down" in ent:
+            d = ent["down"]
+            assert d["hbm_bytes_per_launch"] == d["fetch_bytes"] + d["write_bytes"], key
+    # the decode line's layout (standard) has its record
+    assert "decode_8x7b+standard" in rec["workloads"]
 
 
 def test_routing_workload_pairs_share_their_inputs():
