@@ -68,6 +68,17 @@
 // the SiLU*mul (gate by the w1 row's scale, up by the w3 row's) or the store
 // (down, each K-split partial), as the int8 decode kernels do.
 //
+// Paired last m-tiles (gate/up with fragment-order weights): an expert's last
+// m-tile of at most 128 rows costs nearly as much as a full one (its time is
+// set by the weight stream it shares with the full tiles of its weight tile,
+// not by its own loads or MFMAs: halving either changed nothing, while
+// leaving those tiles out took 9-13% off the launch), so two weight tiles
+// of an XCD share one: 512 weight rows x 128 token rows, each wave the same 64
+// x 128 block as in a 256x256 tile. 8x7B prefill: 4032 -> 3808 tiles, gate/up
+// 1574 -> 1497-1544 us; 8x22B 1510 -> 1458 us. The down projection keeps its own
+// last m-tiles (paired, they ran 2-3% slower there: its tiles are few and
+// long, and the K split already fills the last round).
+//
 // Every output element is one float32 MFMA accumulation over its K range in
 // increasing K, 32 at a time: the order of the 128-row tiled kernels, whose
 // results this kernel reproduces bit for bit.
@@ -105,29 +116,56 @@ constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | 
 // one XCD's L2. Its tiles are listed K part by K part (the longer first part
 // of every tile before any second part, so that the short ones fill the last
 // round), expert by expert, n-tile by n-tile, m-tile by m-tile, and taken in
-// that order, tile q by workgroup 8q + x. Otherwise (fewer or ragged weight
-// tiles) XCD x takes the x-th of 8 equal slices of the list of all tiles,
-// expert by expert, K part, n-tile, m-tile. Surplus workgroups of the
-// worst-case grid return.
+// that order, tile q by workgroup 8q + x. With pair_tails, an expert whose
+// last m-tile holds at most DT/2 rows lists its XCD's weight tiles in pairs
+// (2g, 2g+1): first one tile for both last m-tiles (nt2 = the second weight
+// tile; otherwise nt2 = -1), then the full m-tiles of the two alternately; an
+// odd weight tile left over keeps its own last m-tile. Otherwise (fewer or
+// ragged weight tiles) XCD x takes the x-th of 8 equal slices of the list of
+// all tiles, expert by expert, K part, n-tile, m-tile. Surplus workgroups of
+// the worst-case grid return.
 __device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offsets, int E, int ntn,
-                                               int nsplit, int& e, int& beg, int& M, int& m0,
-                                               int& nt, int& sp) {
+                                               int nsplit, bool pair_tails, int& e, int& beg,
+                                               int& M, int& m0, int& nt, int& nt2, int& sp) {
   const int x = blockIdx.x & 7;
   int q = blockIdx.x >> 3;
+  nt2 = -1;
   if ((ntn & 7) == 0) {
     const int nnx = ntn >> 3;  // weight tiles of each XCD
+    // pairs of the XCD's weight tiles (2g, 2g+1) whose last m-tiles share one
+    // tile when those hold at most DT/2 rows
+    const int pairs = pair_tails ? nnx >> 1 : 0;
     for (int s = 0; s < nsplit; ++s) {
       for (int i = 0; i < E; ++i) {
         const int Mi = offsets[i + 1] - offsets[i];
         const int mt = (Mi + DT - 1) / DT;
-        const int cnt = mt * nnx;
+        const bool small = pairs > 0 && mt > 0 && Mi - (mt - 1) * DT <= DT / 2;
+        const int mf = small ? mt - 1 : mt;  // m-tiles a weight tile runs alone
+        const int gsz = 2 * mf + 1;          // tiles of a pair's group
+        const int cnt = small ? pairs * gsz + (nnx - 2 * pairs) * mt : mt * nnx;
         if (q < cnt) {
           e = i;
           beg = offsets[i];
           M = Mi;
-          m0 = (q % mt) * DT;
-          nt = (q / mt) * 8 + x;
           sp = s;
+          if (small && q < pairs * gsz) {
+            // group g: the shared last m-tile of weight tiles 2g and 2g+1,
+            // then their full m-tiles alternately (so that the tiles reading
+            // either weight tile run together)
+            const int g = q / gsz, r = q % gsz;
+            if (r == 0) {
+              m0 = mf * DT;
+              nt = 2 * g * 8 + x;
+              nt2 = nt + 8;
+            } else {
+              m0 = ((r - 1) >> 1) * DT;
+              nt = (2 * g + ((r - 1) & 1)) * 8 + x;
+            }
+          } else {
+            const int qq = small ? q - pairs * gsz : q;
+            m0 = (qq % mt) * DT;
+            nt = ((small ? 2 * pairs : 0) + qq / mt) * 8 + x;
+          }
           return true;
         }
         q -= cnt;
@@ -176,8 +214,9 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
                                          int nsplit, int ksplit, int64_t pstride,
                                          const float* __restrict__ sa,
                                          const float* __restrict__ sb) {
-  int e, beg, M, m0, nt, sp;
-  if (!decode_tile256(offsets, E, ntn, nsplit, e, beg, M, m0, nt, sp)) return;
+  int e, beg, M, m0, nt, nt2, sp;
+  if (!decode_tile256(offsets, E, ntn, nsplit, PACKED && GATE_UP, e, beg, M, m0, nt, nt2, sp))
+    return;
 
   // one array per buffer: distinct objects let the compiler see that a
   // fragment read does not depend on the loads in flight to other buffers
@@ -190,6 +229,10 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   __shared__ __attribute__((aligned(1024))) uint16_t wb3[kWB3];
   __shared__ __attribute__((aligned(1024))) uint16_t tb0[kTBufE];
   __shared__ __attribute__((aligned(1024))) uint16_t tb1[kTBufE];
+  // (fragment order only: the token stages of a paired tile)
+  constexpr int kXB = PACKED ? kWBufE : 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t xb0[kXB];
+  __shared__ __attribute__((aligned(1024))) uint16_t xb1[kXB];
   auto wbufp = [&](auto bi) -> uint16_t* {
     constexpr int B = decltype(bi)::value;
     if constexpr (B == 0) return wb0;
@@ -201,6 +244,35 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
     constexpr int B = decltype(bi)::value;
     if constexpr (B == 0) return tb0;
     else return tb1;
+  };
+  // A paired tile (WIDE; fragment order only) computes the last m-tile, at
+  // most 128 rows, of two weight tiles nt and nt2 of the same expert: wave
+  // (wn, wm) takes 64 weight rows of tile wm ? nt2 : nt and the tile's 128
+  // token rows, so each wave does what it does in a 256x256 tile. A step's 32
+  // weight fragments (two 16 KiB halves) sit in weight buffer b: b = 0 in
+  // tb0, b = 1 in wb0 and wb1, b = 2 in tb1, b = 3 in wb2 and wb3; the two
+  // 16 KiB token stages in xb0 and xb1. Each LDS array still serves one
+  // buffer only, so no fragment read shares an array with a load in flight.
+  auto body = [&](auto widec) {
+  constexpr bool WIDE = decltype(widec)::value;
+  // (the half is a compile-time constant: a pointer chosen at run time
+  // between two arrays would hide which array a fragment read touches)
+  auto wbw = [&](auto bi, auto hc) -> uint16_t* {
+    constexpr int B = decltype(bi)::value;
+    constexpr int H = decltype(hc)::value;
+    if constexpr (B == 0) return tb0 + H * kWBufE;
+    else if constexpr (B == 1) return H ? wb1 : wb0;
+    else if constexpr (B == 2) return tb1 + H * kWBufE;
+    else return H ? wb3 : wb2;
+  };
+  auto tsp = [&](auto bi) -> uint16_t* {
+    constexpr int B = decltype(bi)::value;
+    if constexpr (WIDE) {
+      if constexpr (B == 0) return xb0;
+      else return xb1;
+    } else {
+      return tbufp(bi);
+    }
   };
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -220,16 +292,22 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
       const_cast<uint16_t*>(wsrc + e * wslice), 0, static_cast<int>(wslice * 2), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(act), 0, static_cast<int>(act_rows * K * 2), kRsrcWord3);
-  int aoff[2];  // fragment order: byte offsets of step 0 (wave-uniform)
+  int aoff[2][2];  // fragment order: byte offsets of step 0 (wave-uniform), [half][q]
   // row-major: per-lane byte offsets of stage 0 for the loads q = 0, 2 and
   // q = 1, 3 (rows placed as the token rows below; load q reads 8q rows
   // further, a wave-uniform offset, and the swizzle slot depends on q % 2)
   int woff[2];
   if constexpr (PACKED) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = GATE_UP ? nt * 128 + (w >> 1) * 32 + q * 16 : nt * 256 + (2 * w + q) * 16;
-      aoff[q] = __builtin_amdgcn_readfirstlane(static_cast<int>(wofs<true>(0, row, k0, N, K) * 2));
+    for (int hh = 0; hh < (WIDE ? 2 : 1); ++hh) {
+      const int ntt = hh ? nt2 : nt;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int row =
+            GATE_UP ? ntt * 128 + (w >> 1) * 32 + q * 16 : ntt * 256 + (2 * w + q) * 16;
+        aoff[hh][q] =
+            __builtin_amdgcn_readfirstlane(static_cast<int>(wofs<true>(0, row, k0, N, K) * 2));
+      }
     }
   } else {
 #pragma unroll
@@ -242,10 +320,13 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   }
   // token loads: wave w moves tile rows 32w .. 32w+31, 8 rows x 128 B per load; lane l puts row
   // 32w + 8q + l/8, LDS slot l%8, which holds 16-byte chunk (l%8) ^ ((row/2) % 8) of the K64 stage
-  int toff[4];
+  // (paired tile: 128 rows, wave w rows 16w .. 16w+15, two loads)
+  constexpr int kTQ = WIDE ? 2 : 4;   // token loads of a wave per stage
+  constexpr int kTR = 8 * kTQ;        // token rows of a wave
+  int toff[kTQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 32 * w + 8 * q + (lane >> 3);
+  for (int q = 0; q < kTQ; ++q) {
+    const int r = kTR * w + 8 * q + (lane >> 3);
     const int mm = min(m0 + r, M - 1);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int src = GATE_UP ? sorted_asg[beg + mm] / ktop : beg + mm;
@@ -257,11 +338,19 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   const int last_stage = nsteps / 2 - 1;
   auto load_w = [&](uint16_t* L, int q, int t) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr)(L + (2 * w + q) * kFragE), 16, lane16,
-                                             aoff[q] + t * (kFragE * 2), 0, 0);
+                                             aoff[0][q] + t * (kFragE * 2), 0, 0);
+  };
+  // paired tile: both fragments of this wave in half hh of weight buffer bi
+  auto load_w2 = [&](auto bi, auto hc, int t) {
+    constexpr int H = decltype(hc)::value;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr)(wbw(bi, hc) + (2 * w + q) * kFragE),
+                                               16, lane16, aoff[H][q] + t * (kFragE * 2), 0, 0);
   };
   auto load_x = [&](uint16_t* L, int q, int s) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_ptr)(L + (32 * w + 8 * q) * 64), 16, toff[q],
-                                             s * 128, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_ptr)(L + (kTR * w + 8 * q) * 64), 16,
+                                             toff[q], s * 128, 0, 0);
   };
   auto load_ws = [&](uint16_t* L, int q, int s) {  // row-major weights, K64 stage s
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr)(L + (32 * w + 8 * q) * 64), 16,
@@ -276,7 +365,14 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   using I3 = std::integral_constant<int, 3>;
   // (row-major weights: weight stages 0-2 and token stages 0-1, in the order
   // odd steps issue them, tokens of stage s with weights of stage s+1)
-  if constexpr (PACKED) {
+  if constexpr (WIDE) {
+    load_w2(I0{}, I0{}, 0); load_w2(I0{}, I1{}, 0);
+    load_x(tsp(I0{}), 0, 0); load_x(tsp(I0{}), 1, 0);
+    load_w2(I1{}, I0{}, min(1, last)); load_w2(I1{}, I1{}, min(1, last));
+    load_w2(I2{}, I0{}, min(2, last)); load_w2(I2{}, I1{}, min(2, last));
+    load_x(tsp(I1{}), 0, min(1, last_stage)); load_x(tsp(I1{}), 1, min(1, last_stage));
+    load_w2(I3{}, I0{}, min(3, last)); load_w2(I3{}, I1{}, min(3, last));
+  } else if constexpr (PACKED) {
     load_w(wbufp(I0{}), 0, 0); load_w(wbufp(I0{}), 1, 0);
     load_x(tbufp(I0{}), 0, 0); load_x(tbufp(I0{}), 1, 0); load_x(tbufp(I0{}), 2, 0); load_x(tbufp(I0{}), 3, 0);
     load_w(wbufp(I1{}), 0, min(1, last)); load_w(wbufp(I1{}), 1, min(1, last));
@@ -294,17 +390,19 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
   }
 
   // fragments of this wave's token tiles that hold a row, rounded up to even
-  const int valid = M - m0 - wm * 128;
+  const int valid = M - m0 - (WIDE ? 0 : wm * 128);
   const int jv = valid >= 128 ? 8 : valid <= 0 ? 0 : (((valid + 15) >> 4) + 1) & ~1;
   // token fragment reads: row (wm*128 + 16j + fr), chunk 4*half + fg, swizzled slot
-  const int trow = (wm * 128 + fr) * 64;
+  const int trow = ((WIDE ? 0 : wm * 128) + fr) * 64;
   const int tcol0 = ((fg) ^ ((fr >> 1) & 7)) * 8;
   const int tcol1 = ((4 + fg) ^ ((fr >> 1) & 7)) * 8;
   // row-major weight fragment reads: row (wn*64 + 16k + fr), same chunks and slots
   const int wrow = (wn * 64 + fr) * 64;
 
-  auto run = [&](auto jvc) {
+  // (WMC: the wave's wm as a constant, for the paired tile's weight reads)
+  auto run = [&](auto jvc, auto wmc) {
     constexpr int JV = decltype(jvc)::value;
+    constexpr int WMC = decltype(wmc)::value;
     u32x4 fa[2][4], fb[2][8];
     f32x4 acc[4][JV > 0 ? JV : 1];
 #pragma unroll
@@ -317,17 +415,20 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
       constexpr int S = decltype(si)::value;
       constexpr int HH = decltype(hh)::value;
       if (k < 4) {
-        if constexpr (PACKED)
+        if constexpr (WIDE)
+          fa[S][k] = *reinterpret_cast<const u32x4*>(wbw(wi, wmc) + (wn * 4 + k) * kFragE + lane * 8);
+        else if constexpr (PACKED)
           fa[S][k] = *reinterpret_cast<const u32x4*>(wbufp(wi) + (wn * 4 + k) * kFragE + lane * 8);
         else
           fa[S][k] = *reinterpret_cast<const u32x4*>(wbufp(wi) + wrow + k * 16 * 64 + (HH ? tcol1 : tcol0));
       } else if (k - 4 < JV) {
-        const uint16_t* TL = tbufp(ti);
+        const uint16_t* TL = tsp(ti);
         fb[S][k - 4] = *reinterpret_cast<const u32x4*>(TL + trow + (k - 4) * 16 * 64 + (HH ? tcol1 : tcol0));
       }
     };
     // weights of step 0 and token stage 0 (row-major: stage 0 of both)
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(PACKED ? 10 : 12));
+    // (paired tile: 14, the prologue's later 4 + 4 + 2 + 4 loads)
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(WIDE ? 14 : PACKED ? 10 : 12));
     lds_barrier();
 #pragma unroll
     for (int k = 0; k < 12; ++k) rd(I0{}, I0{}, I0{}, I0{}, k);
@@ -349,7 +450,10 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
       // (row-major weights: step t+1 of an odd step t is stage (t+1)/2, whose
       // tokens went out in step t-2 before the weights of stage (t+3)/2 and
       // whose weights in step t-4; even steps need nothing new)
-      __builtin_amdgcn_s_waitcnt(vmcnt_le((T & 1) ? 4 : (PACKED ? 8 : 12)));
+      // (paired tile: 4 weight loads a step and 2 token loads in odd steps,
+      // so 8 and 10)
+      __builtin_amdgcn_s_waitcnt(
+          vmcnt_le((T & 1) ? (WIDE ? 8 : 4) : (WIDE ? 10 : PACKED ? 8 : 12)));
       lds_barrier();
       const int tw = min(t + 4, last);
       const int ts = min((t + 3) >> 1, last_stage);
@@ -368,7 +472,17 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
           unrolled([&](auto rm) {
             rd(WN{}, TN{}, HN{}, std::integral_constant<int, NXT>{}, order[3 * g + decltype(rm)::value]);
           }, std::make_integer_sequence<int, 3>{});
-          if constexpr (T & 1) {
+          if constexpr (WIDE) {
+            // odd steps: tokens of stage (t+3)/2, then both halves of step
+            // t+4's weights; even steps: both halves of step t+4's weights
+            using TB = std::integral_constant<int, ((T + 3) >> 1) & 1>;
+            if constexpr (T & 1) {
+              if constexpr (g == 0) { load_x(tsp(TB{}), 0, ts); load_x(tsp(TB{}), 1, ts); }
+              else if constexpr (g < 3) load_w2(tm, std::integral_constant<int, g - 1>{}, tw);
+            } else if constexpr (g < 2) {
+              load_w2(tm, std::integral_constant<int, g>{}, tw);
+            }
+          } else if constexpr (T & 1) {
             // tokens of stage (t+3)/2 into the buffer stage (t-1)/2 has left,
             // then the weights of step t+4 (row-major: of stage (t+5)/2, into
             // the buffer stage (t-1)/2 has left)
@@ -404,16 +518,17 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
     // register class for the allocator.
     // (SCALED: the row scales of the lane's 4 rows of a weight tile, read
     // where they are used; cache hits after the first token tile)
+    const int ntw = WIDE && WMC ? nt2 : nt;  // the wave's weight tile
     const float* rsa = SCALED ? sa + static_cast<size_t>(e) * N : nullptr;
     const float* rsb = SCALED ? sb + static_cast<size_t>(e) * N : nullptr;
 #pragma unroll
     for (int j = 0; j < JV; ++j) {
-      const int m = m0 + wm * 128 + j * 16 + fr;
+      const int m = m0 + (WIDE ? 0 : wm * 128) + j * 16 + fr;
       if (m >= M) continue;
       if constexpr (GATE_UP) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const int n = nt * 128 + wn * 32 + i * 16 + 4 * fg;
+          const int n = ntw * 128 + wn * 32 + i * 16 + 4 * fg;
           f32x4 gt = acc[i][j];
           f32x4 up = acc[i + 2][j];
           asm volatile("" : "+v"(gt), "+v"(up));
@@ -434,18 +549,33 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
           f32x4 v = acc[i][j];
           asm volatile("" : "+v"(v));
           if constexpr (SCALED)
-            v *= *reinterpret_cast<const f32x4*>(rsa + nt * 256 + wn * 64 + i * 16 + 4 * fg);
-          *reinterpret_cast<f32x4*>(y + nt * 256 + wn * 64 + i * 16 + 4 * fg) = v;
+            v *= *reinterpret_cast<const f32x4*>(rsa + ntw * 256 + wn * 64 + i * 16 + 4 * fg);
+          *reinterpret_cast<f32x4*>(y + ntw * 256 + wn * 64 + i * 16 + 4 * fg) = v;
         }
       }
     }
   };
+  auto run_wm = [&](auto jvc) {
+    if constexpr (WIDE) {
+      if (wm) run(jvc, I1{});
+      else run(jvc, I0{});
+    } else {
+      run(jvc, I0{});
+    }
+  };
   switch (jv) {
-    case 8: run(std::integral_constant<int, 8>{}); break;
-    case 6: run(std::integral_constant<int, 6>{}); break;
-    case 4: run(std::integral_constant<int, 4>{}); break;
-    case 2: run(std::integral_constant<int, 2>{}); break;
-    default: run(std::integral_constant<int, 0>{}); break;
+    case 8: run_wm(std::integral_constant<int, 8>{}); break;
+    case 6: run_wm(std::integral_constant<int, 6>{}); break;
+    case 4: run_wm(std::integral_constant<int, 4>{}); break;
+    case 2: run_wm(std::integral_constant<int, 2>{}); break;
+    default: run_wm(std::integral_constant<int, 0>{}); break;
+  }
+  };
+  if constexpr (PACKED && GATE_UP) {
+    if (nt2 >= 0) body(std::true_type{});
+    else body(std::false_type{});
+  } else {
+    body(std::false_type{});
   }
 }
 

@@ -9,7 +9,8 @@ is copied between register files inside the loop, nothing spills to scratch,
 and the only memory waits in the loop are the one per K step that the design
 calls for, together with the barrier's lgkmcnt(0): "vmcnt <= 4" in odd steps,
 and "<= 8" in even ones with fragment-order weights (4-step loop trips) or
-"<= 12" (no wait) with row-major weights (12-step loop trips).
+"<= 12" (no wait) with row-major weights (12-step loop trips); "<= 8" and
+"<= 10" in the loops of the paired last m-tiles (gate/up, fragment order).
 """
 import os
 import re
@@ -82,9 +83,15 @@ def test_loops_keep_accumulators_in_place(asm, kernel, layout):
     code = [c for n, c in _kernels(asm).items() if kernel + tag in n]
     assert len(code) == 1
     loops = _loops(code[0])
-    # one loop per token-fragment count the kernel is instantiated for (8, 6, 4, 2)
-    assert len(loops) == 4
+    # one loop per token-fragment count the kernel is instantiated for (8, 6,
+    # 4, 2); gate/up with fragment order adds the paired tile's loops, one per
+    # count and per half of the workgroup (its weight-half reads are constants)
+    paired = [b for b in loops if any("vmcnt(10)" in x for x in b)]
+    single = [b for b in loops if b not in paired]
+    assert len(single) == 4
+    assert len(paired) == (8 if tag.startswith("ILb1") and kernel.startswith("gate_up") else 0)
     for body in loops:
+        pair = body in paired
         mfma = [b.split() for b in body if "v_mfma" in b]
         # K steps x (4 x 8, 6, 4, 2) tiles
         assert len(mfma) in tuple(steps * 4 * j for j in (8, 6, 4, 2))
@@ -93,13 +100,17 @@ def test_loops_keep_accumulators_in_place(asm, kernel, layout):
         assert not [b for b in body if "accvgpr" in b]
         assert not [b for b in body if "scratch_" in b]
         waits = {re.sub(r"\s+", " ", b.strip()) for b in body if "s_waitcnt" in b}
-        even = f"vmcnt({even_wait})"
-        assert waits == {"s_waitcnt vmcnt(4) lgkmcnt(0)", f"s_waitcnt {even} lgkmcnt(0)"}, waits
-        assert sum("vmcnt(4)" in b for b in body) == steps // 2
+        # paired tile: 4 weight loads a step, 2 token loads in odd steps, so
+        # "<= 8" in odd steps and "<= 10" in even ones
+        odd, even = ("vmcnt(8)", "vmcnt(10)") if pair else ("vmcnt(4)", f"vmcnt({even_wait})")
+        assert waits == {f"s_waitcnt {odd} lgkmcnt(0)", f"s_waitcnt {even} lgkmcnt(0)"}, waits
+        assert sum(odd in b for b in body) == steps // 2
         assert sum(even in b for b in body) == steps // 2
         # per 4 K steps: fragment order, 2 weight loads each and 4 token loads in the two odd
-        # ones; row-major, 4 token and 4 weight loads in the two odd ones
-        assert sum("buffer_load_dwordx4" in b and " lds" in b for b in body) == 4 * steps
+        # ones (paired: 4 weight loads each, 2 token loads in the odd ones); row-major, 4 token
+        # and 4 weight loads in the two odd ones
+        loads = sum("buffer_load_dwordx4" in b and " lds" in b for b in body)
+        assert loads == (5 if pair else 4) * steps
 
 
 def test_kernels_have_no_scratch_and_two_waves_per_simd(asm):

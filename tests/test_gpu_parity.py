@@ -705,6 +705,43 @@ def test_prefill_tail_tiles(m, d, ffn, extra):
     assert rel_err(host(y_p), ref) <= OUT_TOL[gen.BF16]
 
 
+# last m-tiles of 45, 128 (the expert's only tile), 1, 128 and 144 rows and an
+# empty expert: all but the 144-row one are paired across two weight tiles
+PAIRED_COUNTS = [301, 128, 513, 640, 400, 0]
+
+
+@pytest.mark.parametrize("d,ffn", [(4096, 2048), (2048, 3072), (2048, 1024)])
+def test_prefill_paired_tail_tiles(m, d, ffn):
+    """Gate/up with fragment-order weights: an expert's last m-tile of at most
+    128 rows is computed for two of an XCD's weight tiles at once (512 weight
+    rows x 128 tokens). Shapes with one such pair per XCD (ffn = 2048), a pair
+    and one weight tile left over (ffn = 3072: 24 weight tiles, 3 per XCD),
+    and none (ffn = 1024: one weight tile per XCD); the down projection runs
+    its 256x256 tiles as usual. The row-major weights run every last m-tile
+    on its own, with the same MFMA sequence per output, so the two layouts
+    must agree bit for bit; both within the bf16 bar of the oracle."""
+    counts = PAIRED_COUNTS
+    E, k = len(counts), 2
+    A = sum(counts)
+    assert A % k == 0 and A >= 256 * E
+    inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=47 + d)
+    sasg = np.random.default_rng(48).permutation(A).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    print(f"[parity] paired tails d={d} ffn={ffn} A={A}", flush=True)
+    dev = to_device(inp)
+    o_t = torch.from_numpy(offs).cuda()
+    s_t = torch.from_numpy(sasg).cuda()
+    pw = m.PackedWeights(dev["w1"], dev["w3"], dev["w2"])
+    y_p = m.moe_expert_ffn(dev["x"], pw.w1, pw.w3, pw.w2, o_t, s_t, k, packed=True)
+    y_s = m.moe_expert_ffn(dev["x"], dev["w1"], dev["w3"], dev["w2"], o_t, s_t, k)
+    torch.cuda.synchronize()
+    assert torch.equal(y_p, y_s)
+    ref = oracle.expert_ffn(inp["x"], inp["w1"], inp["w3"], inp["w2"], offs, sasg, k)
+    err = rel_err(host(y_p), ref)
+    print(f"[parity]   max|err|/rms {err:.2e}", flush=True)
+    assert err <= OUT_TOL[gen.BF16]
+
+
 # ---------------------------------------------------------------- full size --
 FULL = ["decode_8x7b", "prefill_8x7b", "skew_8x7b", "prefill_8x22b"]
 # tokens the oracle certifies in the full-size workloads (float64 gaps below
