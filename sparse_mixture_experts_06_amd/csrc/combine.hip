@@ -6,9 +6,9 @@
 // so the result is deterministic and a token whose weights are unchanged
 // gives bit-identical output. Workgroup (t, c) handles columns
 // [c*1024, (c+1)*1024) of token t, 4 per thread with 16-byte accesses when
-// d % 4 == 0, so all of a thread's k*nsplit loads are in flight together. When the down projection left its result as nsplit
-// partial sums (split K), each y row is first summed over the splits in
-// split order. With a residual (the block's input, nnterp Mixtral page,
+// d % 4 == 0 (8 per thread, below, for the common shapes). When the down
+// projection left its result as nsplit partial sums (split K), each y row is
+// first summed over the splits in split order. With a residual (the block's input, nnterp Mixtral page,
 // "The Notes": out = h + mlp(post_attention_layernorm(h))), it is added to
 // the finished slot sum.
 #include "common.h"
@@ -81,6 +81,72 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
   }
 }
 
+// The common shapes (k = 1 or 2 slots, 1 or 2 partial sums, d % 8 == 0):
+// 8 columns per thread, every y load of the thread issued before the first
+// sum (k * nsplit * 2 loads of 16 bytes in flight), with the non-temporal
+// hint (y is read once); the same sums in the same order as above.
+template <bool OUT_BF16, int RES, int KT, int NS>
+__global__ __launch_bounds__(kThreads) void combine8_kernel(const float* __restrict__ y,
+                                                           int64_t pstride,
+                                                           const int32_t* __restrict__ asg_pos,
+                                                           const float* __restrict__ w, int d,
+                                                           void* __restrict__ out,
+                                                           const void* __restrict__ res) {
+  const int64_t t = blockIdx.x;
+  const int i = (blockIdx.y * kThreads + threadIdx.x) * 8;
+  if (i >= d) return;
+  f32x4 v[KT][NS][2];
+#pragma unroll
+  for (int j = 0; j < KT; ++j) {
+    const int64_t p = asg_pos[t * KT + j];
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        v[j][sp][hh] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(y + sp * pstride + p * d + i + 4 * hh));
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KT; ++j) {
+    const float wt = w[t * KT + j];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x4 sum = v[j][0][hh];
+#pragma unroll
+      for (int sp = 1; sp < NS; ++sp) sum += v[j][sp][hh];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[4 * hh + c] = fmaf(wt, sum[c], acc[4 * hh + c]);
+    }
+  }
+  if constexpr (RES == 1) {
+    const float* r = static_cast<const float*>(res) + t * d + i;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(r), b = *reinterpret_cast<const f32x4*>(r + 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc[c] += a[c];
+      acc[4 + c] += b[c];
+    }
+  } else if constexpr (RES == 2) {
+    const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(res) + t * d + i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc[2 * c] += __uint_as_float(r[c] << 16);
+      acc[2 * c + 1] += __uint_as_float(r[c] & 0xFFFF0000u);
+    }
+  }
+  if constexpr (OUT_BF16) {
+    u32x4 o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(acc[2 * c], acc[2 * c + 1]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + t * d + i) = o;
+  } else {
+    float* o = static_cast<float*>(out) + t * d + i;
+    *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void sum_partials_kernel(const float* __restrict__ part,
                                                                int nsplit, int64_t n,
                                                                float* __restrict__ y) {
@@ -95,10 +161,33 @@ __global__ __launch_bounds__(kThreads) void sum_partials_kernel(const float* __r
 }  // namespace
 
 namespace {
+template <bool OUT_BF16, int RES, int KT>
+void launch_combine8(const float* y, int nsplit, int64_t pstride, const int32_t* asg_pos,
+                     const float* w, int64_t T, int d, void* out, const void* res,
+                     hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>((d + kThreads * 8 - 1) / (kThreads * 8)));
+  if (nsplit == 1)
+    hipLaunchKernelGGL((combine8_kernel<OUT_BF16, RES, KT, 1>), grid, dim3(kThreads), 0, s, y,
+                       pstride, asg_pos, w, d, out, res);
+  else
+    hipLaunchKernelGGL((combine8_kernel<OUT_BF16, RES, KT, 2>), grid, dim3(kThreads), 0, s, y,
+                       pstride, asg_pos, w, d, out, res);
+}
+
 template <int RES>
 void launch_combine_res(const float* y, int nsplit, int64_t pstride, const int32_t* asg_pos,
                         const float* w, int64_t T, int d, int k, void* out, int out_bf16,
-                        bool vec, const void* res, hipStream_t s) {
+                        bool vec, bool vec8, const void* res, hipStream_t s) {
+  if (vec8 && (k == 1 || k == 2) && (nsplit == 1 || nsplit == 2)) {
+    if (out_bf16) {
+      if (k == 1) launch_combine8<true, RES, 1>(y, nsplit, pstride, asg_pos, w, T, d, out, res, s);
+      else launch_combine8<true, RES, 2>(y, nsplit, pstride, asg_pos, w, T, d, out, res, s);
+    } else {
+      if (k == 1) launch_combine8<false, RES, 1>(y, nsplit, pstride, asg_pos, w, T, d, out, res, s);
+      else launch_combine8<false, RES, 2>(y, nsplit, pstride, asg_pos, w, T, d, out, res, s);
+    }
+    return;
+  }
   const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>((d + kThreads * 4 - 1) / (kThreads * 4)));
   if (out_bf16) {
     if (vec)
@@ -126,12 +215,17 @@ hipError_t launch_combine(const float* y, int nsplit, const int32_t* asg_pos, co
   const auto aligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
   const bool vec = (d % 4 == 0) && aligned(y, 16) && aligned(out, out_bf16 ? 8 : 16) &&
                    (!residual || aligned(residual, res_bf16 ? 8 : 16));
+  const bool vec8 = (d % 8 == 0) && aligned(y, 16) && aligned(out, 16) &&
+                    (!residual || aligned(residual, 16));
   if (!residual)
-    launch_combine_res<0>(y, nsplit, pstride, asg_pos, w, T, d, k, out, out_bf16, vec, nullptr, s);
+    launch_combine_res<0>(y, nsplit, pstride, asg_pos, w, T, d, k, out, out_bf16, vec, vec8,
+                          nullptr, s);
   else if (res_bf16)
-    launch_combine_res<2>(y, nsplit, pstride, asg_pos, w, T, d, k, out, out_bf16, vec, residual, s);
+    launch_combine_res<2>(y, nsplit, pstride, asg_pos, w, T, d, k, out, out_bf16, vec, vec8,
+                          residual, s);
   else
-    launch_combine_res<1>(y, nsplit, pstride, asg_pos, w, T, d, k, out, out_bf16, vec, residual, s);
+    launch_combine_res<1>(y, nsplit, pstride, asg_pos, w, T, d, k, out, out_bf16, vec, vec8,
+                          residual, s);
   return hipGetLastError();
 }
 

@@ -375,11 +375,13 @@ __global__ __launch_bounds__(kWave* kMfmaWaves, 1) void route_mfma_kernel(
   const int t = lane & 15, q = lane >> 4;
   const int64_t row = min(t0 + t, T - 1);  // rows past the batch read the last row
   const uint16_t* xp = x + row * d + 8 * q;
+  // lanes of experts >= E load nothing (zeros; those sums are unused)
   const float* rp[NT];
+  bool ev[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int e = min(16 * nt + t, E - 1);  // experts >= E read a valid row, unused
-    rp[nt] = router + static_cast<int64_t>(e) * d + 8 * q;
+    ev[nt] = 16 * nt + t < E;
+    rp[nt] = router + static_cast<int64_t>(min(16 * nt + t, E - 1)) * d + 8 * q;
   }
   f32x4 acc[NT];
 #pragma unroll
@@ -393,8 +395,11 @@ __global__ __launch_bounds__(kWave* kMfmaWaves, 1) void route_mfma_kernel(
       xv[u] = ldg16(xp + (st + u) * 32);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        ra[u][nt] = *reinterpret_cast<const float4*>(rp[nt] + (st + u) * 32);
-        rb[u][nt] = *reinterpret_cast<const float4*>(rp[nt] + (st + u) * 32 + 4);
+        ra[u][nt] = rb[u][nt] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ev[nt]) {
+          ra[u][nt] = *reinterpret_cast<const float4*>(rp[nt] + (st + u) * 32);
+          rb[u][nt] = *reinterpret_cast<const float4*>(rp[nt] + (st + u) * 32 + 4);
+        }
       }
     }
 #pragma unroll
