@@ -229,14 +229,15 @@ def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
         raise SystemExit("calibration copy or gate/up kernel not found in the counter files")
     f_factor = f_cal[-1] / calib
     w_factor = w_cal[-1] / calib
-    fetch = sum(f_gu) / len(f_gu) / f_factor * 1024
-    write = sum(w_gu) / len(w_gu) / w_factor * 1024
+    # (whole bytes each; the total is their sum)
+    fetch = int(sum(f_gu) / len(f_gu) / f_factor * 1024)
+    write = int(sum(w_gu) / len(w_gu) / w_factor * 1024)
     down = None
     if f_dn and w_dn:
-        dfetch = sum(f_dn) / len(f_dn) / f_factor * 1024
-        dwrite = sum(w_dn) / len(w_dn) / w_factor * 1024
-        down = {"hbm_bytes_per_launch": int(dfetch + dwrite), "fetch_bytes": int(dfetch),
-                "write_bytes": int(dwrite), "dispatches": len(f_dn)}
+        dfetch = int(sum(f_dn) / len(f_dn) / f_factor * 1024)
+        dwrite = int(sum(w_dn) / len(w_dn) / w_factor * 1024)
+        down = {"hbm_bytes_per_launch": dfetch + dwrite, "fetch_bytes": dfetch,
+                "write_bytes": dwrite, "dispatches": len(f_dn)}
     sha = ffn_sources_sha()
     try:
         with open(TRAFFIC_FILE) as f:
@@ -247,8 +248,8 @@ def pmc_summary(workload, fetch_csv, write_csv, calib_mib):
         rec = {}
     rec["ffn_sources_sha256"] = sha
     rec.setdefault("workloads", {})[workload] = {
-        "hbm_bytes_per_launch": int(fetch + write), "fetch_bytes": int(fetch),
-        "write_bytes": int(write), "fetch_counter_per_byte": round(f_factor, 5),
+        "hbm_bytes_per_launch": fetch + write, "fetch_bytes": fetch,
+        "write_bytes": write, "fetch_counter_per_byte": round(f_factor, 5),
         "write_counter_per_byte": round(w_factor, 5), "dispatches": len(f_gu),
         "calibration": f"one {calib_mib} MiB device-to-device copy"}
     if down is not None:
