@@ -44,11 +44,13 @@
  *   MOE_EWORKSPACE nothing ran. MOE_EHIP means the HIP runtime rejected a
  *   launch (the stream state is then the runtime's). No C++ exception and no
  *   abort crosses this boundary.
- * Device-side preconditions (not checked): expert ids in [0, E) and distinct
- *   within a token; offsets, sorted_asg and asg_pos exactly as moe_permute
- *   produces them for the same T, k and E. moe_permute ignores expert ids
- *   out of range; any other violation gives unspecified results and may
- *   read or write out of bounds.
+ * Device-side preconditions: expert ids in [0, E) and distinct within a
+ *   token (moe_check_routing counts the tokens that break either, on the
+ *   device); offsets, sorted_asg and asg_pos exactly as moe_permute produces
+ *   them for the same T, k and E. moe_permute leaves expert ids out of range
+ *   out of the grouping (asg_pos -1, which moe_combine skips); a repeated id
+ *   is grouped twice like any other. Arrays that moe_permute did not produce
+ *   give unspecified results and may be read or written out of bounds.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -136,11 +138,24 @@ int moe_route(const void* x, int x_dtype, const float* router, const float* logi
  *   sorted_asg [T*k]  assignment ids a = t*k + j grouped by expert; within an
  *                     expert in increasing a (a stable counting sort)
  *   asg_pos    [T*k]  inverse: sorted_asg[asg_pos[a]] == a
+ * An expert id outside [0, E) is not counted and gets asg_pos -1; offsets[E]
+ * is then the number of assignments grouped, and sorted_asg past it is left
+ * as it was.
  * ws/ws_bytes: reserved scratch; the current kernel needs none, so NULL/0
  * is accepted (any buffer passed is left untouched). */
 int moe_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts,
                 int32_t* offsets, int32_t* sorted_asg, int32_t* asg_pos, void* ws,
                 size_t ws_bytes, void* stream);
+
+/* Routing check for callers that pass their own expert ids to moe_permute
+ * (a debugging aid; the router's own ids always pass). On the stream, writes
+ * bad_out[0] = the number of tokens with an id outside [0, E) and bad_out[1]
+ * = the number of tokens with an id repeated (a token is dispatched to k
+ * distinct experts: Transformers page, "Architectural details"). topk_idx
+ * [T, k] int32 device; bad_out int32[2] device. Same size checks as
+ * moe_permute; T == 0 writes zeros. */
+int moe_check_routing(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* bad_out,
+                      void* stream);
 
 /* The experts on their grouped rows (nnterp page, support(): the down
  * projection receives act(gate) * up, act = SiLU):
@@ -166,7 +181,8 @@ int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, con
  *   out[t] = sum_{j=0..k-1} topk_w[t*k+j] * y[asg_pos[t*k+j]]
  * accumulated in float32 in slot order; out [T, d] float32 or bfloat16
  * (round to nearest even). topk_w may be any caller array (e.g. with a slot
- * zeroed to ablate an expert). */
+ * zeroed to ablate an expert). Slots with asg_pos < 0 (ids moe_permute left
+ * out) are skipped. */
 int moe_combine(const float* y, const int32_t* asg_pos, const float* topk_w, int64_t T, int d,
                 int k, void* out, int out_dtype, void* stream);
 

@@ -43,6 +43,7 @@ _SIGNATURES = {
     "moe_route": (_c_int, [_vp, _c_int, _vp, _vp, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _vp,
                            _vp]),
     "moe_permute": (_c_int, [_vp, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
+    "moe_check_routing": (_c_int, [_vp, _c_i64, _c_int, _c_int, _vp, _vp]),
     "moe_expert_ffn": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _c_int,
                                 _c_int, _c_int, _vp, _vp, _c_sz, _vp, _opts_p]),
     "moe_combine": (_c_int, [_vp, _vp, _vp, _c_i64, _c_int, _c_int, _vp, _c_int, _vp]),
@@ -311,6 +312,19 @@ def moe_permute(topk_idx, E: int, counts=None, offsets=None, sorted_asg=None, as
                             _ptr(sorted_asg), _ptr(asg_pos), None, 0, _stream(dev))
     _check("moe_permute", st)
     return counts, offsets, sorted_asg, asg_pos
+
+
+def moe_check_routing(topk_idx, E: int, bad=None):
+    """Returns bad [2] int32 on the device: tokens with an expert id outside
+    [0, E), tokens with a repeated id."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    bad = torch.empty(2, dtype=torch.int32, device=dev) if bad is None else bad
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(bad, "bad", torch.int32, (2,), dev)
+    st = load().moe_check_routing(_ptr(topk_idx), T, E, k, _ptr(bad), _stream(dev))
+    _check("moe_check_routing", st)
+    return bad
 
 
 def moe_expert_ffn(x, w1, w3, w2, offsets, sorted_asg, k: int, y=None, ws=None, packed=False,

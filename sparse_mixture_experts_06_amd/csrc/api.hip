@@ -254,6 +254,15 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* count
                                         asg_pos, static_cast<hipStream_t>(stream)));
 }
 
+int moe_check_routing(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* bad_out,
+                      void* stream) {
+  const int st = check_sizes(T, E, k);
+  if (st != MOE_OK) return st;
+  if (!bad_out || (T > 0 && !topk_idx)) return MOE_EINVAL;
+  return hip_status(moe::launch_check_routing(topk_idx, T, k, E, bad_out,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
                    const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d,
                    int ffn, int E, int k, float* y, void* ws, size_t ws_bytes, void* stream,

@@ -4,7 +4,8 @@
 //   out[t] = sum_{j<k} w[t*k+j] * y[asg_pos[t*k+j]]
 // A gather, not a scatter: no atomics, float32 accumulation in slot order,
 // so the result is deterministic and a token whose weights are unchanged
-// gives bit-identical output. Workgroup (t, c) handles columns
+// gives bit-identical output. A slot whose asg_pos is negative (an expert id
+// the grouping left out) adds nothing. Workgroup (t, c) handles columns
 // [c*1024, (c+1)*1024) of token t, 4 per thread with 16-byte accesses when
 // d % 4 == 0 (8 per thread, below, for the common shapes). When the down
 // projection left its result as nsplit partial sums (split K), each y row is
@@ -34,6 +35,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int j = 0; j < k; ++j) {
         const int64_t p = asg_pos[t * k + j];
+        if (p < 0) continue;  // an assignment the grouping left out
         const float wt = w[t * k + j];
         f32x4 v = *reinterpret_cast<const f32x4*>(y + p * d + i);
         for (int sp = 1; sp < nsplit; ++sp)
@@ -66,6 +68,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
       float acc = 0.0f;
       for (int j = 0; j < k; ++j) {
         const int64_t p = asg_pos[t * k + j];
+        if (p < 0) continue;
         float v = y[p * d + i];
         for (int sp = 1; sp < nsplit; ++sp) v += y[sp * pstride + p * d + i];
         acc = fmaf(w[t * k + j], v, acc);
@@ -96,19 +99,22 @@ __global__ __launch_bounds__(kThreads) void combine8_kernel(const float* __restr
   const int i = (blockIdx.y * kThreads + threadIdx.x) * 8;
   if (i >= d) return;
   f32x4 v[KT][NS][2];
+  int64_t p[KT];
 #pragma unroll
   for (int j = 0; j < KT; ++j) {
-    const int64_t p = asg_pos[t * KT + j];
+    p[j] = asg_pos[t * KT + j];
+    const int64_t pj = p[j] < 0 ? 0 : p[j];  // (a slot left out reads row 0, unused)
 #pragma unroll
     for (int sp = 0; sp < NS; ++sp)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
         v[j][sp][hh] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(y + sp * pstride + p * d + i + 4 * hh));
+            reinterpret_cast<const f32x4*>(y + sp * pstride + pj * d + i + 4 * hh));
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < KT; ++j) {
+    if (p[j] < 0) continue;
     const float wt = w[t * KT + j];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {

@@ -115,6 +115,8 @@ hipError_t launch_route(const void* x, int x_bf16, const float* router, const fl
                         float* w, hipStream_t s, const float* gamma = nullptr, float eps = 0.0f,
                         void* norm_out = nullptr);
 
+hipError_t launch_check_routing(const int32_t* idx, int64_t T, int k, int E, int32_t* bad,
+                                hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int64_t A, int E, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_asg, int32_t* asg_pos,
                           hipStream_t s);

@@ -25,7 +25,9 @@
 // an expert the assignments keep their order (a stable sort). Each walk
 // loads 8 steps of ids at a time, all in flight before the first is used.
 // Two barriers (after zeroing the counts, one more). Expert ids outside
-// [0, E) are ignored (no out-of-bounds access).
+// [0, E) take no place in the grouping: they are not counted, and their
+// asg_pos entry is -1 (which the combine skips), so a bad id never leads to
+// an access out of bounds.
 #include "common.h"
 
 namespace moe {
@@ -117,12 +119,64 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
         sorted_asg[pos] = a;
         asg_pos[a] = pos;
         if (below == 0) s_pos[wave][ev[u]] = pos + __popcll(m);
+      } else if (a < hi) {
+        asg_pos[a] = -1;
       }
     }
   }
 }
 
+// Routing check (a debugging aid for callers that pass their own expert ids):
+// bad[0] = tokens with an id outside [0, E), bad[1] = tokens whose ids repeat
+// one (a token goes to k distinct experts). One workgroup strides over the
+// tokens; the per-thread counts are summed in LDS, so the result is exact and
+// needs no zeroed output.
+__global__ __launch_bounds__(kThreads) void check_routing_kernel(const int32_t* __restrict__ idx,
+                                                                 int64_t T, int k, int E,
+                                                                 int32_t* __restrict__ bad) {
+  __shared__ int s_bad[2][kWaves];
+  const int tid = threadIdx.x;
+  int out_of_range = 0, repeated = 0;
+  for (int64_t t = tid; t < T; t += kThreads) {
+    uint32_t seen = 0;
+    bool oor = false, rep = false;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e < 0 || e >= E) {
+        oor = true;
+      } else {
+        rep = rep || ((seen >> e) & 1u);
+        seen |= 1u << e;
+      }
+    }
+    out_of_range += oor;
+    repeated += rep;
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    out_of_range += __shfl_xor(out_of_range, o, kWave);
+    repeated += __shfl_xor(repeated, o, kWave);
+  }
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  if (lane == 0) {
+    s_bad[0][wave] = out_of_range;
+    s_bad[1][wave] = repeated;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    int sum = 0;
+    for (int w = 0; w < kWaves; ++w) sum += s_bad[tid][w];
+    bad[tid] = sum;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_check_routing(const int32_t* idx, int64_t T, int k, int E, int32_t* bad,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(check_routing_kernel, dim3(1), dim3(kThreads), 0, s, idx, T, k, E, bad);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const int32_t* idx, int64_t A, int E, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_asg, int32_t* asg_pos,

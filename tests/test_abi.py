@@ -86,6 +86,12 @@ def test_permute_rejects_bad_arguments():
     assert p(None, 4, 8, 2, BAD, BAD, BAD, BAD, None, 0, None) == moe.MOE_EINVAL   # null idx
     assert p(BAD, 4, 8, 0, BAD, BAD, BAD, BAD, None, 0, None) == moe.MOE_EINVAL    # k < 1
     assert p(BAD, 2 ** 31, 8, 2, BAD, BAD, BAD, BAD, None, 0, None) == moe.MOE_EINVAL  # T*k >= 2^31
+    chk = lib.moe_check_routing
+    assert chk(BAD, 4, 8, 2, None, None) == moe.MOE_EINVAL      # null bad_out
+    assert chk(None, 4, 8, 2, BAD, None) == moe.MOE_EINVAL      # null ids
+    assert chk(BAD, 4, 33, 2, BAD, None) == moe.MOE_EINVAL      # E > 32
+    assert chk(BAD, 4, 8, 9, BAD, None) == moe.MOE_EINVAL       # k > E
+    assert chk(BAD, -1, 8, 2, BAD, None) == moe.MOE_EINVAL      # T < 0
 
 
 def test_expert_ffn_rejects_bad_arguments():

@@ -622,6 +622,57 @@ def test_crafted_near_and_order_ties(m, dtype, kind, T):
     check_permutation(idx_g, 8, host(c), host(o), host(sa), host(ap))
 
 
+def test_routing_check_and_ids_left_out(m):
+    """Caller-made expert ids: moe_check_routing counts the tokens with an id
+    outside [0, E) and those with a repeated id; moe_permute groups only the
+    ids in range (a stable counting sort of them, a repeat grouped twice) and
+    gives the others asg_pos -1; moe_combine skips those slots, so each
+    token's output is the weighted sum over its grouped slots in slot order."""
+    T, k, E, d = 1000, 2, 8, 96
+    rng = np.random.default_rng(90)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    idx[rng.choice(T, 37, replace=False), 1] = E          # out of range (high)
+    idx[rng.choice(T, 11, replace=False), 0] = -3         # out of range (negative)
+    rep_rows = rng.choice(T, 23, replace=False)
+    idx[rep_rows, 1] = idx[rep_rows, 0]                    # repeats (where both in range)
+    oor = ((idx < 0) | (idx >= E)).any(axis=1)
+    repeated = np.array([len(set(r[(r >= 0) & (r < E)])) < ((r >= 0) & (r < E)).sum() for r in idx])
+    idx_d = torch.from_numpy(idx).cuda()
+    print(f"[parity] routing check: {int(oor.sum())} out of range, {int(repeated.sum())} repeated",
+          flush=True)
+    bad = m.moe_check_routing(idx_d, E)
+    clean = m.moe_check_routing(idx_d.clamp(0, E - 1)[:, :1].contiguous(), E)
+    empty = m.moe_check_routing(idx_d[:0], E)
+    counts, offsets, sorted_asg, asg_pos = m.moe_permute(idx_d, E)
+    torch.cuda.synchronize()
+    assert host(bad).tolist() == [int(oor.sum()), int(repeated.sum())]
+    assert host(clean).tolist() == [0, 0] and host(empty).tolist() == [0, 0]
+    flat = idx.ravel()
+    ok = (flat >= 0) & (flat < E)
+    kept = np.nonzero(ok)[0]
+    order = kept[np.argsort(flat[kept], kind="stable")]
+    n = order.size
+    assert np.array_equal(host(counts), np.bincount(flat[kept], minlength=E))
+    assert host(offsets)[-1] == n
+    assert np.array_equal(host(offsets), np.concatenate([[0], np.cumsum(host(counts))]))
+    assert np.array_equal(host(sorted_asg)[:n], order)
+    pos = host(asg_pos)
+    assert np.all(pos[~ok] == -1)
+    assert np.array_equal(pos[order], np.arange(n))
+    # the combine on made-up expert outputs: slots left out add nothing
+    y = rng.standard_normal((T * k, d)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    out = m.moe_combine(torch.from_numpy(y).cuda(), asg_pos, torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    ref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            pj = pos[t * k + j]
+            if pj >= 0:
+                ref[t] += np.float64(w[t, j]) * y[pj]
+    assert rel_err(host(out), ref) <= 1e-6
+
+
 def test_empty_batch_and_zero_counts(m):
     inp = gen.make_inputs(T=0, d=64, ffn=64, E=8, k=2, dtype=gen.BF16, seed=43)
     dev = to_device(inp)
