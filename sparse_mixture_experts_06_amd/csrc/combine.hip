@@ -86,8 +86,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
 
 // The common shapes (k = 1 or 2 slots, 1 or 2 partial sums, d % 8 == 0):
 // 8 columns per thread, every y load of the thread issued before the first
-// sum (k * nsplit * 2 loads of 16 bytes in flight), with the non-temporal
-// hint (y is read once); the same sums in the same order as above.
+// sum (k * nsplit * 2 loads of 16 bytes in flight); the same sums in the same
+// order as above. (Plain loads: the non-temporal hint measured 2 us slower at
+// 8x7B prefill, where part of y is still in the Infinity Cache.)
 template <bool OUT_BF16, int RES, int KT, int NS>
 __global__ __launch_bounds__(kThreads) void combine8_kernel(const float* __restrict__ y,
                                                            int64_t pstride,
@@ -108,8 +109,7 @@ __global__ __launch_bounds__(kThreads) void combine8_kernel(const float* __restr
     for (int sp = 0; sp < NS; ++sp)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        v[j][sp][hh] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(y + sp * pstride + pj * d + i + 4 * hh));
+        v[j][sp][hh] = *reinterpret_cast<const f32x4*>(y + sp * pstride + pj * d + i + 4 * hh);
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll

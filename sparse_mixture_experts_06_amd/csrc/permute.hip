@@ -23,7 +23,9 @@
 //      the speaking lane then advances the running position.
 // Slices, steps and lanes are all in increasing assignment order, so within
 // an expert the assignments keep their order (a stable sort). Each walk
-// loads 8 steps of ids at a time, all in flight before the first is used.
+// loads 8 steps of ids at a time, all in flight before the first is used;
+// when a wave's slice is one such batch (A <= 8192), the second walk reuses
+// the ids the first loaded.
 // Two barriers (after zeroing the counts, one more). Expert ids outside
 // [0, E) take no place in the grouping: they are not counted, and their
 // asg_pos entry is -1 (which the combine skips), so a bad id never leads to
@@ -70,12 +72,17 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
   const int per = ((A + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
   const int lo = min(A, wave * per), hi = min(A, lo + per);
 
+  // a slice of at most one batch (A <= 8192) keeps its ids in registers for
+  // the second walk
+  const bool one_batch = hi - lo <= kSteps * kWave;
+  int ev0[kSteps];
   for (int c0 = lo; c0 < hi; c0 += kSteps * kWave) {
     int ev[kSteps];
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       const int a = c0 + u * kWave + lane;
       ev[u] = a < hi ? idx[a] : -1;
+      ev0[u] = ev[u];
     }
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
@@ -106,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       const int a = c0 + u * kWave + lane;
-      ev[u] = a < hi ? idx[a] : -1;
+      ev[u] = one_batch ? ev0[u] : a < hi ? idx[a] : -1;
     }
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
