@@ -9,9 +9,9 @@ untimed steps run first, then exactly K steps are timed between two device
 synchronisations. Consecutive steps alternate between two copies of the
 expert weights, so no step can find the previous step's weights in the
 256 MB Infinity Cache. Per-kernel times come from HIP events the library
-records on its stream between the stages, on every 4th timed step (an event
+records on its stream between the stages, on every 8th timed step (an event
 record leaves the GPU idle for a few microseconds, so recording them on every
-step would slow the decode step by about 5%).
+step would slow the decode step by about 5%, on every 4th by about 1%).
 
 bf16 expert weights are timed in both layouts: fragment order
 (moe_pack_weight, run once when the weights are loaded, outside the timed
@@ -49,7 +49,7 @@ METRIC = ("MoE-layer tokens/sec at 1 GPU; % of HBM BW peak (decode) / bf16 MFMA 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 STAGES = ("route", "permute", "gate_up", "down", "combine")
-EVENT_EVERY = 4  # timed steps between two steps that record the per-stage HIP events
+EVENT_EVERY = 8  # timed steps between two steps that record the per-stage HIP events
 # the gate/up kernels' sources: traffic counters are only reported while they are unchanged
 FFN_SOURCES = [os.path.join(ROOT, "sparse_mixture_experts_06_amd", "csrc", f)
                for f in ("ffn_bf16.hip", "ffn_dma.hip", "ffn_int8.hip", "common.h")]
