@@ -76,8 +76,9 @@
 // of an XCD share one: 512 weight rows x 128 token rows, each wave the same 64
 // x 128 block as in a 256x256 tile. 8x7B prefill: 4032 -> 3808 tiles, gate/up
 // 1574 -> 1497-1544 us; 8x22B 1510 -> 1458 us. The down projection keeps its own
-// last m-tiles (paired, they ran 2-3% slower there: its tiles are few and
-// long, and the K split already fills the last round).
+// last m-tiles: there they cost about half a full tile (leaving out those of at
+// most 64 rows took only 6% off), less than a paired tile's share, and paired
+// they ran 2-3% slower.
 //
 // Every output element is one float32 MFMA accumulation over its K range in
 // increasing K, 32 at a time: the order of the 128-row tiled kernels, whose
