@@ -328,7 +328,8 @@ BOTH = [8208, 8442]  # two experts, A just above 8192 E: w1 and w3 widened too
 
 
 @pytest.mark.parametrize("d,ffn,counts,wide", [(256, 512, MANY, 1), (384, 640, MANY, 0),
-                                               (256, 512, DOWN_ONLY, 1), (256, 512, BOTH, 2)])
+                                               (256, 512, DOWN_ONLY, 1), (256, 512, BOTH, 2),
+                                               (256, 2048, BOTH, 2)])
 def test_int8_prefill_matches_oracle(m, d, ffn, counts, wide):
     """int8 weights at large prefill sizes: the codes of w2 are widened to bf16
     in fragment order in the workspace from A >= 1024 E, those of w1 and w3
@@ -340,7 +341,9 @@ def test_int8_prefill_matches_oracle(m, d, ffn, counts, wide):
     384 nothing is widened: down stays on the streaming int8 kernel (the tile
     kernels need d % 256 == 0); at d = 256, ffn = 512 down splits K in two.
     DOWN_ONLY sits exactly on the threshold of w2, BOTH (two experts) just
-    above that of w1 and w3."""
+    above that of w1 and w3; with ffn = 2048 (16 gate/up weight tiles, two
+    per XCD) the first expert's last m-tile (16 rows) is computed for both
+    weight tiles of an XCD at once, with the row scales of each."""
     E, k = len(counts), 2
     A = sum(counts)
     inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=60 + d)
