@@ -528,10 +528,11 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
     const int ntw = WIDE && WMC ? nt2 : nt;  // the wave's weight tile
     const float* rsa = SCALED ? sa + static_cast<size_t>(e) * N : nullptr;
     const float* rsb = SCALED ? sb + static_cast<size_t>(e) * N : nullptr;
-    if constexpr (PACKED && GATE_UP) {
-      // h through LDS, then whole rows to global memory: each store
-      // instruction writes 1 KiB of whole 128-byte lines instead of 16 pieces
-      // of 32 bytes (8x7B prefill: 2.378 -> 2.367 ms per layer).
+    if constexpr (GATE_UP) {
+      // h through LDS, then whole rows to global memory, for both weight
+      // layouts: each store instruction writes 1 KiB of whole 128-byte lines
+      // instead of 16 pieces of 32 bytes (8x7B prefill, fragment order: 2.378
+      // -> 2.367 ms per layer).
       // tb0 and tb1 are free once every load has landed (the last steps'
       // loads only repeat the last step's data: they are waited for here) and
       // every wave is past its last fragment read (the barrier). Staged tile:
