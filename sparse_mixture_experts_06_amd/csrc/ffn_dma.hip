@@ -136,8 +136,6 @@ __device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offse
   nt2 = -1;
   if ((ntn & 7) == 0) {
     const int nnx = ntn >> 3;  // weight tiles of each XCD
-    // pairs of the XCD's weight tiles (2g, 2g+1) whose last m-tiles share one
-    // tile when those hold at most DT/2 rows
     // the XCD's weight tiles in pairs (2g, 2g+1); an odd one left over last
     const int pairs = nnx >> 1;
     for (int s = 0; s < nsplit; ++s) {
