@@ -99,10 +99,19 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_BF16_PACKED = 2, MOE_INT8_PACKED
  *                 router, events[1] after it, then events[2..5] after the
  *                 permutation, the gate/up step, the down step and the
  *                 combine, all on their stream (a NULL entry is MOE_EINVAL).
- *                 moe_expert_ffn ignores it. */
+ *                 moe_expert_ffn ignores it.
+ *   down_split    K split of the down projection where the 256x256-tile
+ *                 kernel runs with room for two partial sums (bf16 and int8
+ *                 weights at prefill sizes; other kernels ignore it): 0 =
+ *                 chosen on the device from the expert counts (default), -1 =
+ *                 never split, 8..13 = a first part of that many sixteenths
+ *                 of K (rounded down to a multiple of 128 columns). Other
+ *                 values are MOE_EINVAL. Every choice is correct; they differ
+ *                 in speed and in float32 summation order. */
 typedef struct moe_options {
   int ffn_variant;
   void* const* stage_events;
+  int down_split;
 } moe_options;
 
 /* Static description of a status code. Never NULL. */
@@ -167,10 +176,11 @@ int moe_check_routing(const int32_t* topk_idx, int64_t T, int E, int k, int32_t*
  * down projection's MFMA input) and the down projection accumulates in
  * float32 (on few rows per expert, and on many where it packs the tiles
  * better onto the GPU, it splits K two ways and adds the two float32 partial
- * sums in a fixed order; the split depends on T, d, ffn, E and k only, so
- * MOE_BF16 and MOE_BF16_PACKED give bit-identical y). ws must hold
- * moe_workspace_bytes(T, d, ffn, E, k, dtype) bytes. options: NULL or
- * per-call options (the kernel family). */
+ * sums in a fixed order; the split depends on T, d, ffn, E, k, the per-expert
+ * row counts and options->down_split only, so MOE_BF16 and MOE_BF16_PACKED
+ * give bit-identical y). ws must hold moe_workspace_bytes(T, d, ffn, E, k,
+ * dtype) bytes. options: NULL or per-call options (kernel family, down
+ * split). */
 int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
                    const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d,
                    int ffn, int E, int k, float* y, void* ws, size_t ws_bytes, void* stream,
@@ -190,7 +200,7 @@ int moe_combine(const float* y, const int32_t* asg_pos, const float* topk_w, int
  * in one call on one stream. topk_idx_out [T,k], topk_w_out [T,k] and
  * counts_out [E] are optional (NULL) copies of the routing; logit_bias may be
  * NULL. ws must hold moe_workspace_bytes(T, d, ffn, E, k, dtype) bytes.
- * options: NULL or per-call options (kernel family, stage events). */
+ * options: NULL or per-call options (kernel family, stage events, down split). */
 int moe_forward(const void* x, int dtype, const float* router, const float* logit_bias,
                 const void* w1, const void* w3, const void* w2, int64_t T, int d, int ffn,
                 int E, int k, void* out, int out_dtype, int32_t* topk_idx_out,

@@ -31,8 +31,10 @@ _vp = ctypes.c_void_p
 
 
 class MoeOptions(ctypes.Structure):
-    """struct moe_options (include/moe.h): per-call kernel family and stage events."""
-    _fields_ = [("ffn_variant", ctypes.c_int), ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+    """struct moe_options (include/moe.h): per-call kernel family, stage events
+    and down-projection K split."""
+    _fields_ = [("ffn_variant", ctypes.c_int), ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+                ("down_split", ctypes.c_int)]
 
 
 _opts_p = ctypes.POINTER(MoeOptions)
@@ -133,13 +135,14 @@ def _weight_code(t: torch.dtype, packed: bool, w1, w3, w2) -> int:
     return code
 
 
-def _options(variant: int = 0, events=None):
+def _options(variant: int = 0, events=None, down_split: int = 0):
     """A moe_options for one call (None when everything is at its default).
     The returned object keeps the event array alive for the call."""
-    if not variant and not events:
+    if not variant and not events and not down_split:
         return None
     opts = MoeOptions()
     opts.ffn_variant = int(variant)
+    opts.down_split = int(down_split)
     if events:
         if len(events) != 6:
             raise ValueError("stage events: a sequence of 6 hipEvent_t handles")
@@ -328,10 +331,12 @@ def moe_check_routing(topk_idx, E: int, bad=None):
 
 
 def moe_expert_ffn(x, w1, w3, w2, offsets, sorted_asg, k: int, y=None, ws=None, packed=False,
-                   variant: int = 0):
+                   variant: int = 0, down_split: int = 0):
     """Returns y [T*k, d] float32 (unweighted expert outputs, grouped order).
     packed=True: w1/w3/w2 come from moe_pack_weight. variant: the expert-FFN
-    kernel family (0 = by size, 1 = streaming, 2 = tiled)."""
+    kernel family (0 = by size, 1 = streaming, 2 = tiled). down_split: the
+    down projection's K split where the 256x256-tile kernel runs (0 = chosen
+    on the device, -1 = none, 8..13 = first part of that many sixteenths)."""
     T, d = x.shape
     E, ffn, _ = w1.shape
     dev = x.device
@@ -347,7 +352,8 @@ def moe_expert_ffn(x, w1, w3, w2, offsets, sorted_asg, k: int, y=None, ws=None, 
         ws = workspace(T, d, ffn, E, k, code, dev)
     st = load().moe_expert_ffn(_ptr(x), code, _ptr(w1), _ptr(w3), _ptr(w2),
                                _ptr(offsets), _ptr(sorted_asg), T, d, ffn, E, k, _ptr(y),
-                               _ptr(ws), ws.numel(), _stream(dev), _options(variant))
+                               _ptr(ws), ws.numel(), _stream(dev),
+                               _options(variant, down_split=down_split))
     _check("moe_expert_ffn", st)
     return y
 
@@ -371,10 +377,11 @@ def moe_combine(y, asg_pos, topk_w, out=None, out_dtype=torch.float32):
 
 def moe_forward(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dtype=None,
                 ws=None, topk_idx_out=None, topk_w_out=None, counts_out=None, packed=False,
-                variant: int = 0, events=None):
+                variant: int = 0, events=None, down_split: int = 0):
     """The whole layer; returns out [T, d] (dtype out_dtype, default x.dtype).
     packed=True: w1/w3/w2 come from moe_pack_weight. variant: the expert-FFN
-    kernel family; events: 6 hipEvent_t handles recorded between the stages."""
+    kernel family; events: 6 hipEvent_t handles recorded between the stages;
+    down_split: as for moe_expert_ffn."""
     T, d = x.shape
     E, ffn, _ = w1.shape
     dev = x.device
@@ -399,7 +406,7 @@ def moe_forward(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dt
                             _ptr(w1), _ptr(w3), _ptr(w2), T, d, ffn, E, k, _ptr(out),
                             _dtype_code(out.dtype), _ptr(topk_idx_out), _ptr(topk_w_out),
                             _ptr(counts_out), _ptr(ws), ws.numel(), _stream(dev),
-                            _options(variant, events))
+                            _options(variant, events, down_split))
     _check("moe_forward", st)
     return out
 
@@ -407,7 +414,7 @@ def moe_forward(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dt
 def moe_block_forward(hidden, norm_weight, router, w1, w3, w2, k: int, eps: float = 1e-5,
                       logit_bias=None, out=None, out_dtype=None, norm_out=None, ws=None,
                       topk_idx_out=None, topk_w_out=None, counts_out=None, packed=False,
-                      variant: int = 0, events=None):
+                      variant: int = 0, events=None, down_split: int = 0):
     """out = hidden + layer(RMSNorm(hidden)); returns (out, norm_out).
     norm_weight [d] float32; norm_out [T, d] has hidden's dtype."""
     T, d = hidden.shape
@@ -439,14 +446,14 @@ def moe_block_forward(hidden, norm_weight, router, w1, w3, w2, k: int, eps: floa
                                   _ptr(w3), _ptr(w2), T, d, ffn, E, k, _ptr(out),
                                   _dtype_code(out.dtype), _ptr(topk_idx_out), _ptr(topk_w_out),
                                   _ptr(counts_out), _ptr(ws), ws.numel(), _stream(dev),
-                                  _options(variant, events))
+                                  _options(variant, events, down_split))
     _check("moe_block_forward", st)
     return out, norm_out
 
 
 def moe_forward_noalloc(x, router, w1, w3, w2, k: int, logit_bias=None, out=None, out_dtype=None,
                         topk_idx_out=None, topk_w_out=None, counts_out=None, packed=False,
-                        variant: int = 0, events=None):
+                        variant: int = 0, events=None, down_split: int = 0):
     """moe_forward on the library's built-in scratch instead of a workspace (the
     C call allocates nothing; this wrapper allocates `out` only when it is not
     passed). Sizes needing more than MOE_NOALLOC_SCRATCH_BYTES raise MoeError
@@ -473,6 +480,6 @@ def moe_forward_noalloc(x, router, w1, w3, w2, k: int, logit_bias=None, out=None
                                     _ptr(w3), _ptr(w2), T, d, ffn, E, k, _ptr(out),
                                     _dtype_code(out.dtype), _ptr(topk_idx_out),
                                     _ptr(topk_w_out), _ptr(counts_out), _stream(dev),
-                                    _options(variant, events))
+                                    _options(variant, events, down_split))
     _check("moe_forward_noalloc", st)
     return out

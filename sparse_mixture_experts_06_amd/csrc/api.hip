@@ -24,17 +24,21 @@ static_assert(kMaxAssignments + 1024 <= (int64_t(1) << 31), "the permutation's s
 struct Opts {
   int variant = 0;                     // expert-FFN kernel family (0 = by size)
   void* const* events = nullptr;       // 6 stage events, or none
+  int down_split = 0;                  // down K split (0 = chosen on the device)
 };
 
 int read_options(const moe_options* o, Opts* out) {
   *out = Opts{};
   if (!o) return MOE_OK;
   if (o->ffn_variant < 0 || o->ffn_variant > 2) return MOE_EINVAL;
+  if (!(o->down_split == 0 || o->down_split == -1 || (o->down_split >= 8 && o->down_split <= 13)))
+    return MOE_EINVAL;
   if (o->stage_events)
     for (int i = 0; i < 6; ++i)
       if (!o->stage_events[i]) return MOE_EINVAL;
   out->variant = o->ffn_variant;
   out->events = o->stage_events;
+  out->down_split = o->down_split;
   return MOE_OK;
 }
 
@@ -60,7 +64,7 @@ int scratch_address(void** out) {
 }
 
 struct Layout {
-  size_t idx, w, counts, offsets, sorted, pos, h, y, wide, total;
+  size_t idx, w, counts, offsets, sorted, pos, nsplit, h, y, wide, total;
 };
 
 // bfloat16 activations (x, h): bf16 weights in either layout, or int8 weights
@@ -69,8 +73,8 @@ inline bool is_bf16(int dtype) {
 }
 
 // float32 partial results the down projection may leave (split K); the most
-// either kernel family leaves, so that the workspace does not depend on the
-// variant
+// either kernel family may leave, so that the workspace does not depend on
+// the variant (the direct-to-LDS kernel chooses within it on the device)
 int ws_splits(int64_t A, int d, int ffn, int E, int dtype) {
   if (!is_bf16(dtype)) return 1;
   const int a = moe::down_splits(1, A, d, ffn, E), b = moe::down_splits(2, A, d, ffn, E);
@@ -92,6 +96,7 @@ Layout layout(int64_t T, int d, int ffn, int E, int k, int dtype) {
   L.offsets = o; o = align256(o + static_cast<size_t>(E + 1) * 4);
   L.sorted = o;  o = align256(o + A * 4);
   L.pos = o;     o = align256(o + A * 4);
+  L.nsplit = o;  o = align256(o + 4);  // partial arrays the down kernel wrote
   L.h = o;       o = align256(o + A * static_cast<size_t>(ffn) * hb);
   L.y = o;       o = align256(o + ns * A * static_cast<size_t>(d) * 4);
   L.wide = o;
@@ -138,14 +143,19 @@ inline void stage(const Opts& o, int i, hipStream_t s) {
   if (o.events) (void)hipEventRecord(static_cast<hipEvent_t>(o.events[i]), s);
 }
 
-// gate/up then down; the down result is left as `nsplit_out` partial arrays
-// at `part` (the caller sums them: the combine, or moe_expert_ffn). `wide`:
+// gate/up then down; the down result is left as up to `nsplit_out` partial
+// arrays at `part` (the caller sums them: the combine, or moe_expert_ffn).
+// Where the direct-to-LDS down kernel runs it chooses the count on the device
+// and writes it to `ns_word`; *ns_dev_out is then ns_word, else null. `wide`:
 // the workspace region for int8 weights widened to bf16 (prefill sizes)
 int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void* w2,
             const int32_t* offsets, const int32_t* sorted_asg, int64_t T, int d, int ffn, int E,
-            int k, float* part, void* h, void* wide, hipStream_t s, const Opts& opt,
-            bool with_events, int* nsplit_out, const moe::FusedPermute* fp = nullptr) {
+            int k, float* part, void* h, void* wide, int32_t* ns_word, hipStream_t s,
+            const Opts& opt, bool with_events, int* nsplit_out, const int32_t** ns_dev_out,
+            const moe::FusedPermute* fp = nullptr) {
   const int64_t A = T * k;
+  const moe::DownSplit ds{opt.down_split, ns_word};
+  *ns_dev_out = nullptr;
   hipError_t err;
   if (dtype == MOE_INT8_PACKED) {
     // int8 weights: the streaming kernels on the codes (few rows per expert),
@@ -176,7 +186,8 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
       err = moe::launch_widen_int8(w2, E, d, ffn, wb, s);
       if (err == hipSuccess)
         err = moe::launch_down_dma(true, static_cast<const uint16_t*>(h), wb, offsets, A, d, ffn,
-                                   E, *nsplit_out, part, s, moe::int8_scales(w2, E, d, ffn));
+                                   E, *nsplit_out, part, s, moe::int8_scales(w2, E, d, ffn), ds);
+      *ns_dev_out = ns_word;
     } else {
       err = moe::launch_down_int8(dvariant, static_cast<const uint16_t*>(h), w2, offsets, A, d,
                                   ffn, E, *nsplit_out, part, s);
@@ -193,7 +204,9 @@ int run_ffn(const void* x, int dtype, const void* w1, const void* w3, const void
     if (err != hipSuccess) return MOE_EHIP;
     if (with_events) stage(opt, 3, s);
     err = moe::launch_down_bf16(dvariant, packed, static_cast<const uint16_t*>(h),
-                                static_cast<const uint16_t*>(w2), offsets, A, d, ffn, E, part, s);
+                                static_cast<const uint16_t*>(w2), offsets, A, d, ffn, E, part, s,
+                                ds);
+    if (moe::down_dma_runs(dvariant, A, d, ffn, E)) *ns_dev_out = ns_word;
   } else {
     *nsplit_out = 1;
     err = moe::launch_gate_up_f32(static_cast<const float*>(x), static_cast<const float*>(w1),
@@ -293,11 +306,14 @@ int moe_expert_ffn(const void* x, int dtype, const void* w1, const void* w3, con
           : 1;
   float* part = nsplit > 1 ? reinterpret_cast<float*>(base + L.y) : y;
   int used = 1;
+  const int32_t* ns_dev = nullptr;
   st = run_ffn(x, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, part, base + L.h,
-               base + L.wide, s, opt, false, &used);
+               base + L.wide, reinterpret_cast<int32_t*>(base + L.nsplit), s, opt, false, &used,
+               &ns_dev);
   if (st != MOE_OK) return st;
   if (used > 1)
-    return hip_status(moe::launch_sum_partials(part, used, A * static_cast<int64_t>(d), y, s));
+    return hip_status(
+        moe::launch_sum_partials(part, used, A * static_cast<int64_t>(d), y, s, ns_dev));
   return MOE_OK;
 }
 
@@ -371,12 +387,14 @@ int forward_impl(const void* x, int dtype, const float* gamma, float eps, void* 
     return MOE_OK;
   }
   int nsplit = 1;
+  const int32_t* ns_dev = nullptr;
   st = run_ffn(xin, dtype, w1, w3, w2, offsets, sorted_asg, T, d, ffn, E, k, y, h, base + L.wide,
-               s, opt, true, &nsplit, fuse ? &fp : nullptr);
+               reinterpret_cast<int32_t*>(base + L.nsplit), s, opt, true, &nsplit, &ns_dev,
+               fuse ? &fp : nullptr);
   if (st != MOE_OK) return st;
   stage(opt, 4, s);
   if (moe::launch_combine(y, nsplit, asg_pos, w, T, d, k, out, out_dtype == MOE_BF16, s,
-                          gamma ? x : nullptr, is_bf16(dtype)) != hipSuccess)
+                          gamma ? x : nullptr, is_bf16(dtype), ns_dev) != hipSuccess)
     return MOE_EHIP;
   stage(opt, 5, s);
   return MOE_OK;

@@ -9,7 +9,9 @@
 // [c*1024, (c+1)*1024) of token t, 4 per thread with 16-byte accesses when
 // d % 4 == 0 (8 per thread, below, for the common shapes). When the down
 // projection left its result as nsplit partial sums (split K), each y row is
-// first summed over the splits in split order. With a residual (the block's input, nnterp Mixtral page,
+// first summed over the splits in split order; where the down kernel chose
+// its split on the device, the count it used is read from ns_dev (at most
+// nsplit). With a residual (the block's input, nnterp Mixtral page,
 // "The Notes": out = h + mlp(post_attention_layernorm(h))), it is added to
 // the finished slot sum.
 #include "common.h"
@@ -23,11 +25,13 @@ constexpr int kThreads = 256;
 template <bool OUT_BF16, bool VEC, int RES>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y,
                                                           int nsplit, int64_t pstride,
+                                                          const int32_t* __restrict__ ns_dev,
                                                           const int32_t* __restrict__ asg_pos,
                                                           const float* __restrict__ w, int d,
                                                           int k, void* __restrict__ out,
                                                           const void* __restrict__ res) {
   const int64_t t = blockIdx.x;
+  if (ns_dev) nsplit = min(nsplit, *ns_dev);
   const int col0 = blockIdx.y * kThreads * 4;
   const int col1 = min(d, col0 + kThreads * 4);
   if constexpr (VEC) {
@@ -92,6 +96,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
 template <bool OUT_BF16, int RES, int KT, int NS>
 __global__ __launch_bounds__(kThreads) void combine8_kernel(const float* __restrict__ y,
                                                            int64_t pstride,
+                                                           const int32_t* __restrict__ ns_dev,
                                                            const int32_t* __restrict__ asg_pos,
                                                            const float* __restrict__ w, int d,
                                                            void* __restrict__ out,
@@ -99,6 +104,8 @@ __global__ __launch_bounds__(kThreads) void combine8_kernel(const float* __restr
   const int64_t t = blockIdx.x;
   const int i = (blockIdx.y * kThreads + threadIdx.x) * 8;
   if (i >= d) return;
+  // (NS = 2 with ns_dev: the second partial only where the down kernel wrote one)
+  const bool second = NS > 1 && (!ns_dev || *ns_dev > 1);
   f32x4 v[KT][NS][2];
   int64_t p[KT];
 #pragma unroll
@@ -109,7 +116,9 @@ __global__ __launch_bounds__(kThreads) void combine8_kernel(const float* __restr
     for (int sp = 0; sp < NS; ++sp)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        v[j][sp][hh] = *reinterpret_cast<const f32x4*>(y + sp * pstride + pj * d + i + 4 * hh);
+        v[j][sp][hh] = (sp == 0 || second)
+                           ? *reinterpret_cast<const f32x4*>(y + sp * pstride + pj * d + i + 4 * hh)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -120,7 +129,8 @@ __global__ __launch_bounds__(kThreads) void combine8_kernel(const float* __restr
     for (int hh = 0; hh < 2; ++hh) {
       f32x4 sum = v[j][0][hh];
 #pragma unroll
-      for (int sp = 1; sp < NS; ++sp) sum += v[j][sp][hh];
+      for (int sp = 1; sp < NS; ++sp)
+        if (second) sum += v[j][sp][hh];
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[4 * hh + c] = fmaf(wt, sum[c], acc[4 * hh + c]);
     }
@@ -155,7 +165,9 @@ __global__ __launch_bounds__(kThreads) void combine8_kernel(const float* __restr
 
 __global__ __launch_bounds__(kThreads) void sum_partials_kernel(const float* __restrict__ part,
                                                                int nsplit, int64_t n,
+                                                               const int32_t* __restrict__ ns_dev,
                                                                float* __restrict__ y) {
+  if (ns_dev) nsplit = min(nsplit, *ns_dev);
   for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * kThreads) {
     float v = part[i];
@@ -168,29 +180,30 @@ __global__ __launch_bounds__(kThreads) void sum_partials_kernel(const float* __r
 
 namespace {
 template <bool OUT_BF16, int RES, int KT>
-void launch_combine8(const float* y, int nsplit, int64_t pstride, const int32_t* asg_pos,
-                     const float* w, int64_t T, int d, void* out, const void* res,
-                     hipStream_t s) {
+void launch_combine8(const float* y, int nsplit, int64_t pstride, const int32_t* ns_dev,
+                     const int32_t* asg_pos, const float* w, int64_t T, int d, void* out,
+                     const void* res, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>((d + kThreads * 8 - 1) / (kThreads * 8)));
   if (nsplit == 1)
     hipLaunchKernelGGL((combine8_kernel<OUT_BF16, RES, KT, 1>), grid, dim3(kThreads), 0, s, y,
-                       pstride, asg_pos, w, d, out, res);
+                       pstride, ns_dev, asg_pos, w, d, out, res);
   else
     hipLaunchKernelGGL((combine8_kernel<OUT_BF16, RES, KT, 2>), grid, dim3(kThreads), 0, s, y,
-                       pstride, asg_pos, w, d, out, res);
+                       pstride, ns_dev, asg_pos, w, d, out, res);
 }
 
 template <int RES>
-void launch_combine_res(const float* y, int nsplit, int64_t pstride, const int32_t* asg_pos,
-                        const float* w, int64_t T, int d, int k, void* out, int out_bf16,
-                        bool vec, bool vec8, const void* res, hipStream_t s) {
+void launch_combine_res(const float* y, int nsplit, int64_t pstride, const int32_t* ns_dev,
+                        const int32_t* asg_pos, const float* w, int64_t T, int d, int k,
+                        void* out, int out_bf16, bool vec, bool vec8, const void* res,
+                        hipStream_t s) {
   if (vec8 && (k == 1 || k == 2) && (nsplit == 1 || nsplit == 2)) {
     if (out_bf16) {
-      if (k == 1) launch_combine8<true, RES, 1>(y, nsplit, pstride, asg_pos, w, T, d, out, res, s);
-      else launch_combine8<true, RES, 2>(y, nsplit, pstride, asg_pos, w, T, d, out, res, s);
+      if (k == 1) launch_combine8<true, RES, 1>(y, nsplit, pstride, ns_dev, asg_pos, w, T, d, out, res, s);
+      else launch_combine8<true, RES, 2>(y, nsplit, pstride, ns_dev, asg_pos, w, T, d, out, res, s);
     } else {
-      if (k == 1) launch_combine8<false, RES, 1>(y, nsplit, pstride, asg_pos, w, T, d, out, res, s);
-      else launch_combine8<false, RES, 2>(y, nsplit, pstride, asg_pos, w, T, d, out, res, s);
+      if (k == 1) launch_combine8<false, RES, 1>(y, nsplit, pstride, ns_dev, asg_pos, w, T, d, out, res, s);
+      else launch_combine8<false, RES, 2>(y, nsplit, pstride, ns_dev, asg_pos, w, T, d, out, res, s);
     }
     return;
   }
@@ -198,24 +211,24 @@ void launch_combine_res(const float* y, int nsplit, int64_t pstride, const int32
   if (out_bf16) {
     if (vec)
       hipLaunchKernelGGL((combine_kernel<true, true, RES>), grid, dim3(kThreads), 0, s, y, nsplit,
-                         pstride, asg_pos, w, d, k, out, res);
+                         pstride, ns_dev, asg_pos, w, d, k, out, res);
     else
       hipLaunchKernelGGL((combine_kernel<true, false, RES>), grid, dim3(kThreads), 0, s, y, nsplit,
-                         pstride, asg_pos, w, d, k, out, res);
+                         pstride, ns_dev, asg_pos, w, d, k, out, res);
   } else {
     if (vec)
       hipLaunchKernelGGL((combine_kernel<false, true, RES>), grid, dim3(kThreads), 0, s, y, nsplit,
-                         pstride, asg_pos, w, d, k, out, res);
+                         pstride, ns_dev, asg_pos, w, d, k, out, res);
     else
       hipLaunchKernelGGL((combine_kernel<false, false, RES>), grid, dim3(kThreads), 0, s, y,
-                         nsplit, pstride, asg_pos, w, d, k, out, res);
+                         nsplit, pstride, ns_dev, asg_pos, w, d, k, out, res);
   }
 }
 }  // namespace
 
 hipError_t launch_combine(const float* y, int nsplit, const int32_t* asg_pos, const float* w,
                           int64_t T, int d, int k, void* out, int out_bf16, hipStream_t s,
-                          const void* residual, int res_bf16) {
+                          const void* residual, int res_bf16, const int32_t* ns_dev) {
   if (T == 0) return hipSuccess;
   const int64_t pstride = T * k * static_cast<int64_t>(d);
   const auto aligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
@@ -224,22 +237,24 @@ hipError_t launch_combine(const float* y, int nsplit, const int32_t* asg_pos, co
   const bool vec8 = (d % 8 == 0) && aligned(y, 16) && aligned(out, 16) &&
                     (!residual || aligned(residual, 16));
   if (!residual)
-    launch_combine_res<0>(y, nsplit, pstride, asg_pos, w, T, d, k, out, out_bf16, vec, vec8,
-                          nullptr, s);
+    launch_combine_res<0>(y, nsplit, pstride, ns_dev, asg_pos, w, T, d, k, out, out_bf16, vec,
+                          vec8, nullptr, s);
   else if (res_bf16)
-    launch_combine_res<2>(y, nsplit, pstride, asg_pos, w, T, d, k, out, out_bf16, vec, vec8,
-                          residual, s);
+    launch_combine_res<2>(y, nsplit, pstride, ns_dev, asg_pos, w, T, d, k, out, out_bf16, vec,
+                          vec8, residual, s);
   else
-    launch_combine_res<1>(y, nsplit, pstride, asg_pos, w, T, d, k, out, out_bf16, vec, vec8,
-                          residual, s);
+    launch_combine_res<1>(y, nsplit, pstride, ns_dev, asg_pos, w, T, d, k, out, out_bf16, vec,
+                          vec8, residual, s);
   return hipGetLastError();
 }
 
-hipError_t launch_sum_partials(const float* part, int nsplit, int64_t n, float* y, hipStream_t s) {
+hipError_t launch_sum_partials(const float* part, int nsplit, int64_t n, float* y, hipStream_t s,
+                               const int32_t* ns_dev) {
   if (n == 0) return hipSuccess;
   const int64_t want = (n + kThreads - 1) / kThreads;
   const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
-  hipLaunchKernelGGL(sum_partials_kernel, dim3(blocks), dim3(kThreads), 0, s, part, nsplit, n, y);
+  hipLaunchKernelGGL(sum_partials_kernel, dim3(blocks), dim3(kThreads), 0, s, part, nsplit, n,
+                     ns_dev, y);
   return hipGetLastError();
 }
 

@@ -136,10 +136,11 @@ constexpr int kFusedPermuteMaxA = 512;
 bool gate_up_fuses_permute(int variant, int64_t A);
 // bf16 experts: gate/up (+SiLU*mul) -> h [A, ffn] bf16, down -> y [A, d] f32.
 // `variant` is resolved (1 streaming, 2 tiled); `packed` selects the
-// fragment-order weight layout. The down kernel writes
+// fragment-order weight layout. The down kernel writes up to
 // down_splits(variant, A, d, ffn, E) float32 partial results [nsplit, A, d]
-// whose sum (in split order) is y; the count depends on the sizes only, not
-// on the layout, so both layouts give bit-identical y.
+// whose sum (in split order) is y; the count depends on the sizes (and, for
+// the direct-to-LDS kernel, the expert counts), not on the layout, so both
+// layouts give bit-identical y.
 // fp non-null (only where gate_up_fuses_permute): offsets and sorted_asg
 // are not read, the kernel writes fp's arrays
 hipError_t launch_gate_up_bf16(int variant, bool packed, const uint16_t* x, const uint16_t* w1,
@@ -147,10 +148,21 @@ hipError_t launch_gate_up_bf16(int variant, bool packed, const uint16_t* x, cons
                                const int32_t* sorted_asg, int64_t A, int d, int ffn, int E,
                                int k, uint16_t* h, hipStream_t s,
                                const FusedPermute* fp = nullptr);
+// The direct-to-LDS down kernel's K split: the caller's choice (0 = made on
+// the device from the expert counts, -1 = none, 8..13 = a first part of that
+// many sixteenths of K) and a device int32 (or null) that receives the number
+// of partial arrays it wrote (1 or 2; at most down_splits(...)).
+struct DownSplit {
+  int opt = 0;
+  int32_t* word = nullptr;
+};
 hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const uint16_t* w2,
                             const int32_t* offsets, int64_t A, int d, int ffn, int E, float* part,
-                            hipStream_t s);
+                            hipStream_t s, DownSplit ds = {});
+// the most partial arrays the down kernel of this resolved family writes; for
+// the direct-to-LDS kernel (down_dma_runs) the count it used goes to ds.word
 int down_splits(int variant, int64_t A, int d, int ffn, int E);
+bool down_dma_runs(int variant, int64_t A, int d, int ffn, int E);
 // K split of the tiled down kernels below the direct-to-LDS sizes: 2 while
 // the 256-row tiles would leave CUs idle (d % 256 == 0, ffn % 128 == 0), else 1
 int tiled_down_splits(int64_t A, int d, int ffn, int E);
@@ -179,8 +191,9 @@ hipError_t launch_gate_up_dma(bool packed, const uint16_t* x, const uint16_t* w1
 bool dma_down_ok(int64_t A, int d, int ffn, int E);
 int dma_down_splits(int64_t A, int d, int ffn, int E);
 hipError_t launch_down_dma(bool packed, const uint16_t* h, const uint16_t* w2,
-                           const int32_t* offsets, int64_t A, int d, int ffn, int E, int nsplit,
-                           float* part, hipStream_t s, const float* s2 = nullptr);
+                           const int32_t* offsets, int64_t A, int d, int ffn, int E,
+                           int max_split, float* part, hipStream_t s, const float* s2,
+                           DownSplit ds);
 // weight-only int8 experts (ffn_int8.hip): bytes of one quantized matrix
 // (codes, then float32 row scales at the next 256-byte boundary), the
 // quantizer, and the gate/up and down launchers that read it (`variant`
@@ -220,11 +233,15 @@ hipError_t launch_down_f32(const float* h, const float* w2, const int32_t* offse
 // non-null, added after the slot sum; bf16 or float32 per res_bf16), with y
 // the split-order sum of nsplit partial arrays of A x d floats (A = T*k)
 // starting at `part`
+// (ns_dev non-null: a device int32 holding the count actually written, at
+// most nsplit, read by the kernels)
 hipError_t launch_combine(const float* part, int nsplit, const int32_t* asg_pos, const float* w,
                           int64_t T, int d, int k, void* out, int out_bf16, hipStream_t s,
-                          const void* residual = nullptr, int res_bf16 = 0);
-// y[i] = sum_s part[s*n + i] in split order
-hipError_t launch_sum_partials(const float* part, int nsplit, int64_t n, float* y, hipStream_t s);
+                          const void* residual = nullptr, int res_bf16 = 0,
+                          const int32_t* ns_dev = nullptr);
+// y[i] = sum_s part[s*n + i] in split order (ns_dev as for the combine)
+hipError_t launch_sum_partials(const float* part, int nsplit, int64_t n, float* y, hipStream_t s,
+                               const int32_t* ns_dev = nullptr);
 
 // Resolved expert-FFN kernel family for these sizes (1 streaming, 2 tiled).
 int choose_ffn_variant(int requested, int64_t A, int E);   // gate/up

@@ -1213,7 +1213,8 @@ hipError_t gate_up_impl(int variant, const uint16_t* x, const uint16_t* w1, cons
 
 template <bool PACKED>
 hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
-                     int64_t A, int d, int ffn, int E, float* part, hipStream_t s) {
+                     int64_t A, int d, int ffn, int E, float* part, hipStream_t s,
+                     DownSplit ds) {
   const int nsplit = down_splits(variant, A, d, ffn, E);
   if (variant == 1) {
     constexpr int rows = 16 * kDownRT;
@@ -1236,8 +1237,8 @@ hipError_t down_impl(int variant, const uint16_t* h, const uint16_t* w2, const i
                          dim3(kWave * kStreamWaves), 0, s, h, w2, offsets, ffn, d,
                          static_cast<int>(A), nsplit, part);
     }
-  } else if (dma_down_ok(A, d, ffn, E)) {
-    return launch_down_dma(PACKED, h, w2, offsets, A, d, ffn, E, nsplit, part, s);
+  } else if (down_dma_runs(variant, A, d, ffn, E)) {
+    return launch_down_dma(PACKED, h, w2, offsets, A, d, ffn, E, nsplit, part, s, nullptr, ds);
   } else if (PACKED && d % 256 == 0) {
     const int ntn = d / 256;
     hipLaunchKernelGGL((wtiled_kernel<false, PACKED, false, kWRing, kWOcc, kWXSets>),
@@ -1278,13 +1279,17 @@ int tiled_down_splits(int64_t A, int d, int ffn, int E) {
   return tiles < 256 ? 2 : 1;
 }
 
+bool down_dma_runs(int variant, int64_t A, int d, int ffn, int E) {
+  return variant != 1 && dma_down_ok(A, d, ffn, E);
+}
+
 int down_splits(int variant, int64_t A, int d, int ffn, int E) {
   // the streaming down kernel splits K two ways while its float32 partials
-  // stay small; the tiled kernels split K where the 256-row tiles of the
-  // direct-to-LDS kernels would leave the last round over the CUs part-empty,
-  // and below their sizes while the 256-row weights-in-registers tiles would
-  // not give every CU one (all tiled kernels follow the same split, so y does
-  // not depend on the weight layout)
+  // stay small; the direct-to-LDS kernel chooses its split on the device from
+  // the expert counts (at most two parts), and below its sizes the tiled
+  // kernels split K while the 256-row weights-in-registers tiles would not
+  // give every CU one (all tiled kernels of a size follow the same rule, so y
+  // does not depend on the weight layout)
   if (variant == 1) return A <= 4096 ? 2 : 1;
   if (dma_down_ok(A, d, ffn, E)) return dma_down_splits(A, d, ffn, E);
   return tiled_down_splits(A, d, ffn, E);
@@ -1338,10 +1343,10 @@ bool gate_up_fuses_permute(int variant, int64_t A) {
 
 hipError_t launch_down_bf16(int variant, bool packed, const uint16_t* h, const uint16_t* w2,
                             const int32_t* offsets, int64_t A, int d, int ffn, int E, float* part,
-                            hipStream_t s) {
+                            hipStream_t s, DownSplit ds) {
   if (A == 0) return hipSuccess;
-  return packed ? down_impl<true>(variant, h, w2, offsets, A, d, ffn, E, part, s)
-                : down_impl<false>(variant, h, w2, offsets, A, d, ffn, E, part, s);
+  return packed ? down_impl<true>(variant, h, w2, offsets, A, d, ffn, E, part, s, ds)
+                : down_impl<false>(variant, h, w2, offsets, A, d, ffn, E, part, s, ds);
 }
 
 }  // namespace moe

@@ -8,7 +8,8 @@
 //            r = sorted_asg[p] / k for p in expert e's grouped rows; h is bf16;
 //   down:    y[p, n] = sum_i h[p,i] w2[e,n,i], float32, optionally split in K
 //            into two partial sums over [0, ksplit) and [ksplit, K) (written
-//            to part[0] and part[1]; y is their sum in that order).
+//            to part[0] and part[1]; y is their sum in that order), the split
+//            chosen on the device from the expert counts (below).
 //
 // Tile: 256 weight rows x 256 token rows per workgroup of 8 waves, two per
 // SIMD (so one wave's MFMAs run while the other waits on a load issue or the
@@ -68,17 +69,18 @@
 // the SiLU*mul (gate by the w1 row's scale, up by the w3 row's) or the store
 // (down, each K-split partial), as the int8 decode kernels do.
 //
-// Paired last m-tiles (gate/up with fragment-order weights): an expert's last
-// m-tile of at most 128 rows costs nearly as much as a full one (its time is
-// set by the weight stream it shares with the full tiles of its weight tile,
-// not by its own loads or MFMAs: halving either changed nothing, while
-// leaving those tiles out took 9-13% off the launch), so two weight tiles
-// of an XCD share one: 512 weight rows x 128 token rows, each wave the same 64
-// x 128 block as in a 256x256 tile. 8x7B prefill: 4032 -> 3808 tiles, gate/up
-// 1574 -> 1497-1544 us; 8x22B 1510 -> 1458 us. The down projection keeps its own
-// last m-tiles: there they cost about half a full tile (leaving out those of at
-// most 64 rows took only 6% off), less than a paired tile's share, and paired
-// they ran 2-3% slower.
+// Paired last m-tiles (fragment-order weights): an expert's last m-tile of at
+// most 128 rows costs nearly as much as a full one (its time is set by the
+// weight stream it shares with the full tiles of its weight tile, not by its
+// own loads or MFMAs: halving either changed nothing, while leaving those
+// tiles out took 9-13% off the launch), so two weight tiles of an XCD share
+// one: 512 weight rows x 128 token rows, each wave the same 64 x 128 block as
+// in a 256x256 tile. Gate/up always pairs them (8x7B prefill: 4032 -> 3808
+// tiles, 1574 -> 1497-1544 us; 8x22B 1510 -> 1458 us). The down projection
+// pairs them while experts average at most two m-tiles (T*k <= 512 E), where
+// last m-tiles are a large share of its few tiles (32 experts at 4096 tokens:
+// 1099 vs 1139 us unsplit, 1035 us with the split below; 16 experts: 856-889
+// vs about 910 us); with more rows per expert pairing measured 0-2% slower.
 //
 // Every output element is one float32 MFMA accumulation over its K range in
 // increasing K, 32 at a time: the order of the 128-row tiled kernels, whose
@@ -128,87 +130,197 @@ constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | 
 // ragged weight tiles) XCD x takes the x-th of 8 equal slices of the list of
 // all tiles, expert by expert, K part, n-tile, m-tile. Surplus workgroups of
 // the worst-case grid return.
+//
+// Finding the workgroup's expert: every wave of the workgroup does it on its
+// own, one expert per lane (E <= 32), so no wave walks the experts in scalar
+// code (eight waves doing that share the CU's scalar unit: at 32 experts the
+// walk, and the split choice below, cost several microseconds per tile).
+
+// one XCD's tile list of one K part, lane l < E holding expert l: its grouped
+// rows ml and first row bl, its tiles cl and their inclusive prefix sum il
+// over the lanes; n = all the tiles
+struct XcdList {
+  int ml, bl, cl, il, n;
+};
+
+// tiles of one expert of ml rows in an XCD's list (nnx weight tiles per XCD)
+__device__ __forceinline__ int expert_tiles(int ml, int nnx, bool pair_tails) {
+  const int pairs = nnx >> 1;
+  const int mt = (ml + DT - 1) / DT;
+  const bool small = pair_tails && pairs > 0 && mt > 0 && ml - (mt - 1) * DT <= DT / 2;
+  return small ? pairs * (2 * mt - 1) + (nnx - 2 * pairs) * mt : nnx * mt;
+}
+
+// inclusive prefix sum over lanes 0..31 (lane 31: the total of lanes 0..31)
+__device__ __forceinline__ int prefix32(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ XcdList xcd_list(const int32_t* __restrict__ offsets, int E, int ntn,
+                                            bool pair_tails) {
+  const int lane = threadIdx.x & (kWave - 1);
+  XcdList L;
+  const bool in = lane < E;
+  L.bl = in ? offsets[lane] : 0;
+  L.ml = in ? offsets[lane + 1] - L.bl : 0;
+  L.cl = expert_tiles(L.ml, ntn >> 3, pair_tails);
+  L.il = prefix32(L.cl, lane);
+  L.n = __builtin_amdgcn_readfirstlane(__shfl(L.il, 31, kWave));
+  return L;
+}
+
 __device__ __forceinline__ bool decode_tile256(const int32_t* __restrict__ offsets, int E, int ntn,
-                                               int nsplit, bool pair_tails, int& e, int& beg,
-                                               int& M, int& m0, int& nt, int& nt2, int& sp) {
+                                               int nsplit, bool pair_tails, const XcdList& L,
+                                               int& e, int& beg, int& M, int& m0, int& nt,
+                                               int& nt2, int& sp) {
   const int x = blockIdx.x & 7;
   int q = blockIdx.x >> 3;
   nt2 = -1;
   if ((ntn & 7) == 0) {
+    if (q >= nsplit * L.n) return false;
+    sp = q >= L.n ? 1 : 0;  // (nsplit <= 2)
+    q -= sp * L.n;
+    // the expert: the first whose tiles end past q
+    const int lane = threadIdx.x & (kWave - 1);
+    e = __popcll(__ballot(lane < E && L.il <= q));
+    M = __builtin_amdgcn_readfirstlane(__shfl(L.ml, e, kWave));
+    beg = __builtin_amdgcn_readfirstlane(__shfl(L.bl, e, kWave));
+    q -= __builtin_amdgcn_readfirstlane(__shfl(L.il - L.cl, e, kWave));
     const int nnx = ntn >> 3;  // weight tiles of each XCD
     // the XCD's weight tiles in pairs (2g, 2g+1); an odd one left over last
     const int pairs = nnx >> 1;
-    for (int s = 0; s < nsplit; ++s) {
-      for (int i = 0; i < E; ++i) {
-        const int Mi = offsets[i + 1] - offsets[i];
-        const int mt = (Mi + DT - 1) / DT;
-        // small: the last m-tile holds at most DT/2 rows and is shared by the pair
-        const bool small = pair_tails && pairs > 0 && mt > 0 && Mi - (mt - 1) * DT <= DT / 2;
-        const int mf = small ? mt - 1 : mt;  // m-tiles a weight tile runs alone
-        const int gsz = 2 * mf + (small ? 1 : 0);  // tiles of a pair's group
-        const int cnt = pairs * gsz + (nnx - 2 * pairs) * mt;
-        if (q < cnt) {
-          e = i;
-          beg = offsets[i];
-          M = Mi;
-          sp = s;
-          if (q < pairs * gsz) {
-            // group g: the shared last m-tile (if small), then the two weight
-            // tiles' m-tiles alternately, so that the tiles reading either
-            // weight tile run together
-            const int g = q / gsz, r = q % gsz;
-            if (small && r == 0) {
-              m0 = mf * DT;
-              nt = 2 * g * 8 + x;
-              nt2 = nt + 8;
-            } else {
-              const int rr = small ? r - 1 : r;
-              m0 = (rr >> 1) * DT;
-              nt = (2 * g + (rr & 1)) * 8 + x;
-            }
-          } else {
-            const int qq = q - pairs * gsz;
-            m0 = (qq % mt) * DT;
-            nt = (2 * pairs + qq / mt) * 8 + x;
-          }
-          return true;
-        }
-        q -= cnt;
+    const int mt = (M + DT - 1) / DT;
+    // small: the last m-tile holds at most DT/2 rows and is shared by the pair
+    const bool small = pair_tails && pairs > 0 && mt > 0 && M - (mt - 1) * DT <= DT / 2;
+    const int mf = small ? mt - 1 : mt;  // m-tiles a weight tile runs alone
+    const int gsz = 2 * mf + (small ? 1 : 0);  // tiles of a pair's group
+    if (q < pairs * gsz) {
+      // group g: the shared last m-tile (if small), then the two weight
+      // tiles' m-tiles alternately, so that the tiles reading either weight
+      // tile run together
+      const int g = q / gsz, r = q % gsz;
+      if (small && r == 0) {
+        m0 = mf * DT;
+        nt = 2 * g * 8 + x;
+        nt2 = nt + 8;
+      } else {
+        const int rr = small ? r - 1 : r;
+        m0 = (rr >> 1) * DT;
+        nt = (2 * g + (rr & 1)) * 8 + x;
       }
+    } else {
+      const int qq = q - pairs * gsz;
+      m0 = (qq % mt) * DT;
+      nt = (2 * pairs + qq / mt) * 8 + x;
     }
-    return false;
+    return true;
   }
   int total = 0;
   for (int i = 0; i < E; ++i) total += ((offsets[i + 1] - offsets[i] + DT - 1) / DT) * ntn * nsplit;
   const int per = (total + 7) / 8;
   if (q >= per) return false;
-  int L = x * per + q;
-  if (L >= total) return false;
+  int Lq = x * per + q;
+  if (Lq >= total) return false;
   for (int i = 0; i < E; ++i) {
     const int Mi = offsets[i + 1] - offsets[i];
     const int mt = (Mi + DT - 1) / DT;
     const int cnt = mt * ntn * nsplit;
-    if (L < cnt) {
+    if (Lq < cnt) {
       e = i;
       beg = offsets[i];
       M = Mi;
-      m0 = (L % mt) * DT;
-      const int r = L / mt;
+      m0 = (Lq % mt) * DT;
+      const int r = Lq / mt;
       nt = r % ntn;
       sp = r / ntn;
       return true;
     }
-    L -= cnt;
+    Lq -= cnt;
   }
   return false;
 }
 
+// The down projection's K split, chosen by every workgroup from the expert
+// counts (the same choice in all of them). With a split, every tile's longer
+// first K part is listed before any second part, so the short second parts
+// fill the last round over an XCD's CUs; the price is a second fixed cost
+// per tile and a second float32 partial of y for the combine to read. The
+// model: one XCD's 32 CUs take its n tiles (the list above) in order, each CU
+// the next tile as soon as it is free (one workgroup per CU); every tile
+// costs its K steps plus kFixSteps whatever its row count (a part-filled tile
+// issues the loads of a full one, and those set its time: measured,
+// part-filled and full tiles of the down projection take about as long); the
+// combine's extra read costs `pen` K steps. It compares no split with first
+// parts of 8/16 .. 13/16 of K (whole 4-step trips), one candidate per lane,
+// and takes the fastest, no split on a tie; beyond 8 rounds of tiles per XCD
+// it does not split. Measured at 4096 tokens, d = 4096, ffn = 14336 (down,
+// us): k = 1: 625 unsplit, 530 / 497 / 530 / 555 with first parts of 8 / 11 /
+// 12 / 13 sixteenths (the model picks 11); 16 experts: 985 unsplit, 907-914
+// split at 11-13; 8x22B (d = 6144, 2048 tokens): 776 unsplit, 779-813 split
+// (the model keeps it whole).
+constexpr int kFixSteps = 12;  // start-up and epilogue of a tile, in K steps
+constexpr int kXcdCUs = 32;    // compute units of one XCD
+
+// Finish time of kXcdCUs CUs taking n tiles of cost a and then n of cost b
+// (a, b > 0), each the next tile as soon as it is free. After the first
+// parts, r = n % kXcdCUs CUs are at L + a and the others at L (L = (n /
+// kXcdCUs) a); the second parts start at the n smallest of the times L + m b
+// (each for the kXcdCUs - r lower CUs) and L + a + m b (each for the r upper
+// ones), m = 0, 1, ...; the finish is the n-th smallest start plus b, or L + a
+// if that is later. With a = alpha b + beta (0 <= beta < b), the starts up to
+// L + a + m b number 32 (m + 1) + (32 - r) alpha, and those up to L + m b (m b
+// >= a) number 32 (m + 1) - r (alpha + [beta > 0]).
+__device__ __forceinline__ int two_part_makespan(int n, int a, int b) {
+  const int L = (n / kXcdCUs) * a, r = n % kXcdCUs, nlo = kXcdCUs - r;
+  int t = ((n + nlo - 1) / nlo - 1) * b;  // the n-th start if the lower CUs took all
+  if (r > 0 && t >= a) {
+    const int al = a / b, up = al + (a % b ? 1 : 0);
+    const int mhi = max(0, (n - nlo * al + kXcdCUs - 1) / kXcdCUs - 1);
+    const int mlo = max(up, (n + r * up + kXcdCUs - 1) / kXcdCUs - 1);
+    t = min(a + mhi * b, mlo * b);
+  }
+  return L + max(t + b, r > 0 ? a : 0);
+}
+
+// steps of the first K part (a multiple of 4), or 0 for no split; n tiles of
+// one K part per XCD
+__device__ __forceinline__ int down_split_steps(int n, int nsteps, int pen) {
+  if (n == 0 || n > 8 * kXcdCUs) return 0;
+  // lane 0: no split; lane i = 1..6: a first part of i + 7 sixteenths. key =
+  // finish time * 8 + lane, so the smallest key is the fastest, a tie going
+  // to no split, then to the shorter first part
+  const int lane = threadIdx.x & (kWave - 1);
+  int key = 0x7fffffff;
+  if (lane == 0) {
+    key = (n + kXcdCUs - 1) / kXcdCUs * (nsteps + kFixSteps) * 8;
+  } else if (lane <= 6) {
+    const int s0 = (nsteps * (lane + 7) / 16) & ~3;
+    if (s0 >= 4 && nsteps - s0 >= 4)
+      key = (two_part_makespan(n, s0 + kFixSteps, nsteps - s0 + kFixSteps) + pen) * 8 + lane;
+  }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) key = min(key, __shfl_xor(key, o, kWave));
+  const int best = __builtin_amdgcn_readfirstlane(key) & 7;
+  return best == 0 ? 0 : (nsteps * (best + 7) / 16) & ~3;
+}
+
 // GATE_UP: act = x [act_rows = T, K = d] bf16, wa/wb = w1/w3 [E, N = ffn, d],
-// out = h [A, ffn] bf16, nsplit = 1.
+// out = h [A, ffn] bf16, one K part; last m-tiles paired (fragment order).
 // !GATE_UP: act = h [act_rows = A, K = ffn] bf16 in grouped order, wa = w2
 // [E, N = d, ffn], out = part [nsplit][A][d] float32, the partial arrays
 // pstride floats apart; with nsplit = 2 the K parts are [0, ksplit) and
-// [ksplit, K) (ksplit a multiple of 128). SCALED: sa/sb = row scales [E, N] of wa/wb.
+// [ksplit, K). split: -1 = chosen here by down_split_steps (pen: the combine's
+// extra read in K steps), 0 = one K part, > 0 = steps of the first part (a
+// multiple of 4, at least 4 steps in each part). pair_tails: whether the tile
+// list pairs last m-tiles of at most 128 rows (also what the split model
+// counts; only fragment-order weights pair them, so both layouts choose the
+// same split). ns_out (or null): receives nsplit, from workgroup 0. SCALED:
+// sa/sb = row scales [E, N] of wa/wb.
 template <bool GATE_UP, bool PACKED, bool SCALED>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64_t act_rows,
                                          const uint16_t* __restrict__ wa,
@@ -216,11 +328,37 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
                                          const int32_t* __restrict__ offsets,
                                          const int32_t* __restrict__ sorted_asg, int K, int N,
                                          int E, int ktop, void* __restrict__ out, int ntn,
-                                         int nsplit, int ksplit, int64_t pstride,
+                                         int split, int pen, bool pair_tails,
+                                         int32_t* __restrict__ ns_out, int64_t pstride,
                                          const float* __restrict__ sa,
                                          const float* __restrict__ sb) {
+  // the tile list (row-major weights run every last m-tile on its own)
+  const bool xcd = (ntn & 7) == 0;
+  XcdList xl{0, 0, 0, 0, 0};
+  if (xcd) xl = xcd_list(offsets, E, ntn, PACKED && pair_tails);
+  int nsplit = 1, ksplit = K;
+  if constexpr (!GATE_UP) {
+    int s0 = split;
+    if (split < 0) {
+      // the split model counts the tiles as fragment order lists them, so
+      // that both weight layouts choose the same split
+      int n = xl.n;
+      if (!PACKED && xcd && pair_tails) {
+        const int lane = threadIdx.x & (kWave - 1);
+        n = __builtin_amdgcn_readfirstlane(
+            __shfl(prefix32(expert_tiles(xl.ml, ntn >> 3, true), lane), 31, kWave));
+      }
+      s0 = xcd ? down_split_steps(n, K / 32, pen) : 0;
+    }
+    if (s0 > 0) {
+      nsplit = 2;
+      ksplit = s0 * 32;
+    }
+    if (ns_out && blockIdx.x == 0 && threadIdx.x == 0) *ns_out = nsplit;
+  }
   int e, beg, M, m0, nt, nt2, sp;
-  if (!decode_tile256(offsets, E, ntn, nsplit, PACKED && GATE_UP, e, beg, M, m0, nt, nt2, sp))
+  if (!decode_tile256(offsets, E, ntn, nsplit, PACKED && pair_tails, xl, e, beg, M, m0, nt, nt2,
+                      sp))
     return;
 
   // one array per buffer: distinct objects let the compiler see that a
@@ -633,7 +771,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ act, int64
     default: run_wm(std::integral_constant<int, 0>{}); break;
   }
   };
-  if constexpr (PACKED && GATE_UP) {
+  if constexpr (PACKED) {
     if (nt2 >= 0) body(std::true_type{});
     else body(std::false_type{});
   } else {
@@ -648,8 +786,8 @@ __global__ __launch_bounds__(kDmaThreads, 1) void gate_up_dma_kernel(
     const uint16_t* __restrict__ w3, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_asg, int d, int ffn, int E, int ktop,
     uint16_t* __restrict__ h, int ntn, const float* __restrict__ s1, const float* __restrict__ s3) {
-  dma_tile<true, PACKED, SCALED>(x, T, w1, w3, offsets, sorted_asg, d, ffn, E, ktop, h, ntn, 1, d, 0,
-                                 s1, s3);
+  dma_tile<true, PACKED, SCALED>(x, T, w1, w3, offsets, sorted_asg, d, ffn, E, ktop, h, ntn, 0, 0,
+                                 true, nullptr, 0, s1, s3);
 }
 
 // h [A, ffn] bf16 grouped, w2 [E, d, ffn] (fragment order or row-major), part [nsplit, A, d] f32
@@ -657,13 +795,13 @@ template <bool PACKED, bool SCALED>
 __global__ __launch_bounds__(kDmaThreads, 1) void down_dma_kernel(
     const uint16_t* __restrict__ h, int64_t A, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ offsets, int d, int ffn, int E, float* __restrict__ part, int ntn,
-    int nsplit, int ksplit, const float* __restrict__ s2) {
-  dma_tile<false, PACKED, SCALED>(h, A, w2, w2, offsets, nullptr, ffn, d, E, 1, part, ntn, nsplit,
-                                  ksplit, A * d, s2, s2);
+    int split, int pen, int pair_tails, int32_t* __restrict__ ns_out,
+    const float* __restrict__ s2) {
+  dma_tile<false, PACKED, SCALED>(h, A, w2, w2, offsets, nullptr, ffn, d, E, 1, part, ntn, split,
+                                  pen, pair_tails != 0, ns_out, A * d, s2, s2);
 }
 
 constexpr int64_t kMax31 = (int64_t(1) << 31) - 1;
-constexpr int64_t kCUs = 256;  // compute units of an MI355X
 
 }  // namespace
 
@@ -705,103 +843,53 @@ bool dma_down_ok(int64_t A, int d, int ffn, int E) {
   return static_cast<int64_t>(ffn) * d * 2 <= kMax31 && A * ffn * 2 <= kMax31;
 }
 
-namespace {
-
-// Makespan (in K steps) of one XCD's 32 CUs taking the listed tiles in order,
-// each CU the next tile as soon as it is free (how workgroups are dispatched
-// here: one per CU, 128-160 KiB of LDS each).
-int64_t xcd_makespan(const int64_t* cost, int n) {
-  constexpr int kXcdCUs = kCUs / 8;
-  int64_t busy[kXcdCUs] = {};
-  for (int i = 0; i < n; ++i) {
-    int c = 0;
-    for (int j = 1; j < kXcdCUs; ++j)
-      if (busy[j] < busy[c]) c = j;
-    busy[c] += cost[i];
-  }
-  int64_t m = 0;
-  for (int j = 0; j < kXcdCUs; ++j) m = busy[j] > m ? busy[j] : m;
-  return m;
+// The most K parts the kernel may choose (the workspace holds that many
+// partial arrays of y): 2 where the device's choice may split, i.e. weight
+// tiles in multiples of 8, at least 8 K steps, and an XCD's tiles possibly
+// within 8 rounds of its CUs (a lower bound of their count: every expert's
+// rows in whole m-tiles, less one per pair of weight tiles for its last).
+int dma_down_splits(int64_t A, int d, int ffn, int E) {
+  if (!dma_down_ok(A, d, ffn, E) || (d / 256) % 8 != 0 || ffn / 32 < 8) return 1;
+  const int64_t nnx = d / 2048;
+  return nnx * (A / DT - (E + 1) / 2) <= 8 * kXcdCUs ? 2 : 1;
 }
-
-struct DownPlan {
-  int nsplit, ksplit;
-};
-
-// The K split of the down projection. Its tiles are few and long (8x7B
-// prefill: 72 per XCD of 448 K steps each, 2.25 per CU), so the last round
-// over the CUs decides much of the time. Splitting each tile's K range into a
-// longer first and a shorter second part, all first parts listed before any
-// second part, lets the short parts fill that last round; the price is one
-// more fixed cost per tile (start-up and epilogue, about 10 us) and a second
-// float32 partial of y for the combine to read (A*d*4 bytes). Measured on
-// MI355X (down kernel + combine): 8x7B 905 us unsplit, 900 split in halves,
-// 853 with 13/16 first parts; T = 8192 with skewed routing 1707 unsplit,
-// 1645 with 3/4; 8x22B (1.875 tiles per CU) 788 unsplit and 823-839 split.
-// So the split is taken when the last round over an XCD's 32 CUs is at most
-// half full, and its point by simulating one XCD's schedule for first parts
-// of 8/16 .. 13/16 of K: the tiles of an XCD estimated from A (every expert
-// one part-filled last m-tile, costed at 65%; the device holds the true
-// counts) and taken in list order, each CU the next one as soon as it is
-// free, 12 K steps of fixed cost per tile. The choice depends on the sizes
-// only.
-DownPlan dma_down_plan(int64_t A, int d, int ffn, int E) {
-  DownPlan p{1, ffn};
-  if (!dma_down_ok(A, d, ffn, E)) return p;
-  constexpr int kFixed = 12;
-  constexpr int64_t kXcdCUs = kCUs / 8;
-  const int nsteps = ffn / 32;
-  const int64_t ntn = d / 256;
-  const int64_t mfull = A / DT - E / 2;
-  const int64_t full = ((mfull > 0 ? mfull : 0) * ntn + 7) / 8;  // tiles per XCD
-  const int64_t part = (static_cast<int64_t>(E) * ntn + 7) / 8;   // part-filled ones
-  const int64_t n = full + part;
-  const int64_t last = n % kXcdCUs;  // tiles in the last round
-  if (n <= kXcdCUs || last == 0 || 2 * last > kXcdCUs || n > 4096) return p;
-  int64_t cost[2 * 4096];
-  auto fill = [&](int64_t* c, int steps) {
-    for (int64_t i = 0; i < full; ++i) c[i] = steps + kFixed;
-    for (int64_t i = 0; i < part; ++i) c[full + i] = steps * 13 / 20 + kFixed;
-  };
-  int64_t best = -1;
-  for (int j = 8; j <= 13; ++j) {
-    const int s0 = nsteps * j / 16 / 4 * 4;  // a multiple of 4 steps
-    if (s0 < 4 || nsteps - s0 < 4) continue;
-    fill(cost, s0);
-    fill(cost + n, nsteps - s0);
-    const int64_t t = xcd_makespan(cost, static_cast<int>(2 * n));
-    if (best < 0 || t < best) {
-      best = t;
-      p = DownPlan{2, s0 * 32};
-    }
-  }
-  return p;
-}
-
-}  // namespace
-
-int dma_down_splits(int64_t A, int d, int ffn, int E) { return dma_down_plan(A, d, ffn, E).nsplit; }
 
 hipError_t launch_down_dma(bool packed, const uint16_t* h, const uint16_t* w2,
-                           const int32_t* offsets, int64_t A, int d, int ffn, int E, int nsplit,
-                           float* part, hipStream_t s, const float* s2) {
+                           const int32_t* offsets, int64_t A, int d, int ffn, int E,
+                           int max_split, float* part, hipStream_t s, const float* s2,
+                           DownSplit ds) {
+  const int split_opt = ds.opt;
+  int32_t* ns_out = ds.word;
   const int ntn = d / 256;
-  const int64_t tiles = ((A + DT - 1) / DT + E) * ntn * nsplit;  // upper bound
+  const int nsteps = ffn / 32;
+  if (max_split != 1 && max_split != 2) return hipErrorInvalidValue;
+  const int64_t tiles = ((A + DT - 1) / DT + E) * ntn * max_split;  // upper bound
   const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8));
-  if (nsplit != 1 && nsplit != 2) return hipErrorInvalidValue;
-  const DownPlan plan = dma_down_plan(A, d, ffn, E);
-  // (a caller's nsplit is the plan's; otherwise halves on a 128 boundary)
-  const int ksplit = nsplit == 1 ? ffn : plan.nsplit == 2 ? plan.ksplit : ffn / 256 * 128;
+  // split: -1 chosen on the device, 0 none, > 0 a caller's first part of
+  // split_opt sixteenths of K (whole 4-step trips, at least 4 steps each)
+  int split = 0;
+  if (max_split == 2) {
+    if (split_opt == 0) {
+      split = -1;
+    } else if (split_opt >= 8 && split_opt <= 13) {
+      const int s0 = (nsteps * split_opt / 16) & ~3;
+      split = (s0 >= 4 && nsteps - s0 >= 4) ? s0 : 0;
+    }
+  }
+  const int pair = A <= static_cast<int64_t>(2 * DT) * E;
+  // the combine's read of the second partial (A*d*4 bytes at about 5 TB/s) in
+  // tile K steps (about 0.85 us each at the measured MFMA rate)
+  const int pen = static_cast<int>((A * d) >> 20);
   if (s2 && !packed) return hipErrorInvalidValue;  // row scales come with fragment order only
   if (s2)
     hipLaunchKernelGGL((down_dma_kernel<true, true>), grid, dim3(kDmaThreads), 0, s, h, A, w2,
-                       offsets, d, ffn, E, part, ntn, nsplit, ksplit, s2);
+                       offsets, d, ffn, E, part, ntn, split, pen, pair, ns_out, s2);
   else if (packed)
     hipLaunchKernelGGL((down_dma_kernel<true, false>), grid, dim3(kDmaThreads), 0, s, h, A, w2,
-                       offsets, d, ffn, E, part, ntn, nsplit, ksplit, s2);
+                       offsets, d, ffn, E, part, ntn, split, pen, pair, ns_out, s2);
   else
     hipLaunchKernelGGL((down_dma_kernel<false, false>), grid, dim3(kDmaThreads), 0, s, h, A, w2,
-                       offsets, d, ffn, E, part, ntn, nsplit, ksplit, s2);
+                       offsets, d, ffn, E, part, ntn, split, pen, pair, ns_out, s2);
   return hipGetLastError();
 }
 

@@ -42,15 +42,24 @@ def test_workspace_bytes():
     n32 = f(32, 4096, 14336, 8, 2, moe.MOE_F32)                 # h f32, one y
     assert n32 >= A * 14336 * 4 + A * 4096 * 4
     assert f(64, 4096, 14336, 8, 2, moe.MOE_BF16) > n
-    # large batches use the 256x256-tile kernels: 4096 tokens of 8x7B give
-    # each XCD's 32 CUs about 72 down tiles, 2.25 rounds, so the down
-    # projection splits K in two and leaves two partial arrays; 3200 tokens at
-    # d = 6144 give about 87 tiles, a last round more than half full, and
-    # leave y as one array
-    big = 4096 * 2
+    # large batches use the 256x256-tile kernels, whose down projection
+    # chooses on the device, from the expert counts, whether to split K in
+    # two; the workspace holds the two partial arrays wherever it may: weight
+    # tiles in multiples of 8 per XCD (d % 2048 == 0) and at most 8 rounds of
+    # tiles over an XCD's 32 CUs, counted low (every expert's rows in whole
+    # m-tiles, less one per expert for a paired last one)
+    big = 4096 * 2    # 8x7B: (32 - 4) * 2 = 56 tiles per XCD
     assert f(4096, 4096, 14336, 8, 2, moe.MOE_BF16) >= big * 14336 * 2 + 2 * big * 4096 * 4
-    big = 3200 * 2
-    assert f(3200, 6144, 16384, 8, 2, moe.MOE_BF16) < big * 16384 * 2 + 2 * big * 6144 * 4
+    big = 3200 * 2    # 8x22B widths: (25 - 4) * 3 = 63
+    assert f(3200, 6144, 16384, 8, 2, moe.MOE_BF16) >= big * 16384 * 2 + 2 * big * 6144 * 4
+    big = 16384 * 2   # (128 - 4) * 2 = 248 <= 256: may split
+    assert f(16384, 4096, 14336, 8, 2, moe.MOE_BF16) >= big * 14336 * 2 + 2 * big * 4096 * 4
+    big = 16640 * 2   # (130 - 4) * 2 = 252 <= 256
+    assert f(16640, 4096, 14336, 8, 2, moe.MOE_BF16) >= big * 14336 * 2 + 2 * big * 4096 * 4
+    big = 17024 * 2   # (133 - 4) * 2 = 258 > 256: one array
+    assert f(17024, 4096, 14336, 8, 2, moe.MOE_BF16) < big * 14336 * 2 + 2 * big * 4096 * 4
+    big = 3200 * 2    # d = 3072: 12 weight tiles, not a multiple of 8
+    assert f(3200, 3072, 16384, 8, 2, moe.MOE_BF16) < big * 16384 * 2 + 2 * big * 3072 * 4
     # the K split needs the 256x256-tile down kernel (d % 256 == 0)
     assert f(4096, 4224, 14336, 8, 2, moe.MOE_BF16) < 8192 * 14336 * 2 + 2 * 8192 * 4224 * 4
     # int8 weights: as bf16, except for large prefill batches, where the

@@ -84,12 +84,13 @@ def test_loops_keep_accumulators_in_place(asm, kernel, layout):
     assert len(code) == 1
     loops = _loops(code[0])
     # one loop per token-fragment count the kernel is instantiated for (8, 6,
-    # 4, 2); gate/up with fragment order adds the paired tile's loops, one per
-    # count and per half of the workgroup (its weight-half reads are constants)
+    # 4, 2); fragment order adds the paired tile's loops (both projections),
+    # one per count and per half of the workgroup (its weight-half reads are
+    # constants)
     paired = [b for b in loops if any("vmcnt(10)" in x for x in b)]
     single = [b for b in loops if b not in paired]
     assert len(single) == 4
-    assert len(paired) == (8 if tag.startswith("ILb1") and kernel.startswith("gate_up") else 0)
+    assert len(paired) == (8 if tag.startswith("ILb1") else 0)
     for body in loops:
         pair = body in paired
         mfma = [b.split() for b in body if "v_mfma" in b]

@@ -702,16 +702,56 @@ def test_exact_logit_ties_pick_lower_index(m):
     assert (w == 0.5).all()
 
 
-def _down_splits(A, d, ffn, E):
-    """Whether the 256x256-tile down kernel splits K (the library's rule,
-    restated): d % 256 == 0, experts averaging a full tile, and the last
-    round of an XCD's estimated tiles over its 32 CUs at most half full."""
-    if d % 256 or ffn % 128 or A < 256 * E:
+def _down_may_split(A, d, ffn, E):
+    """Whether the workspace holds two partial arrays of y for the
+    256x256-tile down kernel (the library's host rule, restated): that kernel
+    runs (d % 256 == 0, A >= 256 E), its weight tiles come in multiples of 8
+    per XCD (d % 2048 == 0), K has at least 8 steps of 32, and an XCD's tiles,
+    counted low, fit 8 rounds of its 32 CUs."""
+    if d % 2048 or ffn % 128 or A < 256 * E or ffn // 32 < 8:
         return False
-    ntn = d // 256
-    n = (max(0, A // 256 - E // 2) * ntn + 7) // 8 + (E * ntn + 7) // 8
-    last = n % 32
-    return n > 32 and last != 0 and 2 * last <= 32
+    return (d // 2048) * (A // 256 - (E + 1) // 2) <= 256
+
+
+def _down_split_rule(counts, d, ffn):
+    """The K split the 256x256-tile down kernel chooses on the device, restated
+    from its model: first-part sixteenths j of K (0 = no split). One XCD's 32
+    CUs take its tiles in list order, each the next as soon as it is free;
+    every tile costs its K steps + 12; a split lists all first parts, then
+    all second parts, and costs (A * d) >> 20 more steps (the combine's second
+    read); the fastest of no split and j = 8..13 wins, no split on a tie, and
+    nothing splits past 8 rounds. Last m-tiles of at most 128 rows are paired
+    across two weight tiles (counted so for both layouts) when A <= 512 E."""
+    E, A = len(counts), sum(counts)
+    if not _down_may_split(A, d, ffn, E):
+        return 0
+    nnx, nsteps, P, FIX = d // 2048, ffn // 32, 32, 12
+    pairs = nnx // 2 if A <= 512 * E else 0
+    n = 0
+    for M in counts:
+        mt = -(-M // 256)
+        small = pairs > 0 and mt > 0 and M - (mt - 1) * 256 <= 128
+        n += pairs * (2 * mt - 1) + (nnx - 2 * pairs) * mt if small else nnx * mt
+    if n == 0 or n > 8 * P:
+        return 0
+
+    def two_parts(a, b):
+        # CU finish times, each tile to the CU free first (lowest index on a tie)
+        busy = [0] * P
+        for c in [a] * n + [b] * n:
+            i = busy.index(min(busy))
+            busy[i] += c
+        return max(busy)
+
+    best, choice = -(-n // P) * (nsteps + FIX), 0
+    for j in range(8, 14):
+        s0 = (nsteps * j // 16) // 4 * 4
+        if s0 < 4 or nsteps - s0 < 4:
+            continue
+        t = two_parts(s0 + FIX, nsteps - s0 + FIX) + ((A * d) >> 20)
+        if t < best:
+            best, choice = t, j
+    return choice
 
 
 TAIL_COUNTS = [784, 816, 848, 896, 898, 0, 1024, 1018]
@@ -728,11 +768,11 @@ def test_prefill_tail_tiles(m, d, ffn, extra):
     of 256 (with extra rows added to every non-empty expert in the last case);
     K loops of 4 to 24 steps of 32, so that the row-major kernels' 12-step
     cycle runs not at all, once with 4 or 8 steps left, exactly once and
-    twice, and the fragment-order kernels' 4-step trip once to six times. The
-    last case has enough tiles for the down projection to split K into two
-    parts of unequal length (the workspace then holds the two partial arrays).
-    Oracle within the bf16 bar, and the two weight layouts bit-identical (same
-    MFMA sequence, same split)."""
+    twice, and the fragment-order kernels' 4-step trip once to six times. In
+    the last case the workspace holds two partial arrays and the down kernel
+    may split K (its choice here: no split); it is also run forced to split K
+    at 12 of 16 steps. Oracle within the bf16 bar, and the two weight layouts
+    bit-identical (same MFMA sequence, same split)."""
     counts = [c + extra if c else 0 for c in TAIL_COUNTS]
     E, k = len(counts), 2
     A = sum(counts)
@@ -742,21 +782,25 @@ def test_prefill_tail_tiles(m, d, ffn, extra):
     inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=45 + d)
     sasg = np.random.default_rng(46).permutation(A).astype(np.int32)
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    split = _down_splits(A, d, ffn, E)
+    split = _down_may_split(A, d, ffn, E)
     assert split == (extra > 0)
+    assert _down_split_rule(counts, d, ffn) == 0
     ws = m.moe_workspace_bytes(A // k, d, ffn, E, k, torch.bfloat16)
     assert (ws >= A * ffn * 2 + 2 * A * d * 4) == split
-    print(f"[parity] prefill tails d={d} ffn={ffn} A={A} split={split}", flush=True)
+    print(f"[parity] prefill tails d={d} ffn={ffn} A={A} may split={split}", flush=True)
     dev = to_device(inp)
     o_t = torch.from_numpy(offs).cuda()
     s_t = torch.from_numpy(sasg).cuda()
     pw = m.PackedWeights(dev["w1"], dev["w3"], dev["w2"])
-    y_p = m.moe_expert_ffn(dev["x"], pw.w1, pw.w3, pw.w2, o_t, s_t, k, packed=True, variant=2)
-    y_s = m.moe_expert_ffn(dev["x"], dev["w1"], dev["w3"], dev["w2"], o_t, s_t, k, variant=2)
-    torch.cuda.synchronize()
-    assert torch.equal(y_p, y_s)
     ref = oracle.expert_ffn(inp["x"], inp["w1"], inp["w3"], inp["w2"], offs, sasg, k)
-    assert rel_err(host(y_p), ref) <= OUT_TOL[gen.BF16]
+    for ds in ((0, 12) if split else (0,)):
+        y_p = m.moe_expert_ffn(dev["x"], pw.w1, pw.w3, pw.w2, o_t, s_t, k, packed=True,
+                               variant=2, down_split=ds)
+        y_s = m.moe_expert_ffn(dev["x"], dev["w1"], dev["w3"], dev["w2"], o_t, s_t, k,
+                               variant=2, down_split=ds)
+        torch.cuda.synchronize()
+        assert torch.equal(y_p, y_s), ds
+        assert rel_err(host(y_p), ref) <= OUT_TOL[gen.BF16], ds
 
 
 # last m-tiles of 45, 128 (the expert's only tile), 1, 128 and 144 rows and an
@@ -770,10 +814,13 @@ def test_prefill_paired_tail_tiles(m, d, ffn):
     128 rows is computed for two of an XCD's weight tiles at once (512 weight
     rows x 128 tokens). Shapes with one such pair per XCD (ffn = 2048), a pair
     and one weight tile left over (ffn = 3072: 24 weight tiles, 3 per XCD),
-    and none (ffn = 1024: one weight tile per XCD); the down projection runs
-    its 256x256 tiles as usual. The row-major weights run every last m-tile
-    on its own, with the same MFMA sequence per output, so the two layouts
-    must agree bit for bit; both within the bf16 bar of the oracle."""
+    and none (ffn = 1024: one weight tile per XCD). The down projection
+    (A <= 512 E here) pairs its last m-tiles the same way where d = 4096 (16
+    weight tiles, 2 per XCD) and, at d = 4096, splits K at 12 of 16 steps
+    (18 tiles per XCD: the second parts fill idle CUs). The row-major weights
+    run every last m-tile on its own, with the same MFMA sequence per output
+    and the same split, so the two layouts must agree bit for bit; both
+    within the bf16 bar of the oracle."""
     counts = PAIRED_COUNTS
     E, k = len(counts), 2
     A = sum(counts)
@@ -781,7 +828,8 @@ def test_prefill_paired_tail_tiles(m, d, ffn):
     inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=47 + d)
     sasg = np.random.default_rng(48).permutation(A).astype(np.int32)
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    print(f"[parity] paired tails d={d} ffn={ffn} A={A}", flush=True)
+    print(f"[parity] paired tails d={d} ffn={ffn} A={A} "
+          f"down split {_down_split_rule(counts, d, ffn)}/16", flush=True)
     dev = to_device(inp)
     o_t = torch.from_numpy(offs).cuda()
     s_t = torch.from_numpy(sasg).cuda()
@@ -794,6 +842,57 @@ def test_prefill_paired_tail_tiles(m, d, ffn):
     err = rel_err(host(y_p), ref)
     print(f"[parity]   max|err|/rms {err:.2e}", flush=True)
     assert err <= OUT_TOL[gen.BF16]
+
+
+# (d, ffn, per-expert rows): the down kernel's own K split, as _down_split_rule
+# restates it: 12/16 (18 tiles per XCD, fewer than its CUs), none (39 tiles,
+# short K), 11/16 (16 experts of about 256 rows, paired last m-tiles, 38
+# tiles) and 11/16 (8 experts, 39 tiles, long K)
+SPLIT_CASES = [(4096, 2048, PAIRED_COUNTS),
+               (2048, 512, [1174] + [c + 389 if c else 0 for c in TAIL_COUNTS[1:]]),
+               (4096, 4096, [244, 283, 254, 270, 230, 268, 265, 261, 231, 260, 240, 249, 253,
+                             249, 256, 291]),
+               (2048, 4096, [1100, 1050, 1200, 1090, 1000, 1110, 1030, 1120])]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
+def test_down_split_choice(m, case):
+    """The 256x256-tile down kernel chooses its K split on the device from the
+    expert counts: its result equals, bit for bit, the result forced to the
+    split _down_split_rule predicts (down_split = j, or -1 for none), in both
+    weight layouts, and differs from the other choice only by float32
+    summation order. The sum of the two parts is read back by the same
+    partial-sum path either way."""
+    d, ffn, counts = SPLIT_CASES[case]
+    E, k = len(counts), 2
+    A = sum(counts)
+    assert A % k == 0 and A >= 256 * E
+    j = _down_split_rule(counts, d, ffn)
+    assert j == (12, 0, 11, 11)[case]
+    print(f"[parity] down split d={d} ffn={ffn} A={A} E={E}: predicted {j}/16", flush=True)
+    inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=60 + case)
+    sasg = np.random.default_rng(61 + case).permutation(A).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    dev = to_device(inp)
+    o_t = torch.from_numpy(offs).cuda()
+    s_t = torch.from_numpy(sasg).cuda()
+    pw = m.PackedWeights(dev["w1"], dev["w3"], dev["w2"])
+
+    def run(ds, packed):
+        w = (pw.w1, pw.w3, pw.w2) if packed else (dev["w1"], dev["w3"], dev["w2"])
+        return m.moe_expert_ffn(dev["x"], *w, o_t, s_t, k, packed=packed, variant=2,
+                                down_split=ds)
+
+    auto = run(0, True)
+    same = run(j if j else -1, True)
+    other = run(-1 if j else 12, True)
+    auto_s = run(0, False)
+    torch.cuda.synchronize()
+    assert torch.equal(auto, same)
+    assert torch.equal(auto, auto_s)
+    assert not torch.equal(auto, other)
+    diff = (auto - other).abs().max().item() / auto.pow(2).mean().sqrt().item()
+    assert diff <= 1e-5, diff
 
 
 # ---------------------------------------------------------------- full size --
