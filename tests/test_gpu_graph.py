@@ -20,10 +20,13 @@ def m():
     yield lib
 
 
-# a decode-sized batch (streaming kernels, permutation inside gate/up) and a
-# larger one (separate permutation, tiled kernels, split down projection)
+# a decode-sized batch (streaming kernels, permutation inside gate/up), a
+# larger one (separate permutation, tiled kernels, split down projection) and
+# a prefill-sized one (256x256-tile kernels; the down kernel chooses its K
+# split on the device and records it for the combine in the workspace)
 CASES = [dict(T=32, d=512, ffn=1024, E=8, k=2, dtype=gen.BF16, seed=401),
-         dict(T=300, d=256, ffn=512, E=8, k=2, dtype=gen.BF16, seed=402)]
+         dict(T=300, d=256, ffn=512, E=8, k=2, dtype=gen.BF16, seed=402),
+         dict(T=1024, d=2048, ffn=1024, E=8, k=2, dtype=gen.BF16, seed=403)]
 
 
 @pytest.mark.parametrize("cfg", CASES)
