@@ -847,12 +847,16 @@ def test_prefill_paired_tail_tiles(m, d, ffn):
 # (d, ffn, per-expert rows): the down kernel's own K split, as _down_split_rule
 # restates it: 12/16 (18 tiles per XCD, fewer than its CUs), none (39 tiles,
 # short K), 11/16 (16 experts of about 256 rows, paired last m-tiles, 38
-# tiles) and 11/16 (8 experts, 39 tiles, long K)
+# tiles), 11/16 (8 experts, 39 tiles, long K), 8/16 (5 tiles: the second
+# halves run on idle CUs) and 13/16 (22 tiles, 96 K steps)
 SPLIT_CASES = [(4096, 2048, PAIRED_COUNTS),
                (2048, 512, [1174] + [c + 389 if c else 0 for c in TAIL_COUNTS[1:]]),
                (4096, 4096, [244, 283, 254, 270, 230, 268, 265, 261, 231, 260, 240, 249, 253,
                              249, 256, 291]),
-               (2048, 4096, [1100, 1050, 1200, 1090, 1000, 1110, 1030, 1120])]
+               (2048, 4096, [1100, 1050, 1200, 1090, 1000, 1110, 1030, 1120]),
+               (2048, 512, [226, 287, 268, 245]),
+               (2048, 3072, [1252, 1089, 1093, 1544])]
+SPLIT_CHOICES = (12, 0, 11, 11, 8, 13)
 
 
 @pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
@@ -868,7 +872,7 @@ def test_down_split_choice(m, case):
     A = sum(counts)
     assert A % k == 0 and A >= 256 * E
     j = _down_split_rule(counts, d, ffn)
-    assert j == (12, 0, 11, 11)[case]
+    assert j == SPLIT_CHOICES[case]
     print(f"[parity] down split d={d} ffn={ffn} A={A} E={E}: predicted {j}/16", flush=True)
     inp = gen.make_inputs(T=A // k, d=d, ffn=ffn, E=E, k=k, dtype=gen.BF16, seed=60 + case)
     sasg = np.random.default_rng(61 + case).permutation(A).astype(np.int32)
