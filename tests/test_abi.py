@@ -182,9 +182,10 @@ def test_pack_weight_rejects_bad_arguments():
               ctypes.c_void_p((1 << 40) + 4096), None) == moe.MOE_EINVAL   # overlapping buffers
 
 
-def _options(variant=0, events=None):
+def _options(variant=0, events=None, down_split=0):
     o = moe.MoeOptions()
     o.ffn_variant = variant
+    o.down_split = down_split
     if events is not None:
         arr = (ctypes.c_void_p * 6)(*events)
         o.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
@@ -207,9 +208,17 @@ def test_options_are_checked_per_call():
         return f(BAD, moe.MOE_BF16, BAD, BAD, BAD, BAD, BAD, 4, 128, 256, 8, 2, BAD, BAD, ws,
                  None, opts)
 
-    for bad in (_options(3), _options(-1), _options(0, [1, 2, 3, None, 5, 6])):
+    for bad in (_options(3), _options(-1), _options(0, [1, 2, 3, None, 5, 6]),
+                _options(down_split=-2), _options(down_split=1), _options(down_split=7),
+                _options(down_split=14), _options(down_split=16)):
         assert fwd(bad) == moe.MOE_EINVAL
         assert ffn(bad) == moe.MOE_EINVAL
+    # every down split the options allow passes the option check (here the
+    # workspace is what fails)
+    for ds in (-1, 0, 8, 9, 10, 11, 12, 13):
+        assert fw(BAD, moe.MOE_BF16, BAD, None, BAD, BAD, BAD, 4, 128, 256, 8, 2, BAD,
+                  moe.MOE_BF16, None, None, None, BAD, 0, None, _options(down_split=ds)) == \
+            moe.MOE_EWORKSPACE, ds
     # valid options leave the other checks in charge (here: the workspace)
     assert fw(BAD, moe.MOE_BF16, BAD, None, BAD, BAD, BAD, 4, 128, 256, 8, 2, BAD, moe.MOE_BF16,
               None, None, None, BAD, 0, None, _options(2, [1, 2, 3, 4, 5, 6])) == \
