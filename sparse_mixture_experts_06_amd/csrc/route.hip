@@ -346,19 +346,25 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(
 // Large batches: the logits as a small GEMM on fp32 MFMA
 // (v_mfma_f32_16x16x4_f32: 16 tokens x 4 k x 16 experts, float32 operands
 // and accumulation). A workgroup takes 16 tokens and all E experts (one or two
-// 16-expert tiles); its 16 waves split d into 16 slices of 32-wide steps
-// (one workgroup per CU at prefill sizes, so the waves of a CU cover each
-// other's load latency; each wave also loads 4 steps ahead). In a step lane
-// (t, q) = (l % 16, l / 16) loads token t's 8 values k0 + 8q .. +7 (16 bytes
-// of bf16, widened) and, per expert tile, expert (l % 16)'s router values at
-// the same k (32 bytes); MFMA i of the step multiplies value i of both, so
-// the 8 MFMAs cover the 32 k of the step (the k order inside the step differs
-// from the scalar kernel's, as any float32 summation order would). The router
-// is read once per 16 tokens. The waves' partial sums meet in LDS in a fixed
-// order; one thread per token then scores it. Needs d % 2048 == 0 (whole
-// 4-step batches per wave), x and router 16-byte aligned, E <= 32.
-constexpr int kMfmaWaves = 16;
-constexpr int kMfmaAhead = 4;  // steps loaded ahead
+// 16-expert tiles); its 8 waves split d into 8 slices, each walked in groups
+// of 64 k. A group is loaded in whole cache lines (tokens: 8 rows x 128 bytes
+// per load, lane l row l / 8, 16-byte chunk l % 8; router: 4 rows x 256 bytes,
+// lane l row l / 16, chunk l % 16), the next group's loads in flight while the
+// wave works on this one; the wave writes the group into its own LDS area
+// (chunk c of row r at slot c ^ (r % 8) for tokens, c ^ (r % 16) for router
+// rows; no barrier: only the wave reads it back, and a wave's LDS operations
+// complete in order) and reads the MFMA operands from there: in a 32-k step
+// lane (t, q) = (l % 16, l / 16) takes token t's 8 values 8q .. 8q+7 (16
+// bytes of bf16, widened) and, per expert tile, expert (l % 16)'s router
+// values at the same k (32 bytes); MFMA i of the step multiplies value i of
+// both, so the 8 MFMAs cover the 32 k of the step. (Read straight from global
+// memory in that operand layout, every load touched 16 rows 8 or 16 KiB apart:
+// the same bytes as whole lines measured a fifth faster.) The router is read
+// once per 16 tokens. The waves' partial sums meet in LDS in a fixed order;
+// one thread per token then scores it. Needs d % 512 == 0 (whole groups per
+// wave), x and router 16-byte aligned, E <= 32.
+constexpr int kMfmaWaves = 8;
+constexpr int kGroupK = 64;  // k of one group
 
 template <int NT>  // expert tiles of 16
 __global__ __launch_bounds__(kWave* kMfmaWaves, 1) void route_mfma_kernel(
@@ -366,58 +372,90 @@ __global__ __launch_bounds__(kWave* kMfmaWaves, 1) void route_mfma_kernel(
     const float* __restrict__ bias, int64_t T, int d, int E, int k, float* __restrict__ logits_out,
     int32_t* __restrict__ idx, float* __restrict__ wout) {
   constexpr int EM = 16 * NT;
+  constexpr int kXBytes = 16 * kGroupK * 2;   // 16 token rows x 64 k bf16 (2 KiB)
+  constexpr int kRBytes = EM * kGroupK * 4;   // EM router rows x 64 k fp32
+  constexpr int kRLoads = EM / 4;             // router loads per group (4 rows each)
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kMfmaWaves][kXBytes + kRBytes];
   __shared__ f32x4 s_part[kMfmaWaves][NT][kWave];
   __shared__ float s_logit[16][EM];
+  __shared__ float s_l[16][32];  // scoring: logits + bias, exponentials
+  __shared__ float s_p[16][32];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int t = lane & 15, q = lane >> 4;
-  const int64_t row = min(t0 + t, T - 1);  // rows past the batch read the last row
-  const uint16_t* xp = x + row * d + 8 * q;
-  // lanes of experts >= E load nothing (zeros; those sums are unused)
-  const float* rp[NT];
-  bool ev[NT];
+  uint8_t* xs = s_stage[wave];
+  uint8_t* rs = s_stage[wave] + kXBytes;
+
+  // global loads of a group (k0 = its first k): tokens rows 8i + l/8 (rows past
+  // the batch read the last row), router rows 4i + l/16 (rows of experts >= E
+  // load nothing: zeros, whose sums are unused)
+  const int xr = lane >> 3, xc = lane & 7;
+  const int rr = lane >> 4, rc = lane & 15;
+  const uint16_t* xrow[2];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    ev[nt] = 16 * nt + t < E;
-    rp[nt] = router + static_cast<int64_t>(min(16 * nt + t, E - 1)) * d + 8 * q;
-  }
+  for (int i = 0; i < 2; ++i) xrow[i] = x + min(t0 + 8 * i + xr, T - 1) * d + 8 * xc;
+  auto load_group = [&](int k0, u32x4 (&xv)[2], float4 (&rv)[kRLoads]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xv[i] = ldg16(xrow[i] + k0);
+#pragma unroll
+    for (int i = 0; i < kRLoads; ++i) {
+      const int e = 4 * i + rr;
+      rv[i] = e < E ? *reinterpret_cast<const float4*>(router + static_cast<int64_t>(e) * d + k0 + 4 * rc)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int per = d / 32 / kMfmaWaves;  // steps of this wave, a multiple of kMfmaAhead
-  for (int st = wave * per; st < (wave + 1) * per; st += kMfmaAhead) {
-    u32x4 xv[kMfmaAhead];
-    float4 ra[kMfmaAhead][NT], rb[kMfmaAhead][NT];
+  auto use_group = [&](const u32x4 (&xv)[2], const float4 (&rv)[kRLoads]) {
 #pragma unroll
-    for (int u = 0; u < kMfmaAhead; ++u) {
-      xv[u] = ldg16(xp + (st + u) * 32);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        ra[u][nt] = rb[u][nt] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (ev[nt]) {
-          ra[u][nt] = *reinterpret_cast<const float4*>(rp[nt] + (st + u) * 32);
-          rb[u][nt] = *reinterpret_cast<const float4*>(rp[nt] + (st + u) * 32 + 4);
-        }
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * i + xr;
+      *reinterpret_cast<u32x4*>(xs + r * 128 + ((xc ^ (r & 7)) * 16)) = xv[i];
     }
 #pragma unroll
-    for (int u = 0; u < kMfmaAhead; ++u) {
+    for (int i = 0; i < kRLoads; ++i) {
+      const int e = 4 * i + rr;
+      *reinterpret_cast<float4*>(rs + e * 256 + ((rc ^ (e & 15)) * 16)) = rv[i];
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {  // 32-k steps of the group
+      const int cx = 4 * s + q;    // token chunk: k 32s + 8q .. +7
+      const u32x4 xw = *reinterpret_cast<const u32x4*>(xs + t * 128 + ((cx ^ (t & 7)) * 16));
       float xf[8];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        xf[2 * h] = __uint_as_float(xv[u][h] << 16);
-        xf[2 * h + 1] = __uint_as_float(xv[u][h] & 0xFFFF0000u);
+        xf[2 * h] = __uint_as_float(xw[h] << 16);
+        xf[2 * h + 1] = __uint_as_float(xw[h] & 0xFFFF0000u);
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float rf[8] = {ra[u][nt].x, ra[u][nt].y, ra[u][nt].z, ra[u][nt].w,
-                             rb[u][nt].x, rb[u][nt].y, rb[u][nt].z, rb[u][nt].w};
+        const int e = 16 * nt + t;
+        const int c0 = 8 * s + 2 * q;  // router chunks: k 32s + 8q .. +3, +4 .. +7
+        const float4 a = *reinterpret_cast<const float4*>(rs + e * 256 + ((c0 ^ t) * 16));
+        const float4 b = *reinterpret_cast<const float4*>(rs + e * 256 + (((c0 + 1) ^ t) * 16));
+        const float rf[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[i], rf[i], acc[nt], 0, 0, 0);
       }
+    }
+  };
+  // this wave's groups, two at a time (two register sets: the next group's
+  // loads are in flight while this one is used)
+  const int ng = d / kGroupK / kMfmaWaves;  // groups per wave (d % 512 == 0)
+  const int kb = wave * ng * kGroupK;
+  u32x4 xa[2], xb[2];
+  float4 ra[kRLoads], rb[kRLoads];
+  load_group(kb, xa, ra);
+  for (int g = 0; g < ng; g += 2) {
+    if (g + 1 < ng) load_group(kb + (g + 1) * kGroupK, xb, rb);
+    use_group(xa, ra);
+    if (g + 1 < ng) {
+      if (g + 2 < ng) load_group(kb + (g + 2) * kGroupK, xa, ra);
+      use_group(xb, rb);
     }
   }
   // lane l holds tokens 4 (l / 16) + i of expert 16 nt + l % 16
@@ -435,13 +473,54 @@ __global__ __launch_bounds__(kWave* kMfmaWaves, 1) void route_mfma_kernel(
     }
   }
   __syncthreads();
-  if (tid >= 16) return;
-  const int64_t tok = t0 + tid;
-  if (tok >= T) return;
-  float l[EM];
+  // scoring, as score_token computes it: 32 lanes per token (lane e: expert
+  // e) add the bias, write the logits out, take the maximum (an exact
+  // operation in any order) and their exponentials; the token's first lane
+  // then sums the probabilities and selects the top k in expert order, with
+  // the same operations on the same values as score_token
+  {
+    const int tt = tid >> 5, e = tid & 31;
+    const int64_t tok = t0 + tt;
+    const bool valid = e < E;
+    float le = valid ? s_logit[tt][e] : -INFINITY;
+    if (valid && bias) le += bias[e];
+    if (valid && logits_out && tok < T) logits_out[tok * E + e] = le;
+    float m = valid ? le : -INFINITY;
 #pragma unroll
-  for (int e = 0; e < EM; ++e) l[e] = s_logit[tid][e];
-  score_token<EM>(l, bias, tok, E, k, logits_out, idx, wout);
+    for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    s_l[tt][e] = le;
+    s_p[tt][e] = valid ? expf(le - m) : 0.0f;
+    // (the lanes of a token share a wave, whose LDS operations complete in order)
+    if (e != 0 || tok >= T) return;
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EM; ++j) sum += s_p[tt][j];
+    uint32_t taken = 0;
+    float psum = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      float bl = 0.0f;
+#pragma unroll
+      for (int x = 0; x < EM; ++x) {
+        const float lx = s_l[tt][x];
+        if (x < E && !((taken >> x) & 1u) && (best < 0 || lx > bl)) {
+          best = x;
+          bl = lx;
+        }
+      }
+      if (best < 0) {  // only with NaN logits: take the lowest free expert
+#pragma unroll
+        for (int x = EM - 1; x >= 0; --x)
+          if (x < E && !((taken >> x) & 1u)) best = x;
+      }
+      taken |= 1u << best;
+      const float bp = s_p[tt][best] / sum;
+      idx[tok * k + j] = best;
+      psum += bp;
+      wout[tok * k + j] = bp;  // rescaled below
+    }
+    for (int j = 0; j < k; ++j) wout[tok * k + j] = wout[tok * k + j] / psum;
+  }
 }
 
 constexpr int64_t kSmallBatch = 256;
@@ -501,11 +580,12 @@ hipError_t launch_route(const void* x, int x_bf16, const float* router, const fl
                                   norm_out, s);
   }
   const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  // (with 8 experts the scalar kernel is as fast: every workgroup of the MFMA
-  // kernel reads the whole router for 16 tokens, which its CU's load rate
-  // bounds; measured at T = 4096, d = 4096: 17 us scalar, 20 us MFMA at
-  // E = 8; 140 us scalar, 42 us MFMA at E = 32)
-  if (x_bf16 && E > 8 && T > kSmallBatch && d % (32 * kMfmaWaves * kMfmaAhead) == 0 &&
+  // (measured at T = 4096, d = 4096, bench events: 32 experts 140 us scalar,
+  // 49 us with the first MFMA kernel, whose loads each touched 16 rows and
+  // whose 16 scoring threads each ran a 32-expert softmax, 36 us now; 16
+  // experts 28 -> 23 us; with 8 experts the scalar kernel stays faster at
+  // T = 4096, 21 vs 24 us, though not at 8192, 36 vs 27)
+  if (x_bf16 && E > 8 && T > kSmallBatch && d % (kGroupK * kMfmaWaves) == 0 &&
       a16(x) && a16(router)) {
     const dim3 grid(static_cast<unsigned>((T + 15) / 16));
     if (E <= 16)
